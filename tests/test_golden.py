@@ -1,0 +1,89 @@
+"""The stored oracle outputs in ``golden/oracle_small.txt`` still hold: the
+seeded generator reproduces the stored inputs bit for bit, and the oracle
+reproduces the stored outputs bit for bit."""
+import os
+
+import numpy as np
+
+import oracle
+import synthetic
+from tests.golden.make_oracle_small import CASES, case_arrays
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_small.txt")
+
+
+def load_golden():
+    cases = {}
+    cur = None
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("case "):
+            _, name, op, rows, width, eps = line.split()
+            cur = dict(op=op, rows=int(rows), width=int(width), eps=None if eps == "none" else float(eps))
+            cases[name] = cur
+        else:
+            key, vals = line.split(":", 1)
+            cur[key] = np.array([float.fromhex(v) for v in vals.split()], dtype=np.float64)
+    return cases
+
+
+def test_golden_cases_reproduce():
+    stored = load_golden()
+    assert set(stored) == {c[0] for c in CASES}
+    for name, op, rows, width, dist, seed in CASES:
+        g = stored[name]
+        x, r = case_arrays(op, rows, width, dist, seed)
+        assert np.array_equal(x.astype(np.float64).reshape(-1), g["x"])
+        if r is not None:
+            assert np.array_equal(r.astype(np.float64).reshape(-1), g["r"])
+        y = oracle.run_op(op, x, r, eps=g["eps"], threads=1)
+        assert np.array_equal(y.reshape(-1), g["y"]), name
+        if op == "softmax":
+            np.testing.assert_allclose(y.sum(axis=1), 1.0, atol=1e-14)
+
+
+def test_config_registry_matches_workloads():
+    # The five workloads: shapes, operators and distributions.
+    shapes = {(c.cfg, c.op, c.rows, c.width, c.dist) for c in synthetic.all_cases()}
+    assert (1, "layernorm_residual", 17, 257, "uniform") in shapes
+    assert (1, "layernorm_residual", 1, 127, "uniform") in shapes
+    for op in ("softmax", "rmsnorm", "layernorm_residual"):
+        assert (2, op, 1024, 4096, "uniform") in shapes
+        assert (4, op, 16384, 8192, "uniform") in shapes
+    for w in (127, 257, 1537):
+        for op in ("rmsnorm", "softmax"):
+            assert (3, op, 131072, w, "normal") in shapes
+    assert (5, "softmax", 8192, 32768, "stress") in shapes
+    assert len(shapes) == 2 + 3 + 6 + 3 + 1
+
+
+def test_generator_distributions():
+    u = synthetic.draw("uniform", 256, 1024, synthetic.seed_sequence(2, "softmax", "x", 256, 1024))
+    assert u.dtype == np.float32 and -1 <= u.min() and u.max() <= 1
+    assert abs(float(u.mean())) < 0.01 and abs(float(u.var()) - 1 / 3) < 0.01
+    n = synthetic.draw("normal", 256, 1024, synthetic.seed_sequence(3, "rmsnorm", "x", 256, 1024))
+    assert abs(float(n.mean())) < 0.01 and abs(float(n.std()) - 1) < 0.01
+    s = synthetic.draw("stress", 64, 32768, synthetic.seed_sequence(5, "softmax", "x", 64, 32768))
+    frac = float(np.isneginf(s).mean())
+    assert 0.009 < frac < 0.011
+    assert not np.isneginf(s).all(axis=1).any()
+    fin = np.where(np.isfinite(s), s, np.nan)
+    assert np.nanmax(fin) < 80 + 8 * 7 and np.nanmin(fin) > -80 - 8 * 7
+    # deterministic
+    s2 = synthetic.draw("stress", 64, 32768, synthetic.seed_sequence(5, "softmax", "x", 64, 32768))
+    assert np.array_equal(s, s2)
+    # different tensors get different streams
+    a = synthetic.case_input(synthetic.CONFIGS[1][0], "x")
+    b = synthetic.case_input(synthetic.CONFIGS[1][0], "r")
+    assert not np.array_equal(a, b)
+
+
+def test_stress_rows_overflow_without_max_subtraction():
+    # Row offsets up to +80 plus 8-sigma noise put row maxima above
+    # ln(FLT_MAX) ~ 88.72 on a good share of rows, so an FP32 softmax that
+    # skips the max subtraction would overflow there.
+    s = synthetic.draw("stress", 512, 4096, synthetic.seed_sequence(5, "softmax", "x", 512, 4096))
+    frac = float((s.max(axis=1) > 88.72).mean())
+    assert frac > 0.05
