@@ -1,0 +1,189 @@
+/*
+ * rowred.h -- fused FP32 row reductions on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point is extern "C", takes plain pointers and sizes,
+ * returns an int status (enum rowred_status) and never throws.
+ *
+ * Layout: every matrix is row-major FP32, `rows` x `width`, row stride equal
+ * to `width` elements, contiguous.  All matrix pointers are device pointers
+ * and must be 4-byte aligned; 16-byte alignment is not required.  x is read
+ * 16 bytes at a time; r and y are read / written 16 bytes at a time when
+ * they share x's address modulo 16, otherwise 4 bytes at a time (equally
+ * valid results, lower bandwidth).
+ *
+ * Reads: each row is fetched as the run of whole 16-byte granules that
+ * contain it, so a call may read up to 12 bytes before the first element and
+ * after the last element of x (and r), always inside the 16-byte granules
+ * that hold valid elements.  Those extra values are never used and never
+ * written.
+ *
+ * Writes: exactly the rows*width elements of y, each once.
+ *
+ * Ownership: the caller owns all memory.  The library allocates nothing,
+ * keeps no per-call state and is safe to call from several host threads.
+ *
+ * Asynchrony: work is enqueued on `stream` (NULL = the default stream) and
+ * the call returns without synchronising, so calls can be captured into a
+ * HIP graph.  ROWRED_ERR_HIP reports a failed launch; a fault during the
+ * kernel surfaces at the caller's next synchronisation.
+ *
+ * Aliasing: y must not overlap x or r (checked on the host,
+ * ROWRED_ERR_ALIAS); x and r may overlap each other (both are only read).
+ * The kernels keep each row in registers between its phases, so an in-place
+ * call would be computable, but the no-overlap rule follows the pages'
+ * requirement that the caller guarantee noalias and that a packed row tail
+ * never reads and writes one buffer ("Immutable input reuse in Metal
+ * reductions", section "What the transformation actually preserves";
+ * "Cooperating-program packing: implementation and fixed-plan evidence",
+ * section "Implementation boundary").
+ *
+ * Sizes: rows < 0 or width < 0 -> ROWRED_ERR_INVALID_ARG.  rows == 0 or
+ * width == 0 -> ROWRED_OK with nothing launched (pointers may then be NULL).
+ * A NULL or misaligned pointer otherwise -> ROWRED_ERR_INVALID_ARG.  A row is
+ * held in registers across the phases, so width is capped: the 16-byte slot
+ * window of a row (ceil((width + misalignment) / 4)) must not exceed 8192,
+ * i.e. width <= 32768 for 16-byte-aligned rows; wider rows give
+ * ROWRED_ERR_UNSUPPORTED.
+ *
+ * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
+ * accepted; a LayerNorm row with zero variance then gives NaN (0/0), as
+ * IEEE arithmetic does.  NaN and infinite inputs propagate with no special
+ * case.
+ *
+ * Determinism: for a fixed plan (see rowred_plan_query) results are bitwise
+ * reproducible from run to run.
+ */
+#ifndef ROWRED_H
+#define ROWRED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (identical to the typedef in hip_runtime_api.h). */
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+enum rowred_status {
+  ROWRED_OK = 0,
+  ROWRED_ERR_INVALID_ARG = 1, /* bad size, pointer, eps or plan */
+  ROWRED_ERR_ALIAS = 2,       /* y overlaps an input */
+  ROWRED_ERR_UNSUPPORTED = 3, /* row too wide for one register-resident pass */
+  ROWRED_ERR_HIP = 4          /* the HIP runtime refused the launch */
+};
+
+enum rowred_op {
+  ROWRED_OP_LAYERNORM_RESIDUAL = 0,
+  ROWRED_OP_RMSNORM = 1,
+  ROWRED_OP_SOFTMAX = 2
+};
+
+/*
+ * Residual LayerNorm without affine parameters, per row i:
+ *   c = x_i + r_i;  mean = sum(c) / width;  d = c - mean;
+ *   var = sum(d^2) / width  (biased, second pass over d);
+ *   y_i = d / sqrt(var + eps).
+ * Defined by the residual LayerNorm program in "Residual LayerNorm
+ * shared-Tile materialization search", section "Structural finding"; the
+ * pages use eps = 1e-5.  Only y is written (the combined row is not).
+ * x, r: inputs (rows x width); r must be non-NULL.  y: output.
+ */
+int rowred_layernorm_residual(const float *x, const float *r, float *y,
+                              int64_t rows, int64_t width, float eps,
+                              hipStream_t stream);
+
+/*
+ * RMSNorm without weight, per row i:  y_i = x_i / sqrt(sum(x_i^2)/width + eps).
+ * "Immutable input reuse in Metal reductions", section "What the
+ * transformation actually preserves", gives its phases (one sum-of-squares
+ * reduction, then an output map over the same input); the formula is the
+ * plain definition.  Typical eps = 1e-6.
+ */
+int rowred_rmsnorm(const float *x, float *y, int64_t rows, int64_t width,
+                   float eps, hipStream_t stream);
+
+/*
+ * Softmax with max subtraction, per row i:
+ *   m = max_j x_ij;  e_j = exp(x_ij - m);  y_ij = e_j / sum_j e_j.
+ * Phases as in "Immutable input reuse in Metal reductions", section "What
+ * the transformation actually preserves" (max, then exp-sum over a computed
+ * stripe, then normalise).  -inf entries get weight 0; a row that is all
+ * -inf gives NaN (-inf - -inf).  The normaliser is applied as one
+ * reciprocal per row times each e_j.
+ */
+int rowred_softmax(const float *x, float *y, int64_t rows, int64_t width,
+                   hipStream_t stream);
+
+/*
+ * Launch geometry.  A row is owned by `lanes_per_row` (L) consecutive lanes
+ * of one workgroup; `rows_per_group` = threads / L rows share a workgroup
+ * (several short rows per wavefront when L < 64, one or more wavefronts per
+ * row when L >= 64).  Lane l of a row holds, for chunk c < chunks, the 16-byte
+ * slot c*L + l of the row's window, so each input element is read once and
+ * stays in registers through every phase of the reduction.  This is the
+ * packing geometry of "Cooperating-program packing: implementation and
+ * fixed-plan evidence", section "Implementation boundary", and the element
+ * ownership map of "Immutable input reuse in Metal reductions", section
+ * "What the transformation actually preserves", with 4 elements per slot.
+ * The last workgroup's surplus row slots recompute the last row and store
+ * nothing.
+ */
+typedef struct rowred_plan {
+  int32_t lanes_per_row;  /* L: power of two, 1..1024 */
+  int32_t rows_per_group; /* threads / L */
+  int32_t chunks;         /* 16-byte slots per lane: 1..8, 10, 12 or 16 */
+  int32_t threads;        /* workgroup size: multiple of 64, <= 1024 (<= 512 when chunks > 8) */
+  int64_t grid;           /* workgroups launched: ceil(rows / rows_per_group) */
+  int32_t vector_io;      /* 1: r and y share x's address modulo 16 (all accesses 16 bytes) */
+  int32_t window;         /* largest number of 16-byte granules a row of x spans (L*chunks covers it) */
+  int32_t policy;         /* memory policy: ROWRED_POLICY_* bits */
+  int32_t reserved;       /* 0 */
+} rowred_plan;
+
+/* Memory policy bits of a plan.  They change speed, never results. */
+enum rowred_policy {
+  ROWRED_POLICY_NT_LOADS = 1,  /* loads carry the non-temporal (streaming) hint */
+  ROWRED_POLICY_NT_STORES = 2, /* stores carry the non-temporal hint */
+  ROWRED_POLICY_XCD_REMAP = 4  /* each XCD walks one contiguous range of row blocks */
+};
+
+/*
+ * Host-only: fill *out with the plan the matching entry point would launch
+ * for these arguments (x, r, y are only inspected for their alignment; r may
+ * be NULL for ops without a residual).  No device work, callable without a
+ * GPU.  Returns the status the entry point would return before launching.
+ */
+int rowred_plan_query(int op, const float *x, const float *r, const float *y,
+                      int64_t rows, int64_t width, rowred_plan *out);
+
+/*
+ * Run one operator with an explicit plan instead of the chooser's (for
+ * tuning sweeps and tests of every geometry).  lanes_per_row, chunks,
+ * threads and policy are read from *plan; grid, rows_per_group, vector_io and
+ * window are derived.  A plan that breaks a constraint listed in rowred_plan, or
+ * whose lanes_per_row * chunks does not cover the row window, ->
+ * ROWRED_ERR_INVALID_ARG.
+ * eps is ignored for softmax.  Same contract as the entry points above.
+ */
+int rowred_run_plan(int op, const float *x, const float *r, float *y,
+                    int64_t rows, int64_t width, float eps,
+                    const rowred_plan *plan, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *rowred_status_string(int status);
+
+/*
+ * Measurement aid: y[i] = x[i] for i < n, with the same 16-byte streaming
+ * loads and stores as the reductions, to measure the bandwidth a plain copy
+ * reaches and to calibrate traffic counters.  x and y must not overlap; both
+ * 16-byte aligned, n a multiple of 4, else ROWRED_ERR_INVALID_ARG.
+ */
+int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWRED_H */

@@ -1,0 +1,258 @@
+"""Python binding of ``librowred.so``: fused FP32 row reductions on MI355X.
+
+Argument marshalling only -- every step of every reduction runs in the HIP
+kernels behind the C ABI declared in ``include/rowred.h``.  There is no
+fallback: if the library is not built, or a call fails, an exception is
+raised.
+
+Each C entry point has a Python function of the same name.  Matrix
+arguments may be torch tensors (CUDA, float32, row-major contiguous; the
+last dimension is the row width and leading dimensions are rows) or raw
+device addresses (ints, then ``rows`` and ``width`` are required).  With
+tensors the call is enqueued on torch's current stream unless ``stream`` (a
+raw ``hipStream_t`` as int) is given.  Torch is used for device memory and
+streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librowred.so")
+
+ROWRED_OK = 0
+ROWRED_ERR_INVALID_ARG = 1
+ROWRED_ERR_ALIAS = 2
+ROWRED_ERR_UNSUPPORTED = 3
+ROWRED_ERR_HIP = 4
+
+ROWRED_POLICY_NT_LOADS = 1
+ROWRED_POLICY_NT_STORES = 2
+ROWRED_POLICY_XCD_REMAP = 4
+
+ROWRED_OP_LAYERNORM_RESIDUAL = 0
+ROWRED_OP_RMSNORM = 1
+ROWRED_OP_SOFTMAX = 2
+OPS = {"layernorm_residual": ROWRED_OP_LAYERNORM_RESIDUAL, "rmsnorm": ROWRED_OP_RMSNORM,
+       "softmax": ROWRED_OP_SOFTMAX}
+
+
+class RowRedError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({rowred_status_string(status)})")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("lanes_per_row", ctypes.c_int32), ("rows_per_group", ctypes.c_int32),
+                ("chunks", ctypes.c_int32), ("threads", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("vector_io", ctypes.c_int32), ("window", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+@dataclass
+class Plan:
+    lanes_per_row: int
+    rows_per_group: int
+    chunks: int
+    threads: int
+    grid: int
+    vector_io: int = 0
+    window: int = 0
+    policy: int = 0
+    reserved: int = 0
+
+    def _c(self) -> _Plan:
+        return _Plan(self.lanes_per_row, self.rows_per_group, self.chunks, self.threads, self.grid,
+                     self.vector_io, self.window, self.policy, self.reserved)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def lib():
+    """The loaded ``librowred.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m row_wise_reduction_amd.build` "
+                              "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        sigs = {
+            "rowred_layernorm_residual": [_P, _P, _P, _I64, _I64, ctypes.c_float, _P],
+            "rowred_rmsnorm": [_P, _P, _I64, _I64, ctypes.c_float, _P],
+            "rowred_softmax": [_P, _P, _I64, _I64, _P],
+            "rowred_plan_query": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan)],
+            "rowred_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
+            "rowred_copy": [_P, _P, _I64, _P],
+        }
+        for name, argtypes in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_int
+        L.rowred_status_string.argtypes = [ctypes.c_int]
+        L.rowred_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def rowred_status_string(status: int) -> str:
+    return lib().rowred_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+
+def _is_tensor(a) -> bool:
+    return hasattr(a, "data_ptr") and hasattr(a, "dtype")
+
+
+def _matrix(a, name, rows=None, width=None):
+    """(address, rows, width) of a tensor or raw address."""
+    if a is None:
+        return None, rows, width
+    if _is_tensor(a):
+        import torch
+        if a.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {a.dtype}")
+        if not a.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        if not a.is_contiguous():
+            raise ValueError(f"{name} must be row-major contiguous")
+        if a.dim() == 0:
+            return a.data_ptr(), 1, 1
+        r = 1
+        for d in a.shape[:-1]:
+            r *= int(d)
+        return a.data_ptr(), r, int(a.shape[-1])
+    return int(a), rows, width
+
+
+def _shape(pairs, rows, width):
+    """Check that every tensor argument agrees on (rows, width)."""
+    for name, (addr, r, w) in pairs:
+        if addr is None:
+            continue
+        if rows is None:
+            rows, width = r, w
+        elif (r, w) != (rows, width):
+            raise ValueError(f"{name} has shape ({r}, {w}), expected ({rows}, {width})")
+    if rows is None or width is None:
+        raise ValueError("rows and width are required with raw addresses")
+    return int(rows), int(width)
+
+
+def _stream(stream, *args):
+    if stream is not None:
+        return int(stream)
+    if any(_is_tensor(a) for a in args):
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return 0
+
+
+def _check(status, what):
+    if status != ROWRED_OK:
+        raise RowRedError(status, what)
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+
+def rowred_layernorm_residual(x, r, y, rows=None, width=None, eps=1e-5, stream=None):
+    """y = (x + r - mean) / sqrt(var + eps) per row (biased variance, no affine)."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    st = lib().rowred_layernorm_residual(mx[0], mr[0], my[0], rows, width, float(eps), _stream(stream, x, r, y))
+    _check(st, "rowred_layernorm_residual")
+
+
+def rowred_rmsnorm(x, y, rows=None, width=None, eps=1e-6, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) per row (no weight)."""
+    mx, my = _matrix(x, "x", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("y", my)], rows, width)
+    st = lib().rowred_rmsnorm(mx[0], my[0], rows, width, float(eps), _stream(stream, x, y))
+    _check(st, "rowred_rmsnorm")
+
+
+def rowred_softmax(x, y, rows=None, width=None, stream=None):
+    """y = exp(x - max) / sum(exp(x - max)) per row."""
+    mx, my = _matrix(x, "x", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("y", my)], rows, width)
+    st = lib().rowred_softmax(mx[0], my[0], rows, width, _stream(stream, x, y))
+    _check(st, "rowred_softmax")
+
+
+def _op_id(op):
+    return OPS[op] if isinstance(op, str) else int(op)
+
+
+def rowred_plan_query(op, x, r, y, rows=None, width=None) -> Plan:
+    """The plan the entry point would launch (host only; no device work)."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    p = _Plan()
+    st = lib().rowred_plan_query(_op_id(op), mx[0], mr[0], my[0], rows, width, ctypes.byref(p))
+    _check(st, "rowred_plan_query")
+    return Plan(p.lanes_per_row, p.rows_per_group, p.chunks, p.threads, p.grid, p.vector_io, p.window, p.policy,
+                p.reserved)
+
+
+def rowred_run_plan(op, x, r, y, plan: Plan, rows=None, width=None, eps=0.0, stream=None):
+    """Run `op` with an explicit launch plan."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    c = plan._c()
+    st = lib().rowred_run_plan(_op_id(op), mx[0], mr[0], my[0], rows, width, float(eps), ctypes.byref(c),
+                               _stream(stream, x, r, y))
+    _check(st, "rowred_run_plan")
+
+
+def rowred_copy(x, y, n=None, stream=None):
+    """y[:n] = x[:n] with the library's streaming 16-byte copy (measurement aid)."""
+    if _is_tensor(x):
+        n = x.numel() if n is None else n
+    st = lib().rowred_copy(_matrix(x, "x")[0] if _is_tensor(x) else int(x),
+                           _matrix(y, "y")[0] if _is_tensor(y) else int(y), int(n), _stream(stream, x, y))
+    _check(st, "rowred_copy")
+
+
+# Short aliases over tensors (allocate the output with torch when not given).
+
+def layernorm_residual(x, r, out=None, eps=1e-5):
+    import torch
+    out = torch.empty_like(x) if out is None else out
+    rowred_layernorm_residual(x, r, out, eps=eps)
+    return out
+
+
+def rmsnorm(x, out=None, eps=1e-6):
+    import torch
+    out = torch.empty_like(x) if out is None else out
+    rowred_rmsnorm(x, out, eps=eps)
+    return out
+
+
+def softmax(x, out=None):
+    import torch
+    out = torch.empty_like(x) if out is None else out
+    rowred_softmax(x, out)
+    return out
+
+
+def run_op(op: str, x, r, y, eps=None):
+    """Dispatch by operator name with the pages' eps defaults (1e-5 LN, 1e-6 RMS)."""
+    if op == "layernorm_residual":
+        rowred_layernorm_residual(x, r, y, eps=1e-5 if eps is None else eps)
+    elif op == "rmsnorm":
+        rowred_rmsnorm(x, y, eps=1e-6 if eps is None else eps)
+    elif op == "softmax":
+        rowred_softmax(x, y)
+    else:
+        raise ValueError(f"unknown op {op!r}")

@@ -1,0 +1,251 @@
+// rowred_api.cpp -- C ABI of the row-reduction library: argument checks, the
+// launch-geometry chooser and the entry points.  Host code only; the kernels
+// live in rowred_kernels.hip.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "rowred_internal.h"
+
+#define ROWRED_API extern "C" __attribute__((visibility("default")))
+
+
+namespace rowred {
+namespace {
+
+constexpr int kNumOps = 3;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+
+bool chunks_supported(int chunks) {
+  for (int c : kChunkSet)
+    if (c == chunks) return true;
+  return false;
+}
+
+// Smallest instantiated chunk count >= want, or -1.
+int round_up_chunks(int64_t want) {
+  for (int c : kChunkSet)
+    if (c >= want) return c;
+  return -1;
+}
+
+// Shape of one call after argument checks.
+struct Call {
+  int op;
+  const float *x, *r;
+  float *y;
+  int64_t rows, width;
+  bool r_vec, y_vec;  // r / y share x's address modulo 16
+  int window;         // largest number of 16-byte granules a row of x spans
+};
+
+bool overlaps(const void *a, const void *b, int64_t bytes) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + (uintptr_t)bytes && pb < pa + (uintptr_t)bytes;
+}
+
+// Largest granule window over the rows: a row starting `o` floats past a
+// 16-byte boundary spans ceil((width + o) / 4) granules.  Row i starts at
+// (x + i*width) so its offset cycles with period <= 4 rows.
+int max_window(const float *x, int64_t rows, int64_t width) {
+  const int64_t off0 = (int64_t)(((uintptr_t)x >> 2) & 3);
+  int64_t worst = 0;
+  const int64_t probe = rows < 4 ? rows : 4;
+  for (int64_t i = 0; i < probe; ++i) {
+    const int64_t off = (off0 + i * width) & 3;
+    const int64_t w = (width + off + 3) / 4;
+    if (w > worst) worst = w;
+  }
+  return worst > INT32_MAX ? INT32_MAX : (int)worst;
+}
+
+// Checks shared by every entry point.  `need_eps` marks ops with an eps.
+int check_call(int op, const float *x, const float *r, const float *y, int64_t rows, int64_t width, bool need_r,
+               bool need_eps, float eps, Call *out) {
+  if (op < 0 || op >= kNumOps) return ROWRED_ERR_INVALID_ARG;
+  if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
+  if (need_eps && (!isfinite(eps) || eps < 0.0f)) return ROWRED_ERR_INVALID_ARG;
+  out->op = op;
+  out->x = x;
+  out->r = r;
+  out->y = const_cast<float *>(y);
+  out->rows = rows;
+  out->width = width;
+  out->r_vec = out->y_vec = false;
+  out->window = 0;
+  if (rows == 0 || width == 0) return ROWRED_OK;
+  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (!x || !y || (need_r && !r)) return ROWRED_ERR_INVALID_ARG;
+  if (((uintptr_t)x & 3) || ((uintptr_t)y & 3) || (r && ((uintptr_t)r & 3))) return ROWRED_ERR_INVALID_ARG;
+  const int64_t bytes = rows * width * 4;
+  if (overlaps(x, y, bytes) || (r && overlaps(r, y, bytes))) return ROWRED_ERR_ALIAS;
+  const uintptr_t ax = (uintptr_t)x & 15;
+  out->y_vec = ((uintptr_t)y & 15) == ax;
+  out->r_vec = r && ((uintptr_t)r & 15) == ax;
+  out->window = max_window(x, rows, width);
+  if (out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
+// Fill grid / rows_per_group / window and check every plan constraint.
+int finish_plan(const Call &c, rowred_plan *p) {
+  const int64_t L = p->lanes_per_row, T = p->threads;
+  if (!is_pow2(L) || L > 1024) return ROWRED_ERR_INVALID_ARG;
+  if (T < 64 || T > 1024 || T % 64 != 0 || T % L != 0) return ROWRED_ERR_INVALID_ARG;
+  if (!chunks_supported(p->chunks) || T > max_threads_for_chunks(p->chunks)) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
+  p->window = c.window;
+  p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
+  if (L * p->chunks < p->window) return ROWRED_ERR_INVALID_ARG;
+  p->rows_per_group = (int32_t)(T / L);
+  p->grid = (c.rows + p->rows_per_group - 1) / p->rows_per_group;
+  // The dispatch packet counts work-items in 32 bits.
+  if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
+// The chooser, keyed on the row window and the matrix size; its rules come
+// from sweeps of every geometry and memory policy on MI355X at the workload
+// shapes (widths 127, 257, 1537, 4096, 8192, 32768).
+//
+// Geometry: every input element is loaded once into registers, so the
+// per-lane stripe sets register use and the serial work per lane.  Short
+// stripes with many lanes per row win: at most 2 slots (8 floats) per lane --
+// the pages' 8-float stripe at 4096 columns -- or 4 slots for inputs of at
+// most 32 MiB, which run in a single round of waves where fewer, fatter
+// waves amortise the wave start-up.  L is the smallest power of two meeting
+// that bound (at most 1024), chunks the smallest instantiated count covering
+// the window.  Workgroups have 256 threads, or L when a row needs more.
+//
+// Memory policy: streaming (non-temporal) stores are fastest when each
+// row's stores leave in one or two instructions.  Where neighbouring rows
+// share a 16-byte granule (rows not starting on 16-byte boundaries) and a lane
+// holds more than 2 slots, the two partial writes of a shared line are issued
+// far apart and streaming stores turn them into separate partial
+// write-backs; cached stores let L2 merge them.  The XCD remap (each XCD
+// walks one contiguous range of rows) pays off once the grid runs in several
+// rounds (> 64 MiB per input) or when rows share boundary granules.
+void choose_plan(const Call &c, rowred_plan *p) {
+  const int64_t w = c.window;
+  const int64_t in_bytes = c.rows * c.width * 4;
+  const int64_t max_chunks = in_bytes <= (int64_t(32) << 20) ? 4 : 2;
+  int64_t L = 1;
+  while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
+  p->lanes_per_row = (int32_t)L;
+  p->chunks = round_up_chunks((w + L - 1) / L);
+  p->threads = (int32_t)(L > 256 ? L : 256);
+  const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+  int policy = kPolicyNtLoads;
+  if (rows_aligned || p->chunks <= 2) policy |= kPolicyNtStores;
+  if (!rows_aligned || in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
+  p->policy = policy;
+  p->reserved = 0;
+}
+
+int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
+  RowArgs a;
+  a.x = c.x;
+  a.r = c.r;
+  a.y = c.y;
+  a.rows = c.rows;
+  a.width = (int32_t)c.width;
+  a.lanes_log2 = ilog2(plan.lanes_per_row);
+  a.eps = eps;
+  a.inv_width = 1.0f / (float)c.width;
+  a.policy = plan.policy;
+  a.r_vec = c.r_vec ? 1 : 0;
+  a.y_vec = c.y_vec ? 1 : 0;
+  a.pad_ = 0;
+  const int err = launch_rows(c.op, plan.chunks, plan.grid, plan.threads, a, stream);
+  return err == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
+}
+
+int entry(int op, const float *x, const float *r, float *y, int64_t rows, int64_t width, float eps, bool need_r,
+          bool need_eps, hipStream_t stream) {
+  Call c;
+  int st = check_call(op, x, r, y, rows, width, need_r, need_eps, eps, &c);
+  if (st != ROWRED_OK || rows == 0 || width == 0) return st;
+  rowred_plan p;
+  choose_plan(c, &p);
+  st = finish_plan(c, &p);
+  if (st != ROWRED_OK) return st;
+  return run(c, p, eps, stream);
+}
+
+bool op_has_eps(int op) { return op == ROWRED_OP_LAYERNORM_RESIDUAL || op == ROWRED_OP_RMSNORM; }
+
+}  // namespace
+}  // namespace rowred
+
+using namespace rowred;
+
+ROWRED_API int rowred_layernorm_residual(const float *x, const float *r, float *y, int64_t rows, int64_t width,
+                                         float eps, hipStream_t stream) {
+  return entry(ROWRED_OP_LAYERNORM_RESIDUAL, x, r, y, rows, width, eps, true, true, stream);
+}
+
+ROWRED_API int rowred_rmsnorm(const float *x, float *y, int64_t rows, int64_t width, float eps,
+                              hipStream_t stream) {
+  return entry(ROWRED_OP_RMSNORM, x, nullptr, y, rows, width, eps, false, true, stream);
+}
+
+ROWRED_API int rowred_softmax(const float *x, float *y, int64_t rows, int64_t width, hipStream_t stream) {
+  return entry(ROWRED_OP_SOFTMAX, x, nullptr, y, rows, width, 0.0f, false, false, stream);
+}
+
+ROWRED_API int rowred_plan_query(int op, const float *x, const float *r, const float *y, int64_t rows,
+                                 int64_t width, rowred_plan *out) {
+  if (!out) return ROWRED_ERR_INVALID_ARG;
+  Call c;
+  const bool need_r = op == ROWRED_OP_LAYERNORM_RESIDUAL;
+  int st = check_call(op, x, need_r ? r : nullptr, y, rows, width, need_r, false, 0.0f, &c);
+  if (st != ROWRED_OK) return st;
+  if (rows == 0 || width == 0) {
+    *out = rowred_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return ROWRED_OK;
+  }
+  choose_plan(c, out);
+  return finish_plan(c, out);
+}
+
+ROWRED_API int rowred_run_plan(int op, const float *x, const float *r, float *y, int64_t rows, int64_t width,
+                               float eps, const rowred_plan *plan, hipStream_t stream) {
+  if (!plan) return ROWRED_ERR_INVALID_ARG;
+  Call c;
+  const bool need_r = op == ROWRED_OP_LAYERNORM_RESIDUAL;
+  int st = check_call(op, x, need_r ? r : nullptr, y, rows, width, need_r, op_has_eps(op), eps, &c);
+  if (st != ROWRED_OK || rows == 0 || width == 0) return st;
+  rowred_plan p = *plan;
+  st = finish_plan(c, &p);
+  if (st != ROWRED_OK) return st;
+  return run(c, p, eps, stream);
+}
+
+ROWRED_API const char *rowred_status_string(int status) {
+  switch (status) {
+    case ROWRED_OK: return "ok";
+    case ROWRED_ERR_INVALID_ARG: return "invalid argument (size, pointer, eps or plan)";
+    case ROWRED_ERR_ALIAS: return "output overlaps an input";
+    case ROWRED_ERR_UNSUPPORTED: return "row too wide for a register-resident pass";
+    case ROWRED_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+ROWRED_API int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream) {
+  if (n < 0 || (n & 3)) return ROWRED_ERR_INVALID_ARG;
+  if (n == 0) return ROWRED_OK;
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return ROWRED_ERR_INVALID_ARG;
+  if (n > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (overlaps(x, y, n * 4)) return ROWRED_ERR_ALIAS;
+  if ((n / 4 + 1023) / 1024 > INT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return launch_copy(x, y, n / 4, stream) == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
+}

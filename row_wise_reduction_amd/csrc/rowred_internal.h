@@ -1,0 +1,47 @@
+// rowred_internal.h -- interface between the host entry points and the
+// gfx950 kernels.  Not installed; not part of the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "rowred.h"
+
+namespace rowred {
+
+// Kernel arguments, passed by value in the kernarg segment.
+struct RowArgs {
+  const float *x;      // rows x width input
+  const float *r;      // residual (LayerNorm) or nullptr
+  float *y;            // rows x width output
+  int64_t rows;
+  int32_t width;
+  int32_t lanes_log2;  // log2(L)
+  float eps;
+  float inv_width;     // 1.0f / width, rounded to FP32
+  int32_t policy;      // ROWRED_POLICY_* bits
+  int32_t r_vec;       // 1: r shares x's address modulo 16 (16-byte loads)
+  int32_t y_vec;       // 1: y shares x's address modulo 16 (16-byte stores)
+  int32_t pad_;
+};
+
+constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;
+constexpr int kPolicyNtStores = ROWRED_POLICY_NT_STORES;
+constexpr int kPolicyXcdRemap = ROWRED_POLICY_XCD_REMAP;
+
+// Chunk counts for which kernels are instantiated (slots per lane).
+constexpr int kChunkSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
+constexpr int kNumChunkSizes = sizeof(kChunkSet) / sizeof(kChunkSet[0]);
+constexpr int kMaxWindow = 8192;  // 16-byte slots per row: 1024 lanes x 8 or 512 x 16
+
+// Largest workgroup the kernel for `chunks` is compiled for.
+constexpr int max_threads_for_chunks(int chunks) { return chunks <= 8 ? 1024 : 512; }
+
+// Enqueue one reduction kernel.  Returns the hipError_t of the launch
+// (0 = success).  The caller has validated every argument.
+int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args,
+                hipStream_t stream);
+
+// Enqueue the streaming copy (n4 = number of 16-byte slots).
+int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);
+
+}  // namespace rowred

@@ -1,0 +1,415 @@
+// rowred_kernels.hip -- gfx950 kernels for fused FP32 row reductions.
+//
+// One skeleton serves residual LayerNorm, RMSNorm and softmax.  A row is
+// owned by L = 2^lanes_log2 consecutive lanes of a workgroup; lane l holds
+// the row's 16-byte slots c*L + l (c < C) in registers (the "stripe"), so
+// every input element is fetched from HBM once and reused by all phases:
+//
+//   load (+ residual add)  ->  reduction 1  ->  element map + reduction 2
+//   ->  output map  ->  predicated store
+//
+// This follows the element ownership map and cross-phase input reuse of
+// "Immutable input reuse in Metal reductions" (section "What the
+// transformation actually preserves"), and the row packing, two-level
+// collective and tail replay of "Cooperating-program packing:
+// implementation and fixed-plan evidence" (section "Implementation
+// boundary"), re-planned for 64-lane wavefronts:
+//   * L <= 64: 64/L rows per wavefront; the collective is a DPP / ds_swizzle
+//     butterfly inside the lane group, no LDS and no barrier.
+//   * L > 64: the wavefront total goes to one LDS float per wave, one
+//     barrier, then every lane folds its row's L/64 partials in a fixed
+//     order (so all lanes hold bitwise-identical statistics).
+//   * Rows whose start is not 16-byte aligned are read as the run of whole
+//     16-byte granules that contain them; elements outside the row take the
+//     reduction's identity and are never stored.
+//   * Surplus row slots of the last workgroup recompute the last row and
+//     skip the store, so every barrier is reached by every wave.
+//   * Workgroups are handed out round-robin over the 8 XCDs; the block index
+//     is remapped so each XCD walks one contiguous range of rows, which
+//     keeps the granule shared by two neighbouring rows in one L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rowred_internal.h"
+
+namespace rowred {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kOpLayerNorm = ROWRED_OP_LAYERNORM_RESIDUAL;
+constexpr int kOpRms = ROWRED_OP_RMSNORM;
+constexpr int kOpSoftmax = ROWRED_OP_SOFTMAX;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------------------
+// Memory access.  Each plan picks, per launch, whether global loads and
+// stores carry the non-temporal (streaming) hint; the choice is uniform, so
+// the kernels branch once around each block of accesses.
+// ---------------------------------------------------------------------------
+template <bool NT, class T>
+__device__ __forceinline__ T load_g(const T *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, class T>
+__device__ __forceinline__ void store_g(T *p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange inside a wavefront.
+// ---------------------------------------------------------------------------
+// DPP16 controls: quad_perm [1,0,3,2] (partner lane ^ 1), quad_perm [2,3,0,1]
+// (^ 2), row_half_mirror (lane i <-> 7-i inside 8), row_mirror (i <-> 15-i
+// inside 16).  After the ^1 and ^2 steps every lane of a quad holds the
+// quad's value, so the two mirrors act as the ^4 and ^8 butterfly steps.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+// ds_swizzle bit-mask mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 -> lane ^ 16
+// inside each 32-lane half.
+constexpr int kSwizzleXor16 = (0x10 << 10) | 0x1F;
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kSwizzleXor16));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// 64-bit values move as two 32-bit halves.
+struct Halves {
+  int lo, hi;
+};
+__device__ __forceinline__ Halves split(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  return {(int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ double join(int lo, int hi) {
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+template <int Ctrl>
+__device__ __forceinline__ double dpp(double v) {
+  const Halves h = split(v);
+  return join(__builtin_amdgcn_update_dpp(0, h.lo, Ctrl, 0xF, 0xF, false),
+              __builtin_amdgcn_update_dpp(0, h.hi, Ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ double swizzle_xor16(double v) {
+  const Halves h = split(v);
+  return join(__builtin_amdgcn_ds_swizzle(h.lo, kSwizzleXor16), __builtin_amdgcn_ds_swizzle(h.hi, kSwizzleXor16));
+}
+
+__device__ __forceinline__ double readlane(double v, int lane) {
+  const Halves h = split(v);
+  return join(__builtin_amdgcn_readlane(h.lo, lane), __builtin_amdgcn_readlane(h.hi, lane));
+}
+
+struct SumOp {
+  template <class T>
+  static __device__ __forceinline__ T apply(T a, T b) { return a + b; }
+};
+struct MaxOp {
+  static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+};
+
+// All-reduce over aligned groups of 2^min(lanes_log2, 6) lanes.  Each step
+// combines a lane with its partner commutatively, so every lane of a group
+// ends with the same bits.  lanes_log2 is uniform: the branches are scalar.
+template <class R, class T>
+__device__ __forceinline__ T group_allreduce(T v, int lanes_log2) {
+  if (lanes_log2 >= 1) v = R::apply(v, dpp<kDppXor1>(v));
+  if (lanes_log2 >= 2) v = R::apply(v, dpp<kDppXor2>(v));
+  if (lanes_log2 >= 3) v = R::apply(v, dpp<kDppHalfMirror>(v));
+  if (lanes_log2 >= 4) v = R::apply(v, dpp<kDppMirror>(v));
+  if (lanes_log2 >= 5) v = R::apply(v, swizzle_xor16(v));
+  if (lanes_log2 >= 6) v = R::apply(readlane(v, 0), readlane(v, 32));
+  return v;
+}
+
+// Row all-reduce: lane group first, then (rows wider than a wavefront) one
+// LDS partial per wave, a barrier, and a fixed-order fold of the row's
+// partials.  `partials` must be distinct for each reduction of a kernel so
+// that a fast wave's next write cannot overtake a slow wave's read.
+template <class R, class T>
+__device__ __forceinline__ T row_allreduce(T v, int lanes_log2, T *partials) {
+  v = group_allreduce<R>(v, lanes_log2 < 6 ? lanes_log2 : 6);
+  if (lanes_log2 > 6) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) partials[wave] = v;
+    __syncthreads();
+    const int per_row_log2 = lanes_log2 - 6;
+    const int first = (wave >> per_row_log2) << per_row_log2;
+    T acc = partials[first];
+    for (int w = 1; w < (1 << per_row_log2); ++w) acc = R::apply(acc, partials[first + w]);
+    v = acc;
+  }
+  return v;
+}
+
+// Workgroup -> row block.  The dispatcher deals workgroups to the 8 XCDs in
+// turn; give XCD x the contiguous block range [x*q + min(x, rem), ...).
+__device__ __forceinline__ int64_t row_block(uint32_t bid, uint32_t nblk, bool remap) {
+  if (!remap) return bid;
+  constexpr uint32_t kXcds = 8;
+  const uint32_t q = nblk / kXcds, rem = nblk % kXcds;
+  const uint32_t xcd = bid % kXcds, i = bid / kXcds;
+  return (int64_t)xcd * q + (xcd < rem ? xcd : rem) + i;
+}
+
+template <int OP>
+__device__ __forceinline__ float identity() {
+  return OP == kOpSoftmax ? -__builtin_inff() : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// The row kernel.  C = 16-byte slots per lane.  x fixes the window: slot k of
+// a row is the k-th 16-byte granule holding any of its elements, and lane
+// li of the row holds slots c*L + li.  r and y are accessed 16 bytes at a
+// time when they share x's address modulo 16 (a.r_vec / a.y_vec), otherwise
+// 4 bytes at a time at the same element positions.
+// ---------------------------------------------------------------------------
+template <int OP, int C>
+__global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs a) {
+  __shared__ float partials[2][16];
+  __shared__ double partials_d[16];
+
+  const int lanes_log2 = a.lanes_log2;
+  const int L = 1 << lanes_log2;
+  const int li = threadIdx.x & (L - 1);
+  const int slot = threadIdx.x >> lanes_log2;
+  const int rows_per_group = blockDim.x >> lanes_log2;
+  const int width = a.width;
+
+  int64_t row = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0) * rows_per_group + slot;
+  const bool live = row < a.rows;
+  if (!live) row = a.rows - 1;  // tail replay: recompute the last row, store nothing
+  const int64_t base = row * (int64_t)width;
+
+  // Position of this row inside its first granule and the number of
+  // granules it touches.
+  const float *xrow = a.x + base;
+  const int off = (int)(((uintptr_t)xrow >> 2) & 3);
+  const int nwin = (width + off + 3) >> 2;
+  const int kmax = nwin - 1;
+
+  // Element index (inside the row) of stripe element 4c+j; < 0 or >= width
+  // at the window edges and in slots past the window.
+  auto elem = [&](int c, int j) -> int { return 4 * (c * L + li) + j - off; };
+  auto valid = [&](int c, int j) -> bool { return (unsigned)elem(c, j) < (unsigned)width; };
+
+  float s[4 * C];
+
+  // ---- load: every input element once, all loads issued back to back
+  // before any use.  Slots past the row's last granule load the last granule
+  // again instead of branching around the load (a cache hit that keeps the
+  // loads unconditional); they are masked to the identity below by their
+  // unclamped position.
+  const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
+  const bool nt_loads = (a.policy & kPolicyNtLoads) != 0;
+  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  const float *rrow = has_r ? a.r + base : nullptr;
+  f32x4 xv[C], rv[C];
+  auto load_rows = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+#pragma unroll
+    for (int c = 0; c < C; ++c) xv[c] = load_g<NT>(xw + min(c * L + li, kmax));
+    if (has_r) {
+      if (a.r_vec) {
+        const f32x4 *rw = reinterpret_cast<const f32x4 *>(rrow - off);
+#pragma unroll
+        for (int c = 0; c < C; ++c) rv[c] = load_g<NT>(rw + min(c * L + li, kmax));
+      } else {
+        // r sits at another phase of the 16-byte grid: read the same elements
+        // one by one, each index clamped into the row.
+        const int emax = width - 1;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rv[c][j] = load_g<NT>(rrow + max(0, min(elem(c, j), emax)));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c) rv[c] = f32x4(0.0f);
+    }
+  };
+  if (nt_loads) load_rows(std::true_type{});
+  else load_rows(std::false_type{});
+  // x + r exactly (in FP64), 0 outside the row.
+  auto combined = [&](int c, int j) -> double {
+    return valid(c, j) ? (double)xv[c][j] + (double)rv[c][j] : 0.0;
+  };
+  if constexpr (OP != kOpLayerNorm) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[4 * c + j] = valid(c, j) ? xv[c][j] : identity<OP>();
+  }
+
+  // ---- phases.
+  if constexpr (OP == kOpRms) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) acc[i & 3] = fmaf(s[i], s[i], acc[i & 3]);
+    float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    ss = row_allreduce<SumOp>(ss, lanes_log2, partials[0]);
+    const float scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) s[i] *= scale;
+  } else if constexpr (OP == kOpSoftmax) {
+    float mx[4] = {s[0], s[1], s[2], s[3]};
+#pragma unroll
+    for (int i = 4; i < 4 * C; ++i) mx[i & 3] = fmaxf(mx[i & 3], s[i]);
+    float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) {
+      s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);  // exp(x - m); -inf -> 0
+      acc[i & 3] += s[i];
+    }
+    float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
+    const float inv = __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) s[i] *= inv;
+  } else {  // LayerNorm
+    // The combined value x + r, the mean and the centring are formed in FP64:
+    // the sum of two floats is exact in double, so each centred value d = c -
+    // mean is correct to FP32 rounding even when the row's spread is far
+    // below its magnitude (a large common offset, or variance << eps, where
+    // FP32 rounding of c and of the mean would be amplified by
+    // 1/sqrt(var + eps)).  Variance and output are FP32: from here on every
+    // error is relative.
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += combined(c, j);
+    double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    sum = row_allreduce<SumOp>(sum, lanes_log2, partials_d);
+    const double mean = sum / (double)width;
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d = valid(c, j) ? (float)(combined(c, j) - mean) : 0.0f;  // outside the row: 0
+        s[4 * c + j] = d;
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+    float var = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    var = row_allreduce<SumOp>(var, lanes_log2, partials[1]);
+    const float rstd = __builtin_amdgcn_rsqf(fmaf(var, a.inv_width, a.eps));
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) s[i] *= rstd;
+  }
+
+  // ---- predicated store: replayed row slots write nothing.
+  if (!live) return;
+  float *yrow = a.y + base;
+  auto store_rows = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    if (a.y_vec) {
+      f32x4 *yw = reinterpret_cast<f32x4 *>(yrow - off);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int k = c * L + li;
+        const int e0 = 4 * k - off;
+        if (e0 >= 0 && e0 + 4 <= width) {
+          store_g<NT>(yw + k, f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]});
+        } else if (k < nwin) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((unsigned)(e0 + j) < (unsigned)width) store_g<NT>(yrow + e0 + j, s[4 * c + j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (valid(c, j)) store_g<NT>(yrow + elem(c, j), s[4 * c + j]);
+    }
+  };
+  if (a.policy & kPolicyNtStores) store_rows(std::true_type{});
+  else store_rows(std::false_type{});
+}
+
+// Plain streaming copy: 4 slots of 16 bytes per lane, loads before stores.
+__global__ void __launch_bounds__(256) copy_kernel(const f32x4 *x, f32x4 *y, int64_t n4) {
+  constexpr int kPer = 4;
+  const int64_t first = (int64_t)blockIdx.x * (256 * kPer) + threadIdx.x;
+  f32x4 v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t i = first + u * 256;
+    v[u] = load_g<true>(x + (i < n4 ? i : n4 - 1));  // clamped: unconditional loads
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t i = first + u * 256;
+    if (i < n4) store_g<true>(y + i, v[u]);
+  }
+}
+
+using KernelFn = void (*)(RowArgs);
+
+#define ROWRED_CHUNK_ROW(OP)                                                                     \
+  {rows_kernel<OP, 1>, rows_kernel<OP, 2>, rows_kernel<OP, 3>,  rows_kernel<OP, 4>,                \
+   rows_kernel<OP, 5>, rows_kernel<OP, 6>, rows_kernel<OP, 7>,  rows_kernel<OP, 8>,                \
+   rows_kernel<OP, 10>, rows_kernel<OP, 12>, rows_kernel<OP, 16>}
+
+// [op][chunk index in kChunkSet]
+const KernelFn kKernels[3][kNumChunkSizes] = {
+    ROWRED_CHUNK_ROW(kOpLayerNorm),
+    ROWRED_CHUNK_ROW(kOpRms),
+    ROWRED_CHUNK_ROW(kOpSoftmax),
+};
+#undef ROWRED_CHUNK_ROW
+
+static_assert(kNumChunkSizes == 11, "kernel table rows must match kChunkSet");
+
+int chunk_index(int chunks) {
+  for (int i = 0; i < kNumChunkSizes; ++i)
+    if (kChunkSet[i] == chunks) return i;
+  return -1;
+}
+
+}  // namespace
+
+int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args, hipStream_t stream) {
+  const int ci = chunk_index(chunks);
+  if (op < 0 || op > 2 || ci < 0) return (int)hipErrorInvalidValue;
+  KernelFn fn = kKernels[op][ci];
+  RowArgs a = args;
+  void *params[] = {&a};
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)grid), dim3(threads), params, 0,
+                              stream);
+}
+
+int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream) {
+  const int64_t grid = (n4 + 1023) / 1024;
+  const f32x4 *xs = reinterpret_cast<const f32x4 *>(x);
+  f32x4 *ys = reinterpret_cast<f32x4 *>(y);
+  int64_t n = n4;
+  void *params[] = {&xs, &ys, &n};
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(copy_kernel), dim3((uint32_t)grid), dim3(256), params,
+                              0, stream);
+}
+
+}  // namespace rowred

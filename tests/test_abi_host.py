@@ -1,0 +1,243 @@
+"""Host-side checks of the C ABI (no GPU, no device work).
+
+* the library loads and exports every function ``include/rowred.h`` declares;
+* the plan chooser's geometry covers every row and respects the limits;
+* every argument error is reported before anything touches the GPU.
+
+Pointers here are fake addresses: the checked paths never dereference them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_wise_reduction_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rowred.h")
+
+CHUNKS = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rowred_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rowred_layernorm_residual", "rowred_rmsnorm", "rowred_softmax", "rowred_plan_query",
+              "rowred_run_plan", "rowred_status_string", "rowred_copy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(R.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_library_exports_nothing_else():
+    # -fvisibility=hidden: only the C ABI is visible.
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {n for n in exported if n.startswith("rowred_")} == set(declared_functions())
+
+
+def test_status_strings():
+    for s in range(5):
+        assert R.rowred_status_string(s)
+    assert R.rowred_status_string(99) == "unknown status"
+
+
+X, RR, Y = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000  # 16-byte aligned, far apart
+
+
+def window(x, rows, width):
+    off0 = (x >> 2) & 3
+    return max((width + ((off0 + i * width) & 3) + 3) // 4 for i in range(min(rows, 4)))
+
+
+@pytest.mark.parametrize("op", ["layernorm_residual", "rmsnorm", "softmax"])
+@pytest.mark.parametrize("width", [1, 2, 3, 4, 5, 7, 8, 31, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 1023,
+                                   1024, 1025, 1537, 2048, 4095, 4096, 4097, 8191, 8192, 16384, 32764, 32765])
+@pytest.mark.parametrize("mis", [0, 1, 2, 3])
+def test_plan_covers_rows_and_respects_limits(op, width, mis):
+    for rows in (1, 3, 17, 1024, 131072):
+        x, y = X + 4 * mis, Y + 4 * mis
+        r = RR + 4 * mis
+        p = R.rowred_plan_query(op, x, r, y, rows=rows, width=width)
+        L, T = p.lanes_per_row, p.threads
+        assert L & (L - 1) == 0 and 1 <= L <= 1024
+        assert T % 64 == 0 and 64 <= T <= 1024 and T % L == 0
+        assert p.chunks in CHUNKS
+        assert T <= (1024 if p.chunks <= 8 else 512)
+        assert p.rows_per_group == T // L
+        assert p.grid == -(-rows // p.rows_per_group)
+        assert p.grid * p.rows_per_group >= rows
+        assert p.vector_io == 1  # same alignment everywhere
+        assert p.window == window(x, rows, width)
+        assert L * p.chunks >= p.window
+        # stripe within the private budget: <= 64 floats per lane
+        assert 4 * p.chunks <= 64
+        assert p.policy in (0, 1, 2, 3, 4, 5, 6, 7) and p.reserved == 0
+
+
+def test_plan_for_workload_shapes():
+    # the shapes of the five workloads, aligned buffers
+    nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
+    cases = {(131072, 127): (32, 2, nl | ns | rm), (131072, 257): (64, 2, nl | ns | rm),
+             (131072, 1537): (256, 2, nl | ns | rm), (1024, 4096): (256, 4, nl | ns),
+             (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
+             (17, 257): (32, 3, nl | rm)}
+    for (rows, width), (L, C, pol) in cases.items():
+        p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
+        assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
+
+
+def test_plan_memory_policy():
+    nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
+    # small, every row on a 16-byte boundary: streaming, no remap
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=4096).policy == nl | ns
+    # rows share boundary granules and lanes hold > 2 slots: cached stores + remap
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == nl | rm
+    assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | rm
+    # large aligned matrix: streaming + remap
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=4096).policy == nl | ns | rm
+
+
+def test_plan_reports_4byte_io_on_mixed_alignment():
+    p = R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=10, width=100)
+    assert p.vector_io == 0 and p.window == 25
+    p = R.rowred_plan_query("layernorm_residual", X, RR + 8, Y, rows=10, width=100)
+    assert p.vector_io == 0
+    p = R.rowred_plan_query("layernorm_residual", X + 4, RR + 4, Y + 4, rows=10, width=100)
+    assert p.vector_io == 1 and p.window == 26
+
+
+def test_pages_stripe_arithmetic():
+    # At 4096 columns with 512 lanes of 4-element slots, one row needs
+    # 2 slots per lane: an eight-float stripe per input, the RMSNorm figure in
+    # "Immutable input reuse in Metal reductions" (section "What the
+    # transformation actually preserves").  A 512-lane, 2-chunk plan is
+    # accepted and its window is exactly covered.
+    plan = R.Plan(lanes_per_row=512, rows_per_group=1, chunks=2, threads=512, grid=0)
+    st = R.lib().rowred_run_plan(1, 0, 0, 0, 0, 4096, ctypes.c_float(1e-6), ctypes.byref(plan._c()), None)
+    assert st == R.ROWRED_OK  # rows == 0: validated, nothing launched
+    p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=1024, width=4096)
+    assert p.window == 4096 // 4 == 512 * 2
+
+
+def raw(fn, *args):
+    return getattr(R.lib(), fn)(*args)
+
+
+def f(v):
+    return ctypes.c_float(v)
+
+
+def test_size_errors():
+    assert raw("rowred_rmsnorm", X, Y, -1, 4, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
+    assert raw("rowred_rmsnorm", X, Y, 4, -1, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
+    # empty matrices: OK with nothing launched, even with NULL pointers
+    assert raw("rowred_rmsnorm", None, None, 0, 4, f(1e-6), None) == R.ROWRED_OK
+    assert raw("rowred_softmax", None, None, 7, 0, None) == R.ROWRED_OK
+    assert raw("rowred_layernorm_residual", None, None, None, 0, 0, f(1e-5), None) == R.ROWRED_OK
+    # too wide for one register-resident pass
+    assert raw("rowred_softmax", X, Y, 4, 32769, None) == R.ROWRED_ERR_UNSUPPORTED
+    assert raw("rowred_softmax", X + 4, Y + 4, 4, 32768, None) == R.ROWRED_ERR_UNSUPPORTED
+    assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
+
+
+def test_pointer_errors():
+    assert raw("rowred_rmsnorm", None, Y, 4, 4, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
+    assert raw("rowred_rmsnorm", X, None, 4, 4, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
+    assert raw("rowred_layernorm_residual", X, None, Y, 4, 4, f(1e-5), None) == R.ROWRED_ERR_INVALID_ARG
+    assert raw("rowred_softmax", X + 2, Y, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG  # not 4-byte aligned
+    assert raw("rowred_softmax", X, Y + 1, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
+
+
+def test_eps_errors():
+    for eps in (float("nan"), float("inf"), -1e-6):
+        assert raw("rowred_rmsnorm", X, Y, 4, 4, f(eps), None) == R.ROWRED_ERR_INVALID_ARG
+        assert raw("rowred_layernorm_residual", X, RR, Y, 4, 4, f(eps), None) == R.ROWRED_ERR_INVALID_ARG
+
+
+def test_alias_errors():
+    n = 16 * 64 * 4
+    assert raw("rowred_softmax", X, X, 16, 64, None) == R.ROWRED_ERR_ALIAS
+    assert raw("rowred_softmax", X, X + n - 4, 16, 64, None) == R.ROWRED_ERR_ALIAS
+    assert raw("rowred_rmsnorm", X + n - 4, X, 16, 64, f(1e-6), None) == R.ROWRED_ERR_ALIAS
+    assert raw("rowred_layernorm_residual", X, RR, RR + 64, 16, 64, f(1e-5), None) == R.ROWRED_ERR_ALIAS
+    # x and r may overlap each other (both only read); checked before launch,
+    # so use rows=0 to stop right after the argument checks.
+    assert raw("rowred_layernorm_residual", X, X, Y, 0, 64, f(1e-5), None) == R.ROWRED_OK
+
+
+def bad_plan(**kw):
+    base = dict(lanes_per_row=64, rows_per_group=0, chunks=4, threads=256, grid=0, vector_io=0, window=0)
+    base.update(kw)
+    return R.Plan(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lanes_per_row=48),           # not a power of two
+    dict(lanes_per_row=2048, threads=1024),
+    dict(threads=1056),               # over the 1024-thread workgroup limit
+    dict(threads=96),                 # not a whole number of wavefronts
+    dict(lanes_per_row=512, threads=256),   # row wider than the workgroup
+    dict(chunks=9),                   # no kernel instantiated for 9 chunks
+    dict(chunks=16, threads=1024, lanes_per_row=1024),  # 16 chunks compiled for <= 512 threads
+    dict(chunks=1),                   # 64 lanes x 1 slot does not cover 1024 slots
+    dict(policy=8),                   # unknown policy bit
+    dict(reserved=1),
+])
+def test_run_plan_rejects_bad_plans(kw):
+    c = bad_plan(**kw)._c()
+    st = R.lib().rowred_run_plan(1, X, None, Y, 8, 4096, f(1e-6), ctypes.byref(c), None)
+    assert st == R.ROWRED_ERR_INVALID_ARG, kw
+
+
+def test_run_plan_coverage_depends_on_x_alignment():
+    # 4096 columns from a 16-byte aligned x span 1024 granules (64 x 16 covers
+    # them); shifted by one float they span 1025, which 64 x 16 does not.
+    c = bad_plan(lanes_per_row=64, chunks=16, threads=256)._c()
+    assert R.lib().rowred_run_plan(1, X, None, Y, 0, 4096, f(1e-6), ctypes.byref(c), None) == R.ROWRED_OK
+    assert R.lib().rowred_run_plan(1, X + 4, None, Y, 8, 4096, f(1e-6), ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+
+
+def test_copy_argument_errors():
+    assert raw("rowred_copy", X, Y, 6, None) == R.ROWRED_ERR_INVALID_ARG       # not a multiple of 4
+    assert raw("rowred_copy", X + 4, Y, 8, None) == R.ROWRED_ERR_INVALID_ARG   # not 16-byte aligned
+    assert raw("rowred_copy", X, X + 16, 64, None) == R.ROWRED_ERR_ALIAS
+    assert raw("rowred_copy", None, None, 0, None) == R.ROWRED_OK
+
+
+def test_python_binding_shape_checks():
+    with pytest.raises(ValueError):
+        R.rowred_softmax(X, Y)  # raw addresses need rows/width
+    with pytest.raises(R.RowRedError) as e:
+        R.rowred_softmax(X, X, rows=4, width=4)
+    assert e.value.status == R.ROWRED_ERR_ALIAS
+
+
+def test_xcd_block_remap_is_a_bijection():
+    # Workgroup b runs on XCD b % 8 as that XCD's (b // 8)-th block; the
+    # kernel maps it to row block x*q + min(x, rem) + i.  Every grid size must
+    # give a permutation of [0, G) in which each XCD's blocks are contiguous.
+    for G in list(range(1, 130)) + [4096, 4097, 32768, 131071]:
+        q, rem = divmod(G, 8)
+        seen = []
+        per_xcd = {}
+        for b in range(G):
+            x, i = b % 8, b // 8
+            blk = x * q + min(x, rem) + i
+            seen.append(blk)
+            per_xcd.setdefault(x, []).append(blk)
+        assert sorted(seen) == list(range(G)), G
+        for blks in per_xcd.values():
+            assert blks == list(range(blks[0], blks[0] + len(blks)))
