@@ -7,8 +7,8 @@ A step is one call of every operator of the workload on one batch of seeded
 synthetic input (the default workload: residual LayerNorm, RMSNorm and
 softmax on 1024x4096 FP32, inputs U[-1, 1]).  Inputs and outputs are
 resident in HBM before timing starts.  Each operator's K timed calls run on
-a rotation of >= 3 buffer sets totalling >= 2 GiB, so no call finds its data
-in the 256 MB last-level cache; the K calls are captured in one HIP graph per
+its own rotation of >= 3 buffer sets totalling >= 2 GiB, so no call finds its
+data in the 256 MB last-level cache; the K calls are captured in one HIP graph per
 operator so the host's launch cost does not gate 5-10 us kernels.  HIP
 events on the launch stream bracket each graph replay; an operator's average
 call time is its replay time / K.
@@ -98,9 +98,10 @@ class CaseBuffers:
         R.run_op(self.case.op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
 
 
-def rotation_sets(cases):
-    per_set = sum(algo_bytes(c) for c in cases)
-    return max(3, -(-POOL_BYTES // per_set))
+def rotation_sets(case):
+    """Buffer sets for one case: >= 3 and >= 2 GiB of inputs + outputs, so a
+    call never finds its operands in the 256 MB last-level cache."""
+    return max(3, -(-POOL_BYTES // algo_bytes(case)))
 
 
 # ---------------------------------------------------------------------------
@@ -110,8 +111,8 @@ def rotation_sets(cases):
 def time_workload(cfg, steps, warmup):
     import torch
     cases = synthetic.CONFIGS[cfg]
-    sets = rotation_sets(cases)
-    bufs = [CaseBuffers(c, sets) for c in cases]
+    bufs = [CaseBuffers(c, rotation_sets(c)) for c in cases]
+    sets = [b.sets for b in bufs]
     torch.cuda.synchronize()
     for w in range(warmup):
         for b in bufs:
@@ -223,8 +224,8 @@ def bench(cfg, steps, warmup, cpu_seconds):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg], "config_id": cfg,
                    "cases": [f"{c.op} {c.rows}x{c.width} {c.dist}" for c in cases],
-                   "rotation_sets": sets, "timing": f"one HIP graph of {steps} calls per operator, "
-                                                     f"rotating {sets} buffer sets, HIP events per replay"},
+                   "rotation_sets": sets, "timing": f"one HIP graph of {steps} calls per operator on rotating "
+                                                     f"buffer sets (>= 2 GiB per operator), HIP events per replay"},
         "roofline": roof,
         "ops": ops,
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
@@ -296,6 +297,107 @@ def pmc_pass(cfg):
     print(f"pmc copy {n * 4} bytes read, {n * 4} bytes written", flush=True)
 
 
+# ---------------------------------------------------------------------------
+# profile summaries (from rocprofv3 CSV output)
+# ---------------------------------------------------------------------------
+
+PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {ctr} --output-format csv -d <out_{ctr}> -o run -- "
+           "python3 <repo>/bench.py --pmc --all")
+TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+             "python3 <repo>/bench.py --cpu-seconds 0")
+
+
+def _csv_rows(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def traffic_summary(fetch_csv, write_csv, out_dir):
+    """Write profiles/pmc_traffic_cfg<N>.txt from the two counter passes of
+    `bench.py --pmc --all`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    scaled by what each counter reads for the 256 MiB copy that ends each
+    workload's pass."""
+    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in synthetic.CONFIGS[cfg]]
+    per_cfg = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        i = 0
+        pending = []
+        for row in _csv_rows(path):
+            if row["Counter_Name"] != ctr:
+                continue
+            name = row["Kernel_Name"]
+            if "rows_kernel" in name:
+                cfg, case = expected[i]
+                pending.append((cfg, case, float(row["Counter_Value"]), name))
+                i += 1
+            elif "copy_kernel" in name:
+                copy_kib = float(row["Counter_Value"])
+                for cfg, case, kib, kname in pending:
+                    d = per_cfg.setdefault(cfg, {}).setdefault(f"{case.op} {case.rows}x{case.width}", {})
+                    d[ctr] = kib
+                    d[ctr + "_copy"] = copy_kib
+                    d["kernel"] = kname
+                pending = []
+        if i != len(expected):
+            raise SystemExit(f"{path}: found {i} reduction dispatches, expected {len(expected)}")
+    copy_bytes = 2 ** 28  # each side of the calibration copy
+    h = kernel_source_hash()
+    written = []
+    for cfg, cases in per_cfg.items():
+        lines = [f"# HBM traffic per dispatch, workload {cfg}: {WORKLOAD_NAMES[cfg]}",
+                 "# Two counter passes over the same program, one dispatch per kernel on cold buffers:",
+                 "#   " + PMC_CMD.format(ctr="FETCH_SIZE"),
+                 "#   " + PMC_CMD.format(ctr="WRITE_SIZE"),
+                 "# Counters are KiB per dispatch.  Scale: the copy kernel that ends the pass moves",
+                 f"# {copy_bytes} B each way; read_scale = {copy_bytes} / (FETCH_SIZE_copy * 1024),",
+                 f"# write_scale = {copy_bytes} / (WRITE_SIZE_copy * 1024).",
+                 f"kernel_source_hash: {h}"]
+        for key, d in cases.items():
+            case = next(c for c in synthetic.CONFIGS[cfg] if f"{c.op} {c.rows}x{c.width}" == key)
+            rs = copy_bytes / (d["FETCH_SIZE_copy"] * 1024)
+            ws = copy_bytes / (d["WRITE_SIZE_copy"] * 1024)
+            rd = d["FETCH_SIZE"] * 1024 * rs
+            wr = d["WRITE_SIZE"] * 1024 * ws
+            alg_r = 4 * case.rows * case.width * n_inputs(case.op)
+            alg_w = 4 * case.rows * case.width
+            lines += [f"kernel[{key}]: {d['kernel']}",
+                      f"fetch_kib[{key}]: {d['FETCH_SIZE']:.2f} (copy {d['FETCH_SIZE_copy']:.2f}, "
+                      f"read_scale {rs:.4f})",
+                      f"write_kib[{key}]: {d['WRITE_SIZE']:.2f} (copy {d['WRITE_SIZE_copy']:.2f}, "
+                      f"write_scale {ws:.4f})",
+                      f"read_bytes[{key}]: {rd:.0f} (algorithmic {alg_r}, ratio {rd / alg_r:.4f})",
+                      f"write_bytes[{key}]: {wr:.0f} (algorithmic {alg_w}, ratio {wr / alg_w:.4f})",
+                      f"traffic_bytes[{key}]: {rd + wr:.0f}"]
+        path = os.path.join(out_dir, f"pmc_traffic_cfg{cfg}.txt")
+        open(path, "w").write("\n".join(lines) + "\n")
+        written.append(path)
+    return written
+
+
+def trace_summary(stats_csv, bench_json, out_path):
+    """Write the rocprofv3 kernel statistics of the default benchmark command
+    next to the benchmark's own HIP-event averages."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    lines = [f"# rocprofv3 kernel statistics, workload {b['config']['config_id']}: {b['config']['workload']}",
+             "#   " + TRACE_CMD,
+             f"# kernel_source_hash: {kernel_source_hash()}",
+             "# name | calls | total_ns | average_ns | min_ns | max_ns | percentage"]
+    for r in rows:
+        nm = r["Name"].replace("void rowred::(anonymous namespace)::", "")
+        lines.append(" | ".join([nm, r["Calls"], r["TotalDurationNs"], f"{float(r['AverageNs']):.0f}",
+                                 r["MinNs"], r["MaxNs"], f"{float(r['Percentage']):.2f}"]))
+    lines.append("# benchmark (same command without the profiler): HIP-event average per call")
+    for k, v in b["ops"].items():
+        lines.append(f"bench[{k}]: {v['us_per_call']} us, {v['GB_s']} GB/s")
+    lines.append(f"roofline: {json.dumps(b['roofline'])}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    return out_path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,7 +407,18 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/pmc_traffic_cfg*.txt from two counter passes (no GPU)")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "BENCH_JSON", "OUT"),
+                    help="write a kernel-trace summary (no GPU)")
     args = ap.parse_args(argv)
+    if args.traffic_summary:
+        for p in traffic_summary(*args.traffic_summary, os.path.join(ROOT, "profiles")):
+            print(p)
+        return 0
+    if args.trace_summary:
+        print(trace_summary(*args.trace_summary))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: rows are independent, so N GPUs would each "
                                    "run the same kernel on rows/N; only --gpus 1 is measured"}))

@@ -114,7 +114,8 @@ int finish_plan(const Call &c, rowred_plan *p) {
 
 // The chooser, keyed on the row window and the matrix size; its rules come
 // from sweeps of every geometry and memory policy on MI355X at the workload
-// shapes (widths 127, 257, 1537, 4096, 8192, 32768).
+// shapes (widths 127, 257, 1537, 4096, 8192, 32768), each call on buffers
+// rotated through >= 2 GiB so that no call runs from the last-level cache.
 //
 // Geometry: every input element is loaded once into registers, so the
 // per-lane stripe sets register use and the serial work per lane.  Short
@@ -123,29 +124,32 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // most 32 MiB, which run in a single round of waves where fewer, fatter
 // waves amortise the wave start-up.  L is the smallest power of two meeting
 // that bound (at most 1024), chunks the smallest instantiated count covering
-// the window.  Workgroups have 256 threads, or L when a row needs more.
+// the window.  Workgroups have max(256, L) threads for small inputs and
+// max(512, L) for large ones.
 //
 // Memory policy: streaming (non-temporal) stores are fastest when each
 // row's stores leave in one or two instructions.  Where neighbouring rows
-// share a 16-byte granule (rows not starting on 16-byte boundaries) and a lane
-// holds more than 2 slots, the two partial writes of a shared line are issued
-// far apart and streaming stores turn them into separate partial
+// share a 16-byte granule (rows not starting on 16-byte boundaries) and a
+// lane holds more than 2 slots, the two partial writes of a shared line are
+// issued far apart and streaming stores turn them into separate partial
 // write-backs; cached stores let L2 merge them.  The XCD remap (each XCD
-// walks one contiguous range of rows) pays off once the grid runs in several
-// rounds (> 64 MiB per input) or when rows share boundary granules.
+// walks one contiguous range of rows) pays off for aligned rows once the grid
+// runs in several rounds (> 64 MiB per input).
 void choose_plan(const Call &c, rowred_plan *p) {
   const int64_t w = c.window;
   const int64_t in_bytes = c.rows * c.width * 4;
-  const int64_t max_chunks = in_bytes <= (int64_t(32) << 20) ? 4 : 2;
+  const bool small = in_bytes <= (int64_t(32) << 20);
+  const int64_t max_chunks = small ? 4 : 2;
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
   p->lanes_per_row = (int32_t)L;
   p->chunks = round_up_chunks((w + L - 1) / L);
-  p->threads = (int32_t)(L > 256 ? L : 256);
+  const int64_t t_min = small ? 256 : 512;
+  p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
   int policy = kPolicyNtLoads;
   if (rows_aligned || p->chunks <= 2) policy |= kPolicyNtStores;
-  if (!rows_aligned || in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
+  if (rows_aligned && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
   p->policy = policy;
   p->reserved = 0;
 }
