@@ -144,9 +144,13 @@ typedef struct rowred_plan {
 
 /* Memory policy bits of a plan.  They change speed, never results. */
 enum rowred_policy {
-  ROWRED_POLICY_NT_LOADS = 1,  /* loads carry the non-temporal (streaming) hint */
-  ROWRED_POLICY_NT_STORES = 2, /* stores carry the non-temporal hint */
-  ROWRED_POLICY_XCD_REMAP = 4  /* each XCD walks one contiguous range of row blocks */
+  ROWRED_POLICY_NT_LOADS = 1,   /* loads carry the non-temporal (streaming) hint */
+  ROWRED_POLICY_NT_STORES = 2,  /* stores carry the non-temporal hint */
+  ROWRED_POLICY_XCD_REMAP = 4,  /* each XCD walks one contiguous range of row blocks */
+  ROWRED_POLICY_STAGE_STORES = 8 /* a workgroup's outputs (its rows are consecutive) are
+                                    assembled in LDS and stored as whole 16-byte granules by
+                                    consecutive threads; needs y at x's 16-byte phase,
+                                    threads <= 512 and chunks <= 4 */
 };
 
 /*

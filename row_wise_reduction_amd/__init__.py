@@ -31,6 +31,7 @@ ROWRED_ERR_HIP = 4
 ROWRED_POLICY_NT_LOADS = 1
 ROWRED_POLICY_NT_STORES = 2
 ROWRED_POLICY_XCD_REMAP = 4
+ROWRED_POLICY_STAGE_STORES = 8
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1

@@ -100,12 +100,14 @@ int finish_plan(const Call &c, rowred_plan *p) {
   if (!is_pow2(L) || L > 1024) return ROWRED_ERR_INVALID_ARG;
   if (T < 64 || T > 1024 || T % 64 != 0 || T % L != 0) return ROWRED_ERR_INVALID_ARG;
   if (!chunks_supported(p->chunks) || T > max_threads_for_chunks(p->chunks)) return ROWRED_ERR_INVALID_ARG;
-  if (p->policy & ~(kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~kPolicyAll) return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
   if (L * p->chunks < p->window) return ROWRED_ERR_INVALID_ARG;
   p->rows_per_group = (int32_t)(T / L);
+  if ((p->policy & kPolicyStageStores) && (!c.y_vec || T > kMaxStageThreads || p->chunks > kMaxStageChunks))
+    return ROWRED_ERR_INVALID_ARG;
   p->grid = (c.rows + p->rows_per_group - 1) / p->rows_per_group;
   // The dispatch packet counts work-items in 32 bits.
   if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
@@ -122,33 +124,43 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // stripes with many lanes per row win: at most 2 slots (8 floats) per lane --
 // the pages' 8-float stripe at 4096 columns -- or 4 slots for inputs of at
 // most 32 MiB, which run in a single round of waves where fewer, fatter
-// waves amortise the wave start-up.  L is the smallest power of two meeting
+// waves amortise the wave start-up, and for rows of at most 256 granules
+// whose outputs are staged in LDS (below), where 4 slots per lane measured
+// 4-8% faster than 2 (at 1537 columns 2 slots stay 10% faster).  L is the smallest power of two meeting
 // that bound (at most 1024), chunks the smallest instantiated count covering
 // the window.  Workgroups have max(256, L) threads for small inputs and
 // max(512, L) for large ones.
 //
-// Memory policy: streaming (non-temporal) stores are fastest when each
-// row's stores leave in one or two instructions.  Where neighbouring rows
-// share a 16-byte granule (rows not starting on 16-byte boundaries) and a
-// lane holds more than 2 slots, the two partial writes of a shared line are
-// issued far apart and streaming stores turn them into separate partial
-// write-backs; cached stores let L2 merge them.  The XCD remap (each XCD
-// walks one contiguous range of rows) pays off for aligned rows once the grid
-// runs in several rounds (> 64 MiB per input).
+// Memory policy: streaming (non-temporal) stores are fastest.  Where rows
+// do not start on 16-byte boundaries, the cache lines at row boundaries
+// hold two rows' outputs written by different lanes at different times,
+// and each part leaves as its own partial line write-back (up to 1.46x the
+// algorithmic write traffic at width 127, and 3x slower with streaming
+// stores when a lane holds more than 2 slots).  Staging a workgroup's
+// outputs in LDS and storing them as whole granules from consecutive threads
+// removes that (ROWRED_POLICY_STAGE_STORES); without it (y at another
+// 16-byte phase than x) stores stay cached beyond 2 slots per lane.  The XCD
+// remap (each XCD walks one contiguous range of rows) pays off for aligned
+// rows once the grid runs in several rounds (> 64 MiB per input).
 void choose_plan(const Call &c, rowred_plan *p) {
   const int64_t w = c.window;
   const int64_t in_bytes = c.rows * c.width * 4;
   const bool small = in_bytes <= (int64_t(32) << 20);
-  const int64_t max_chunks = small ? 4 : 2;
+  const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+  const bool stage_ok = !rows_aligned && c.y_vec;
+  // Staged rows that fit one wavefront (<= 64 lanes x 4 slots) store through
+  // LDS, so their lanes can hold more slots.
+  const int64_t max_chunks = (small || (stage_ok && w <= 256)) ? 4 : 2;
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
   p->lanes_per_row = (int32_t)L;
   p->chunks = round_up_chunks((w + L - 1) / L);
   const int64_t t_min = small ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
-  const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+  const bool can_stage = stage_ok && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = kPolicyNtLoads;
-  if (rows_aligned || p->chunks <= 2) policy |= kPolicyNtStores;
+  if (rows_aligned || can_stage || p->chunks <= 2) policy |= kPolicyNtStores;
+  if (can_stage) policy |= kPolicyStageStores;
   if (rows_aligned && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
   p->policy = policy;
   p->reserved = 0;

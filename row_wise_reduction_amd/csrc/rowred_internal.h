@@ -27,6 +27,13 @@ struct RowArgs {
 constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;
 constexpr int kPolicyNtStores = ROWRED_POLICY_NT_STORES;
 constexpr int kPolicyXcdRemap = ROWRED_POLICY_XCD_REMAP;
+constexpr int kPolicyStageStores = ROWRED_POLICY_STAGE_STORES;
+constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores;
+constexpr int kMaxStageThreads = 512;  // workgroup size the staged stores support
+constexpr int kMaxStageChunks = 4;     // chunks per lane the staged stores are compiled for
+// LDS for a staged workgroup: its rows span at most threads*chunks granules
+// of the x window, plus the two partial granules at the run's ends.
+constexpr size_t stage_lds_bytes(int chunks, int threads) { return ((size_t)threads * chunks + 2) * 16; }
 
 // Chunk counts for which kernels are instantiated (slots per lane).
 constexpr int kChunkSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16};

@@ -320,10 +320,9 @@ __global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs
   }
 
   // ---- predicated store: replayed row slots write nothing.
-  if (!live) return;
-  float *yrow = a.y + base;
   auto store_rows = [&](auto nt) {
     constexpr bool NT = decltype(nt)::value;
+    float *yrow = a.y + base;
     if (a.y_vec) {
       f32x4 *yw = reinterpret_cast<f32x4 *>(yrow - off);
 #pragma unroll
@@ -346,6 +345,67 @@ __global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs
           if (valid(c, j)) store_g<NT>(yrow + elem(c, j), s[4 * c + j]);
     }
   };
+
+  // Staged stores (ROWRED_POLICY_STAGE_STORES; the host sets it only with y
+  // at x's 16-byte phase, <= 512 threads and <= 4 chunks -- short rows; wider
+  // stripes compile without it).  The workgroup's rows are consecutive, so
+  // its outputs form one contiguous run of y.  When rows do not start on
+  // 16-byte boundaries, the cache lines at row boundaries hold two rows'
+  // outputs written by different lanes at different times, and each part
+  // leaves as its own partial line write-back.  Here every lane first puts
+  // its outputs into the run's image in LDS (whole granules land 16-byte
+  // aligned there, since the run and the row share the phase), and after
+  // one barrier consecutive threads store consecutive whole granules, so each
+  // line is written by one instruction; only the run's two end granules are
+  // partial.
+  if constexpr (C <= kMaxStageChunks) {
+    if (a.policy & kPolicyStageStores) {
+      extern __shared__ f32x4 stage[];  // stage_lds_bytes(C, threads), sized at launch
+      float *stage_f = reinterpret_cast<float *>(stage);
+      const int64_t row_first = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0) * rows_per_group;
+      const int64_t row_stop = row_first + rows_per_group < a.rows ? row_first + rows_per_group : a.rows;
+      const int64_t e_begin = row_first * (int64_t)width, e_end = row_stop * (int64_t)width;
+      const int fb = (int)((((uintptr_t)a.x >> 2) + e_begin) & 3);  // phase of the run's first element
+      if (live) {
+        // LDS float index of this row's element e: fb + slot*width + e;
+        // of its granule k: 4 * (granule0 + k) with granule0 below.
+        const int granule0 = (fb + slot * width - off) >> 2;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int k = c * L + li;
+          const int e0 = 4 * k - off;
+          if (e0 >= 0 && e0 + 4 <= width) {
+            stage[granule0 + k] = f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]};
+          } else if (k < nwin) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if ((unsigned)(e0 + j) < (unsigned)width) stage_f[4 * (granule0 + k) + j] = s[4 * c + j];
+          }
+        }
+      }
+      __syncthreads();
+      const int n_granules = (int)((fb + (e_end - e_begin) + 3) >> 2);
+      f32x4 *yg = reinterpret_cast<f32x4 *>(a.y + e_begin - fb);  // 16-byte aligned: y shares x's phase
+      auto store_run = [&](auto nt) {
+        constexpr bool NT = decltype(nt)::value;
+        for (int g = threadIdx.x; g < n_granules; g += blockDim.x) {
+          const f32x4 v = stage[g];
+          const int64_t e0 = e_begin - fb + 4 * (int64_t)g;
+          if (e0 >= e_begin && e0 + 4 <= e_end) {
+            store_g<NT>(yg + g, v);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (e0 + j >= e_begin && e0 + j < e_end) store_g<NT>(a.y + e0 + j, v[j]);
+          }
+        }
+      };
+      if (a.policy & kPolicyNtStores) store_run(std::true_type{});
+      else store_run(std::false_type{});
+      return;
+    }
+  }
+  if (!live) return;
   if (a.policy & kPolicyNtStores) store_rows(std::true_type{});
   else store_rows(std::false_type{});
 }
@@ -398,7 +458,8 @@ int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &ar
   KernelFn fn = kKernels[op][ci];
   RowArgs a = args;
   void *params[] = {&a};
-  return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)grid), dim3(threads), params, 0,
+  const size_t lds = (a.policy & kPolicyStageStores) ? stage_lds_bytes(chunks, threads) : 0;
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)grid), dim3(threads), params, lds,
                               stream);
 }
 

@@ -83,16 +83,17 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
         assert L * p.chunks >= p.window
         # stripe within the private budget: <= 64 floats per lane
         assert 4 * p.chunks <= 64
-        assert p.policy in (0, 1, 2, 3, 4, 5, 6, 7) and p.reserved == 0
+        assert 0 <= p.policy < 16 and p.reserved == 0
 
 
 def test_plan_for_workload_shapes():
     # the shapes of the five workloads, aligned buffers
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
-    cases = {(131072, 127): (32, 2, nl | ns), (131072, 257): (64, 2, nl | ns),
-             (131072, 1537): (256, 2, nl | ns), (1024, 4096): (256, 4, nl | ns),
+    st = R.ROWRED_POLICY_STAGE_STORES
+    cases = {(131072, 127): (16, 3, nl | ns | st), (131072, 257): (32, 3, nl | ns | st),
+             (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
-             (17, 257): (32, 3, nl)}
+             (17, 257): (32, 3, nl | ns | st)}
     for (rows, width), (L, C, pol) in cases.items():
         p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
@@ -100,11 +101,14 @@ def test_plan_for_workload_shapes():
 
 def test_plan_memory_policy():
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
-    # small, every row on a 16-byte boundary: streaming, no remap
+    st = R.ROWRED_POLICY_STAGE_STORES
+    # small, every row on a 16-byte boundary: streaming, no remap, no staging
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=4096).policy == nl | ns
-    # rows share boundary granules and lanes hold > 2 slots: cached stores
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == nl
-    assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl
+    # rows share boundary lines: outputs staged in LDS, streaming stores
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == nl | ns | st
+    assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns | st
+    # shared lines but y at another phase (no staging), > 2 slots per lane: cached stores
+    assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=64, width=127).policy == nl
     # large aligned matrix: streaming + remap
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=4096).policy == nl | ns | rm
 
@@ -192,13 +196,28 @@ def bad_plan(**kw):
     dict(chunks=9),                   # no kernel instantiated for 9 chunks
     dict(chunks=16, threads=1024, lanes_per_row=1024),  # 16 chunks compiled for <= 512 threads
     dict(chunks=1),                   # 64 lanes x 1 slot does not cover 1024 slots
-    dict(policy=8),                   # unknown policy bit
+    dict(policy=16),                  # unknown policy bit
+    dict(policy=8, chunks=16, lanes_per_row=64, threads=256),  # staging compiled for <= 4 chunks only
+    dict(policy=8, lanes_per_row=1024, chunks=1, threads=1024),  # staging needs <= 512 threads
     dict(reserved=1),
 ])
 def test_run_plan_rejects_bad_plans(kw):
     c = bad_plan(**kw)._c()
     st = R.lib().rowred_run_plan(1, X, None, Y, 8, 4096, f(1e-6), ctypes.byref(c), None)
     assert st == R.ROWRED_ERR_INVALID_ARG, kw
+
+
+def test_stage_policy_preconditions():
+    m = R.ROWRED_POLICY_STAGE_STORES
+    ok = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=m)._c()
+    assert R.lib().rowred_run_plan(1, X, None, Y, 0, 127, f(1e-6), ctypes.byref(ok), None) == R.ROWRED_OK
+    # y at another 16-byte phase than x
+    assert R.lib().rowred_run_plan(1, X, None, Y + 4, 8, 127, f(1e-6), ctypes.byref(ok), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    # more than 512 threads
+    big = bad_plan(lanes_per_row=32, chunks=2, threads=1024, policy=m)._c()
+    assert R.lib().rowred_run_plan(1, X, None, Y, 8, 127, f(1e-6), ctypes.byref(big), None) == \
+        R.ROWRED_ERR_INVALID_ARG
 
 
 def test_run_plan_coverage_depends_on_x_alignment():

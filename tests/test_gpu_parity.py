@@ -114,12 +114,14 @@ def all_plans(window):
             for T in sorted({max(64, L), 256, 1024 if C <= 8 else 512}):
                 if T < L or T % L or T > (1024 if C <= 8 else 512):
                     continue
-                for policy in (0, 3, 4, 7):
+                for policy in (0, 3, 4, 7, 8, 11, 15):
+                    if policy & R.ROWRED_POLICY_STAGE_STORES and (C > 4 or T > 512):
+                        continue
                     yield R.Plan(lanes_per_row=L, rows_per_group=0, chunks=C, threads=T, grid=0, policy=policy)
 
 
 @pytest.mark.parametrize("op", OPS)
-@pytest.mark.parametrize("width", [3, 100, 257, 1000, 4096])
+@pytest.mark.parametrize("width", [3, 5, 100, 257, 1000, 4096])
 def test_every_plan(op, width):
     rows = 67
     x, r = inputs(op, rows, width, seed=11 * width)
@@ -131,6 +133,30 @@ def test_every_plan(op, width):
         assert_close(run_case(op, x, r, plan=plan, shift=(1, 1, 1)), ref, f"{op} {width} {plan}")
         n += 1
     assert n >= 3
+
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("width", [1, 2, 3, 4, 5, 6, 7, 9, 127, 129, 255, 257, 513, 1023])
+@pytest.mark.parametrize("shift", [0, 1, 3])
+def test_staged_stores(op, width, shift):
+    """Outputs assembled in LDS and stored as whole granules: several
+    geometries, rows that end the matrix mid-workgroup, every phase."""
+    window = (width + 3 + 3) // 4
+    for L in (1, 4, 8, 16, 32, 64, 128, 256):
+        C = next((c for c in (1, 2, 3, 4) if L * c >= window), None)
+        if C is None:
+            continue
+        for T in (64, 256, 512):
+            if T < L:
+                continue
+            P = T // L
+            for rows in sorted({1, 2, P - 1, P, P + 1, 2 * P + 3} - {0}):
+                x, r = inputs(op, rows, width, seed=width * 131 + rows + shift)
+                plan = R.Plan(lanes_per_row=L, rows_per_group=0, chunks=C, threads=T, grid=0,
+                              policy=R.ROWRED_POLICY_STAGE_STORES | R.ROWRED_POLICY_NT_STORES)
+                print_case(op, width, shift, L, C, T, rows)
+                assert_close(run_case(op, x, r, plan=plan, shift=(shift, shift, shift)), oracle_of(op, x, r),
+                             f"{op} staged w{width} L{L} C{C} T{T} rows {rows} shift {shift}")
 
 
 # ---------------------------------------------------------------------------

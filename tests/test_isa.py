@@ -5,7 +5,8 @@
 * VGPR counts fit the workgroup sizes the kernels are launched with;
 * 16-byte loads and stores are used; no MFMA (nothing here is a contraction);
 * no packed-FP32 VALU instructions;
-* barriers only in kernels that fold cross-wave partials.
+* barriers only where cross-wave partials are folded or outputs are
+  staged in LDS.
 """
 import os
 import re
@@ -97,8 +98,10 @@ def test_barriers_only_where_partials_are_folded(asm):
     assert "s_barrier" not in kernel_body(asm, copy)
     for name in kernel_meta(asm):
         if "rows_kernel" in name:
-            # RMSNorm folds once, softmax and LayerNorm twice.
+            # RMSNorm folds once, softmax and LayerNorm twice; kernels of at
+            # most 4 chunks add one for the staged stores.
             n = kernel_body(asm, name).count("s_barrier")
             dn = demangle(name)
-            want = 1 if "rows_kernel<1," in dn else 2
+            chunks = int(dn.split("rows_kernel<")[1].split(",")[1].split(">")[0])
+            want = (1 if "rows_kernel<1," in dn else 2) + (1 if chunks <= 4 else 0)
             assert n == want, (dn, n)
