@@ -18,9 +18,11 @@ one write of the output, 4 B per element each) divided by its time.  The
 JSON line also carries the roofline of the dominant kernel, the FP64 CPU
 oracle's throughput on host cores, and per-operator figures.
 
-    python bench.py --pmc       # counter pass: one dispatch of each kernel on
-                                # cold buffers + a 256 MiB copy for calibration
-    python bench.py --all       # one JSON line per workload (1..5)
+    python bench.py --pmc --all # counter pass: one dispatch of each kernel of
+                                # workloads 1..7 on cold buffers, + a 256 MiB
+                                # copy per workload for calibration
+    python bench.py --all       # one JSON line per core workload (1..5)
+    python bench.py --next      # plain and affine LayerNorm (6, 7)
 """
 from __future__ import annotations
 
@@ -53,7 +55,12 @@ WORKLOAD_NAMES = {
     3: "RMSNorm + softmax, 131072 x {127, 257, 1537}, N(0,1)",
     4: "residual LayerNorm + RMSNorm + softmax, 16384x8192, U[-1,1]",
     5: "softmax stress, 8192x32768, 8*N(0,1) + U[-80,80] row offsets, 1% -inf",
+    6: "plain LayerNorm (no residual), 1024x4096 and 16384x8192, U[-1,1]",
+    7: "affine LayerNorm (gamma, beta), 1024x4096 and 16384x8192, U[-1,1]",
 }
+CORE = (1, 2, 3, 4, 5)
+NEXT = (6, 7)
+WORKLOADS = {**synthetic.CONFIGS, **synthetic.NEXT_CONFIGS}
 
 
 def n_inputs(op):
@@ -61,7 +68,10 @@ def n_inputs(op):
 
 
 def algo_bytes(case):
-    return 4 * case.rows * case.width * (n_inputs(case.op) + 1)
+    """One read of every input element, one write of every output element;
+    affine LayerNorm also reads gamma and beta once."""
+    extra = 8 * case.width if case.op == "layernorm_affine" else 0
+    return 4 * case.rows * case.width * (n_inputs(case.op) + 1) + extra
 
 
 def kernel_source_hash():
@@ -85,6 +95,12 @@ class CaseBuffers:
         x = synthetic.case_input(case, "x")
         r = synthetic.case_input(case, "r") if case.op == "layernorm_residual" else None
         self.host_x, self.host_r = x, r
+        self.host_g = self.host_b = None
+        self.g = self.b = None
+        if case.op == "layernorm_affine":
+            self.host_g, self.host_b = synthetic.affine_vectors(case)
+            self.g = torch.from_numpy(self.host_g).cuda()
+            self.b = torch.from_numpy(self.host_b).cuda()
         xd = torch.from_numpy(x).cuda()
         rd = torch.from_numpy(r).cuda() if r is not None else None
         self.x = [xd] + [xd.clone() for _ in range(sets - 1)]
@@ -95,7 +111,16 @@ class CaseBuffers:
     def call(self, i):
         import row_wise_reduction_amd as R
         k = i % self.sets
-        R.run_op(self.case.op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
+        op = self.case.op
+        if op in ("layernorm", "layernorm_affine"):
+            R.rowred_layernorm(self.x[k], None, self.g, self.b, self.y[k], eps=self.case.eps)
+        else:
+            R.run_op(op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
+
+    def oracle(self, rows):
+        import oracle
+        return oracle.run_op(self.case.op, self.host_x[:rows], self.host_r[:rows] if self.host_r is not None else None,
+                             eps=self.case.eps, gamma=self.host_g, beta=self.host_b)
 
 
 def rotation_sets(case):
@@ -110,7 +135,7 @@ def rotation_sets(case):
 
 def time_workload(cfg, steps, warmup):
     import torch
-    cases = synthetic.CONFIGS[cfg]
+    cases = WORKLOADS[cfg]
     bufs = [CaseBuffers(c, rotation_sets(c)) for c in cases]
     sets = [b.sets for b in bufs]
     torch.cuda.synchronize()
@@ -164,14 +189,14 @@ def cpu_baseline(cases, bufs, seconds):
         probe_rows = max(1, min(c.rows, (1 << 20) // c.width))
         t = time.perf_counter()
         oracle.run_op(c.op, b.host_x[:probe_rows], b.host_r[:probe_rows] if b.host_r is not None else None,
-                      eps=c.eps, threads=threads)
+                      eps=c.eps, threads=threads, gamma=b.host_g, beta=b.host_b)
         dt = max(time.perf_counter() - t, 1e-6)
         rows = int(min(c.rows, max(probe_rows, probe_rows * budget / dt)))
         reps = 0
         t = time.perf_counter()
         while True:
             oracle.run_op(c.op, b.host_x[:rows], b.host_r[:rows] if b.host_r is not None else None,
-                          eps=c.eps, threads=threads)
+                          eps=c.eps, threads=threads, gamma=b.host_g, beta=b.host_b)
             reps += 1
             if time.perf_counter() - t >= budget or reps >= 1000:
                 break
@@ -279,7 +304,7 @@ def pmc_pass(cfg):
     import torch
 
     import row_wise_reduction_amd as R
-    cases = synthetic.CONFIGS[cfg]
+    cases = WORKLOADS[cfg]
     bufs = [CaseBuffers(c, 1) for c in cases]
     flush = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
@@ -319,7 +344,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir):
     `bench.py --pmc --all`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     scaled by what each counter reads for the 256 MiB copy that ends each
     workload's pass."""
-    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in synthetic.CONFIGS[cfg]]
+    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]]
     per_cfg = {}
     for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         i = 0
@@ -355,12 +380,12 @@ def traffic_summary(fetch_csv, write_csv, out_dir):
                  f"# write_scale = {copy_bytes} / (WRITE_SIZE_copy * 1024).",
                  f"kernel_source_hash: {h}"]
         for key, d in cases.items():
-            case = next(c for c in synthetic.CONFIGS[cfg] if f"{c.op} {c.rows}x{c.width}" == key)
+            case = next(c for c in WORKLOADS[cfg] if f"{c.op} {c.rows}x{c.width}" == key)
             rs = copy_bytes / (d["FETCH_SIZE_copy"] * 1024)
             ws = copy_bytes / (d["WRITE_SIZE_copy"] * 1024)
             rd = d["FETCH_SIZE"] * 1024 * rs
             wr = d["WRITE_SIZE"] * 1024 * ws
-            alg_r = 4 * case.rows * case.width * n_inputs(case.op)
+            alg_r = algo_bytes(case) - 4 * case.rows * case.width
             alg_w = 4 * case.rows * case.width
             lines += [f"kernel[{key}]: {d['kernel']}",
                       f"fetch_kib[{key}]: {d['FETCH_SIZE']:.2f} (copy {d['FETCH_SIZE_copy']:.2f}, "
@@ -404,7 +429,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
+    ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
+    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6, 7)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -429,11 +455,11 @@ def main(argv=None):
         return 1
     import row_wise_reduction_amd as R
     R.lib()  # fail loudly if the HIP library is not built
-    cfgs = sorted(WORKLOAD_NAMES) if args.all else [args.config]
     if args.pmc:
-        for cfg in cfgs:
+        for cfg in (sorted(WORKLOAD_NAMES) if args.all else [args.config]):
             pmc_pass(cfg)
         return 0
+    cfgs = list(CORE) if args.all else list(NEXT) if args.next else [args.config]
     for cfg in cfgs:
         res = bench(cfg, args.steps, args.warmup, args.cpu_seconds if cfg == cfgs[0] else 0.0)
         print(json.dumps(res), flush=True)

@@ -95,6 +95,25 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
                               hipStream_t stream);
 
 /*
+ * LayerNorm with an optional residual and optional affine vectors, per row i:
+ *   c = x_i (+ r_i);  mean, d, var as above;  y_ij = d_j / sqrt(var + eps)
+ *   (* gamma_j) (+ beta_j).
+ * r, gamma and beta may each be NULL: r = NULL is plain LayerNorm, the form
+ * timed next to softmax and RMSNorm in "Immutable input reuse in Metal
+ * reductions", section "Fixed-width GPU and dispatch results"; gamma/beta
+ * are the affine form named in the tolerance list of "Cooperating-program
+ * packing: implementation and fixed-plan evidence", section "Predeclared
+ * comparison and measurement".  gamma and beta hold `width` floats each
+ * (4-byte aligned, read only, must not overlap y).  With all three NULL
+ * this is the no-affine LayerNorm of the same page's "Validation" section.
+ * With gamma or beta the row cap is 6144 granules (24576 floats for 16-byte
+ * aligned rows); wider rows give ROWRED_ERR_UNSUPPORTED.
+ */
+int rowred_layernorm(const float *x, const float *r, const float *gamma,
+                     const float *beta, float *y, int64_t rows, int64_t width,
+                     float eps, hipStream_t stream);
+
+/*
  * RMSNorm without weight, per row i:  y_i = x_i / sqrt(sum(x_i^2)/width + eps).
  * "Immutable input reuse in Metal reductions", section "What the
  * transformation actually preserves", gives its phases (one sum-of-squares
@@ -133,8 +152,9 @@ int rowred_softmax(const float *x, float *y, int64_t rows, int64_t width,
 typedef struct rowred_plan {
   int32_t lanes_per_row;  /* L: power of two, 1..1024 */
   int32_t rows_per_group; /* threads / L */
-  int32_t chunks;         /* 16-byte slots per lane: 1..8, 10, 12 or 16 */
-  int32_t threads;        /* workgroup size: multiple of 64, <= 1024 (<= 512 when chunks > 8) */
+  int32_t chunks;         /* 16-byte slots per lane: 1..8, 10, 12 or 16 (affine LayerNorm: <= 12) */
+  int32_t threads;        /* workgroup size: multiple of 64, <= 1024 (<= 512 when chunks > 8,
+                             and for affine LayerNorm when chunks >= 7) */
   int64_t grid;           /* workgroups launched: ceil(rows / rows_per_group) */
   int32_t vector_io;      /* 1: r and y share x's address modulo 16 (all accesses 16 bytes) */
   int32_t window;         /* largest number of 16-byte granules a row of x spans (L*chunks covers it) */
@@ -156,7 +176,8 @@ enum rowred_policy {
 /*
  * Host-only: fill *out with the plan the matching entry point would launch
  * for these arguments (x, r, y are only inspected for their alignment; r may
- * be NULL for ops without a residual).  No device work, callable without a
+ * be NULL: for ROWRED_OP_LAYERNORM_RESIDUAL that is the plan of
+ * rowred_layernorm without a residual).  No device work, callable without a
  * GPU.  Returns the status the entry point would return before launching.
  */
 int rowred_plan_query(int op, const float *x, const float *r, const float *y,
@@ -174,6 +195,12 @@ int rowred_plan_query(int op, const float *x, const float *r, const float *y,
 int rowred_run_plan(int op, const float *x, const float *r, float *y,
                     int64_t rows, int64_t width, float eps,
                     const rowred_plan *plan, hipStream_t stream);
+
+/* rowred_layernorm with an explicit plan (as rowred_run_plan). */
+int rowred_layernorm_run_plan(const float *x, const float *r, const float *gamma,
+                              const float *beta, float *y, int64_t rows,
+                              int64_t width, float eps, const rowred_plan *plan,
+                              hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *rowred_status_string(int status);

@@ -210,10 +210,13 @@ def row_minmax(x, threads=None):
     return lo, hi
 
 
-def run_op(op: str, x, r=None, eps=None, threads=None):
-    """Dispatch by operator name: 'layernorm_residual', 'rmsnorm', 'softmax'."""
+def run_op(op: str, x, r=None, eps=None, threads=None, gamma=None, beta=None):
+    """Dispatch by operator name: 'layernorm_residual', 'layernorm' (r, gamma,
+    beta optional), 'layernorm_affine', 'rmsnorm', 'softmax'."""
     if op == "layernorm_residual":
         return layernorm_residual(x, r, eps=1e-5 if eps is None else eps, threads=threads)
+    if op in ("layernorm", "layernorm_affine"):
+        return layernorm(x, r, eps=1e-5 if eps is None else eps, gamma=gamma, beta=beta, threads=threads)
     if op == "rmsnorm":
         return rmsnorm(x, eps=1e-6 if eps is None else eps, threads=threads)
     if op == "softmax":

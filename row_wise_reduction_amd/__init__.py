@@ -86,6 +86,8 @@ def lib():
         sigs = {
             "rowred_layernorm_residual": [_P, _P, _P, _I64, _I64, ctypes.c_float, _P],
             "rowred_rmsnorm": [_P, _P, _I64, _I64, ctypes.c_float, _P],
+            "rowred_layernorm": [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P],
+            "rowred_layernorm_run_plan": [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
             "rowred_softmax": [_P, _P, _I64, _I64, _P],
             "rowred_plan_query": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan)],
             "rowred_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
@@ -172,6 +174,38 @@ def rowred_layernorm_residual(x, r, y, rows=None, width=None, eps=1e-5, stream=N
     rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
     st = lib().rowred_layernorm_residual(mx[0], mr[0], my[0], rows, width, float(eps), _stream(stream, x, r, y))
     _check(st, "rowred_layernorm_residual")
+
+
+def _vector(v, name, width):
+    """Address of a length-`width` vector (tensor or raw address), or None."""
+    if v is None:
+        return None
+    if _is_tensor(v):
+        addr, r, w = _matrix(v, name)
+        if r * w != width:
+            raise ValueError(f"{name} must hold width={width} floats")
+        return addr
+    return int(v)
+
+
+def rowred_layernorm(x, r, gamma, beta, y, rows=None, width=None, eps=1e-5, stream=None):
+    """LayerNorm with optional residual r and affine gamma/beta (each may be None)."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    st = lib().rowred_layernorm(mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width), my[0],
+                                rows, width, float(eps), _stream(stream, x, r, gamma, beta, y))
+    _check(st, "rowred_layernorm")
+
+
+def rowred_layernorm_run_plan(x, r, gamma, beta, y, plan: "Plan", rows=None, width=None, eps=1e-5, stream=None):
+    """rowred_layernorm with an explicit launch plan."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    c = plan._c()
+    st = lib().rowred_layernorm_run_plan(mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width),
+                                         my[0], rows, width, float(eps), ctypes.byref(c),
+                                         _stream(stream, x, r, gamma, beta, y))
+    _check(st, "rowred_layernorm_run_plan")
 
 
 def rowred_rmsnorm(x, y, rows=None, width=None, eps=1e-6, stream=None):

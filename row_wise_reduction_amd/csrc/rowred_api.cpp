@@ -40,6 +40,7 @@ int round_up_chunks(int64_t want) {
 struct Call {
   int op;
   const float *x, *r;
+  const float *gamma = nullptr, *beta = nullptr;  // LayerNorm only
   float *y;
   int64_t rows, width;
   bool r_vec, y_vec;  // r / y share x's address modulo 16
@@ -94,12 +95,17 @@ int check_call(int op, const float *x, const float *r, const float *y, int64_t r
   return ROWRED_OK;
 }
 
+// The kernel operator a call runs: affine LayerNorm has its own kernels.
+int kernel_op(const Call &c) { return (c.gamma || c.beta) ? kKernelOpLayerNormAffine : c.op; }
+
 // Fill grid / rows_per_group / window and check every plan constraint.
 int finish_plan(const Call &c, rowred_plan *p) {
   const int64_t L = p->lanes_per_row, T = p->threads;
   if (!is_pow2(L) || L > 1024) return ROWRED_ERR_INVALID_ARG;
   if (T < 64 || T > 1024 || T % 64 != 0 || T % L != 0) return ROWRED_ERR_INVALID_ARG;
-  if (!chunks_supported(p->chunks) || T > max_threads_for_chunks(p->chunks)) return ROWRED_ERR_INVALID_ARG;
+  const int kop = kernel_op(c);
+  if (!chunks_supported(p->chunks) || !kernel_exists(kop, p->chunks) || T > max_threads_for(kop, p->chunks))
+    return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~kPolicyAll) return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
@@ -153,11 +159,20 @@ void choose_plan(const Call &c, rowred_plan *p) {
   const int64_t max_chunks = (small || (stage_ok && w <= 256)) ? 4 : 2;
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
+  int chunks = round_up_chunks((w + L - 1) / L);
+  const int kop = kernel_op(c);
+  // A stripe too wide for a 1024-lane workgroup of this kernel: halve the
+  // lanes (and so double the stripe) until the kernel exists and fits.
+  while (L > 1 && (L > max_threads_for(kop, chunks) || !kernel_exists(kop, chunks))) {
+    L /= 2;
+    chunks = round_up_chunks((w + L - 1) / L);
+    if (chunks < 0) break;
+  }
   p->lanes_per_row = (int32_t)L;
-  p->chunks = round_up_chunks((w + L - 1) / L);
+  p->chunks = chunks;
   const int64_t t_min = small ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
-  const bool can_stage = stage_ok && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
+  const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = kPolicyNtLoads;
   if (rows_aligned || can_stage || p->chunks <= 2) policy |= kPolicyNtStores;
   if (can_stage) policy |= kPolicyStageStores;
@@ -179,8 +194,15 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
   a.policy = plan.policy;
   a.r_vec = c.r_vec ? 1 : 0;
   a.y_vec = c.y_vec ? 1 : 0;
-  a.pad_ = 0;
-  const int err = launch_rows(c.op, plan.chunks, plan.grid, plan.threads, a, stream);
+  a.gamma = c.gamma;
+  a.beta = c.beta;
+  // gamma/beta granule k is row granule k when every row starts on a
+  // 16-byte boundary and both vectors are 16-byte aligned.
+  a.affine_vec = (c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0 && ((uintptr_t)c.gamma & 15) == 0 &&
+                  ((uintptr_t)c.beta & 15) == 0)
+                     ? 1
+                     : 0;
+  const int err = launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);
   return err == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
 }
 
@@ -191,12 +213,48 @@ int entry(int op, const float *x, const float *r, float *y, int64_t rows, int64_
   if (st != ROWRED_OK || rows == 0 || width == 0) return st;
   rowred_plan p;
   choose_plan(c, &p);
+  if (p.chunks < 0) return ROWRED_ERR_UNSUPPORTED;
   st = finish_plan(c, &p);
   if (st != ROWRED_OK) return st;
   return run(c, p, eps, stream);
 }
 
 bool op_has_eps(int op) { return op == ROWRED_OP_LAYERNORM_RESIDUAL || op == ROWRED_OP_RMSNORM; }
+
+// LayerNorm with optional residual and affine vectors: check gamma / beta
+// (width floats each, 4-byte aligned, not overlapping y) and attach them.
+int attach_affine(Call *c, const float *gamma, const float *beta) {
+  if (c->rows == 0 || c->width == 0) return ROWRED_OK;
+  for (const float *v : {gamma, beta}) {
+    if (!v) continue;
+    if ((uintptr_t)v & 3) return ROWRED_ERR_INVALID_ARG;
+    const uintptr_t pv = (uintptr_t)v, py = (uintptr_t)c->y;
+    const uintptr_t nv = (uintptr_t)c->width * 4, ny = (uintptr_t)(c->rows * c->width * 4);
+    if (pv < py + ny && py < pv + nv) return ROWRED_ERR_ALIAS;
+  }
+  c->gamma = gamma;
+  c->beta = beta;
+  return ROWRED_OK;
+}
+
+int layernorm_entry(const float *x, const float *r, const float *gamma, const float *beta, float *y, int64_t rows,
+                    int64_t width, float eps, const rowred_plan *plan, hipStream_t stream) {
+  Call c;
+  int st = check_call(ROWRED_OP_LAYERNORM_RESIDUAL, x, r, y, rows, width, false, true, eps, &c);
+  if (st != ROWRED_OK || rows == 0 || width == 0) return st;
+  st = attach_affine(&c, gamma, beta);
+  if (st != ROWRED_OK) return st;
+  rowred_plan p;
+  if (plan) {
+    p = *plan;
+  } else {
+    choose_plan(c, &p);
+    if (p.chunks < 0) return ROWRED_ERR_UNSUPPORTED;  // affine rows wider than 6144 granules
+  }
+  st = finish_plan(c, &p);
+  if (st != ROWRED_OK) return st;
+  return run(c, p, eps, stream);
+}
 
 }  // namespace
 }  // namespace rowred
@@ -206,6 +264,18 @@ using namespace rowred;
 ROWRED_API int rowred_layernorm_residual(const float *x, const float *r, float *y, int64_t rows, int64_t width,
                                          float eps, hipStream_t stream) {
   return entry(ROWRED_OP_LAYERNORM_RESIDUAL, x, r, y, rows, width, eps, true, true, stream);
+}
+
+ROWRED_API int rowred_layernorm(const float *x, const float *r, const float *gamma, const float *beta, float *y,
+                                int64_t rows, int64_t width, float eps, hipStream_t stream) {
+  return layernorm_entry(x, r, gamma, beta, y, rows, width, eps, nullptr, stream);
+}
+
+ROWRED_API int rowred_layernorm_run_plan(const float *x, const float *r, const float *gamma, const float *beta,
+                                         float *y, int64_t rows, int64_t width, float eps, const rowred_plan *plan,
+                                         hipStream_t stream) {
+  if (!plan) return ROWRED_ERR_INVALID_ARG;
+  return layernorm_entry(x, r, gamma, beta, y, rows, width, eps, plan, stream);
 }
 
 ROWRED_API int rowred_rmsnorm(const float *x, float *y, int64_t rows, int64_t width, float eps,
@@ -221,14 +291,15 @@ ROWRED_API int rowred_plan_query(int op, const float *x, const float *r, const f
                                  int64_t width, rowred_plan *out) {
   if (!out) return ROWRED_ERR_INVALID_ARG;
   Call c;
-  const bool need_r = op == ROWRED_OP_LAYERNORM_RESIDUAL;
-  int st = check_call(op, x, need_r ? r : nullptr, y, rows, width, need_r, false, 0.0f, &c);
+  const bool has_r = op == ROWRED_OP_LAYERNORM_RESIDUAL;  // LayerNorm: the residual is optional here
+  int st = check_call(op, x, has_r ? r : nullptr, y, rows, width, false, false, 0.0f, &c);
   if (st != ROWRED_OK) return st;
   if (rows == 0 || width == 0) {
     *out = rowred_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};
     return ROWRED_OK;
   }
   choose_plan(c, out);
+  if (out->chunks < 0) return ROWRED_ERR_UNSUPPORTED;
   return finish_plan(c, out);
 }
 

@@ -12,6 +12,8 @@ namespace rowred {
 struct RowArgs {
   const float *x;      // rows x width input
   const float *r;      // residual (LayerNorm) or nullptr
+  const float *gamma;  // LayerNorm scale per column or nullptr
+  const float *beta;   // LayerNorm shift per column or nullptr
   float *y;            // rows x width output
   int64_t rows;
   int32_t width;
@@ -21,7 +23,7 @@ struct RowArgs {
   int32_t policy;      // ROWRED_POLICY_* bits
   int32_t r_vec;       // 1: r shares x's address modulo 16 (16-byte loads)
   int32_t y_vec;       // 1: y shares x's address modulo 16 (16-byte stores)
-  int32_t pad_;
+  int32_t affine_vec;  // 1: rows start on 16-byte boundaries and gamma/beta are 16-byte aligned
 };
 
 constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;
@@ -35,16 +37,28 @@ constexpr int kMaxStageChunks = 4;     // chunks per lane the staged stores are 
 // of the x window, plus the two partial granules at the run's ends.
 constexpr size_t stage_lds_bytes(int chunks, int threads) { return ((size_t)threads * chunks + 2) * 16; }
 
+// Kernel operator ids: the three public operators plus affine LayerNorm.
+constexpr int kKernelOpLayerNormAffine = 3;
+constexpr int kNumKernelOps = 4;
+
 // Chunk counts for which kernels are instantiated (slots per lane).
 constexpr int kChunkSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
 constexpr int kNumChunkSizes = sizeof(kChunkSet) / sizeof(kChunkSet[0]);
 constexpr int kMaxWindow = 8192;  // 16-byte slots per row: 1024 lanes x 8 or 512 x 16
 
-// Largest workgroup the kernel for `chunks` is compiled for.
-constexpr int max_threads_for_chunks(int chunks) { return chunks <= 8 ? 1024 : 512; }
+// Largest workgroup the kernel for (op, chunks) is compiled for: stripes of
+// up to 8 slots fit the 128 VGPRs of a 1024-thread workgroup, except affine
+// LayerNorm from 7 slots on, whose gamma/beta need the 256 VGPRs of 512.
+constexpr int max_threads_for(int op, int chunks) {
+  return chunks <= 8 && !(op == kKernelOpLayerNormAffine && chunks >= 7) ? 1024 : 512;
+}
+// Whether (op, chunks) is instantiated (affine LayerNorm stops at 12 slots:
+// 16 would not fit its registers).
+constexpr bool kernel_exists(int op, int chunks) { return !(op == kKernelOpLayerNormAffine && chunks > 12); }
 
-// Enqueue one reduction kernel.  Returns the hipError_t of the launch
-// (0 = success).  The caller has validated every argument.
+// Enqueue one reduction kernel (op: a kernel operator id).  Returns the
+// hipError_t of the launch (0 = success).  The caller has validated every
+// argument.
 int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args,
                 hipStream_t stream);
 

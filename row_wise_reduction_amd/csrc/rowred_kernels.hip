@@ -42,6 +42,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kOpLayerNorm = ROWRED_OP_LAYERNORM_RESIDUAL;
 constexpr int kOpRms = ROWRED_OP_RMSNORM;
 constexpr int kOpSoftmax = ROWRED_OP_SOFTMAX;
+constexpr int kOpLayerNormAffine = kKernelOpLayerNormAffine;  // LayerNorm with gamma and/or beta
+constexpr bool is_layernorm(int op) { return op == kOpLayerNorm || op == kOpLayerNormAffine; }
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -184,7 +186,7 @@ __device__ __forceinline__ float identity() {
 // 4 bytes at a time at the same element positions.
 // ---------------------------------------------------------------------------
 template <int OP, int C>
-__global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs a) {
+__global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a) {
   __shared__ float partials[2][16];
   __shared__ double partials_d[16];
 
@@ -221,7 +223,7 @@ __global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs
   // unclamped position.
   const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
   const bool nt_loads = (a.policy & kPolicyNtLoads) != 0;
-  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  const bool has_r = is_layernorm(OP) && a.r != nullptr;
   const float *rrow = has_r ? a.r + base : nullptr;
   f32x4 xv[C], rv[C];
   auto load_rows = [&](auto nt) {
@@ -249,11 +251,7 @@ __global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs
   };
   if (nt_loads) load_rows(std::true_type{});
   else load_rows(std::false_type{});
-  // x + r exactly (in FP64), 0 outside the row.
-  auto combined = [&](int c, int j) -> double {
-    return valid(c, j) ? (double)xv[c][j] + (double)rv[c][j] : 0.0;
-  };
-  if constexpr (OP != kOpLayerNorm) {
+  if constexpr (!is_layernorm(OP)) {
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -288,35 +286,114 @@ __global__ void __launch_bounds__(max_threads_for_chunks(C)) rows_kernel(RowArgs
 #pragma unroll
     for (int i = 0; i < 4 * C; ++i) s[i] *= inv;
   } else {  // LayerNorm
-    // The combined value x + r, the mean and the centring are formed in FP64:
-    // the sum of two floats is exact in double, so each centred value d = c -
-    // mean is correct to FP32 rounding even when the row's spread is far
-    // below its magnitude (a large common offset, or variance << eps, where
-    // FP32 rounding of c and of the mean would be amplified by
-    // 1/sqrt(var + eps)).  Variance and output are FP32: from here on every
-    // error is relative.
+    // The centred values d = (x + r) - mean must be correct to FP32 rounding
+    // even when a row's spread is far below its magnitude (a large common
+    // offset, or variance << eps), where the FP32 rounding of x + r and of
+    // the mean would be amplified by 1/sqrt(var + eps).  So:
+    //  * x + r is kept exactly as an unevaluated sum hi + lo (Knuth's
+    //    TwoSum: hi = fl(x + r), lo = the rounding error, both FP32);
+    //  * the row sum accumulates hi in FP64 and lo in FP32 (lo is below one
+    //    ulp of hi, so its FP32 sum is exact to far below the FP64 sum's
+    //    own error), and the mean is split into m_hi + m_lo;
+    //  * d = (hi - m_hi) + (lo - m_lo) in FP32: the first difference is
+    //    rounded relative to itself, which is d up to terms of ulp size, the
+    //    second is tiny.
+    // From here on every error is relative; variance and output are FP32.
+    float hi[4 * C], lo[4 * C];
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += combined(c, j);
-    double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      for (int j = 0; j < 4; ++j) {
+        const float xv_ = valid(c, j) ? xv[c][j] : 0.0f;
+        const float rv_ = valid(c, j) ? rv[c][j] : 0.0f;
+        const float h = xv_ + rv_;
+        const float bb = h - xv_;
+        const float l = (xv_ - (h - bb)) + (rv_ - bb);  // exact: h + l == xv_ + rv_
+        hi[4 * c + j] = h;
+        lo[4 * c + j] = l;
+        acc[j] += (double)h;
+        acc_lo += l;
+      }
+    double sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo;
     sum = row_allreduce<SumOp>(sum, lanes_log2, partials_d);
     const double mean = sum / (double)width;
+    const float m_hi = (float)mean;
+    const float m_lo = (float)(mean - (double)m_hi);
     float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float d = valid(c, j) ? (float)(combined(c, j) - mean) : 0.0f;  // outside the row: 0
-        s[4 * c + j] = d;
+        const int i = 4 * c + j;
+        const float d = valid(c, j) ? (hi[i] - m_hi) + (lo[i] - m_lo) : 0.0f;  // outside the row: 0
+        s[i] = d;
         sq[j] = fmaf(d, d, sq[j]);
       }
     float var = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    // Affine LayerNorm: gamma and beta hold one value per column.  They are
+    // cached loads (every row reuses them).  With few chunks they go out
+    // before the second collective, which hides their latency; wider
+    // stripes load them just before use to stay within their registers.
+    constexpr bool kAffine = OP == kOpLayerNormAffine;
+    constexpr bool kEarlyAffine = kAffine && C <= 4;
+    f32x4 gv[kEarlyAffine ? C : 1], bv[kEarlyAffine ? C : 1];
+    auto load_affine = [&]() {
+      if constexpr (kEarlyAffine) {
+        if (a.affine_vec) {  // rows start on 16-byte boundaries: row granule k is gamma/beta granule k
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const int k = min(c * L + li, kmax);
+            gv[c] = a.gamma ? load_g<false>(reinterpret_cast<const f32x4 *>(a.gamma) + k) : f32x4(1.0f);
+            bv[c] = a.beta ? load_g<false>(reinterpret_cast<const f32x4 *>(a.beta) + k) : f32x4(0.0f);
+          }
+        } else {
+          const int emax = width - 1;
+#pragma unroll
+          for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int e = max(0, min(elem(c, j), emax));
+              gv[c][j] = a.gamma ? load_g<false>(a.gamma + e) : 1.0f;
+              bv[c][j] = a.beta ? load_g<false>(a.beta + e) : 0.0f;
+            }
+        }
+      }
+    };
+    if constexpr (kEarlyAffine) load_affine();
     var = row_allreduce<SumOp>(var, lanes_log2, partials[1]);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(var, a.inv_width, a.eps));
+    if constexpr (kEarlyAffine) {
 #pragma unroll
-    for (int i = 0; i < 4 * C; ++i) s[i] *= rstd;
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[4 * c + j] = fmaf(s[4 * c + j] * rstd, gv[c][j], bv[c][j]);
+    } else if constexpr (kAffine) {
+      // one chunk at a time: two 16-byte (or four 4-byte) loads per vector
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        f32x4 g, b;
+        if (a.affine_vec) {
+          const int k = min(c * L + li, kmax);
+          g = a.gamma ? load_g<false>(reinterpret_cast<const f32x4 *>(a.gamma) + k) : f32x4(1.0f);
+          b = a.beta ? load_g<false>(reinterpret_cast<const f32x4 *>(a.beta) + k) : f32x4(0.0f);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = max(0, min(elem(c, j), width - 1));
+            g[j] = a.gamma ? load_g<false>(a.gamma + e) : 1.0f;
+            b[j] = a.beta ? load_g<false>(a.beta + e) : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[4 * c + j] = fmaf(s[4 * c + j] * rstd, g[j], b[j]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next chunk's loads after this chunk's use
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * C; ++i) s[i] *= rstd;
+    }
   }
 
   // ---- predicated store: replayed row slots write nothing.
@@ -429,16 +506,23 @@ __global__ void __launch_bounds__(256) copy_kernel(const f32x4 *x, f32x4 *y, int
 
 using KernelFn = void (*)(RowArgs);
 
-#define ROWRED_CHUNK_ROW(OP)                                                                     \
-  {rows_kernel<OP, 1>, rows_kernel<OP, 2>, rows_kernel<OP, 3>,  rows_kernel<OP, 4>,                \
-   rows_kernel<OP, 5>, rows_kernel<OP, 6>, rows_kernel<OP, 7>,  rows_kernel<OP, 8>,                \
-   rows_kernel<OP, 10>, rows_kernel<OP, 12>, rows_kernel<OP, 16>}
+template <int OP, int C>
+constexpr KernelFn kernel_or_null() {
+  if constexpr (kernel_exists(OP, C)) return rows_kernel<OP, C>;
+  else return nullptr;
+}
 
-// [op][chunk index in kChunkSet]
-const KernelFn kKernels[3][kNumChunkSizes] = {
+#define ROWRED_CHUNK_ROW(OP)                                                                          \
+  {kernel_or_null<OP, 1>(), kernel_or_null<OP, 2>(),  kernel_or_null<OP, 3>(),  kernel_or_null<OP, 4>(), \
+   kernel_or_null<OP, 5>(), kernel_or_null<OP, 6>(),  kernel_or_null<OP, 7>(),  kernel_or_null<OP, 8>(), \
+   kernel_or_null<OP, 10>(), kernel_or_null<OP, 12>(), kernel_or_null<OP, 16>()}
+
+// [kernel op][chunk index in kChunkSet]
+const KernelFn kKernels[kNumKernelOps][kNumChunkSizes] = {
     ROWRED_CHUNK_ROW(kOpLayerNorm),
     ROWRED_CHUNK_ROW(kOpRms),
     ROWRED_CHUNK_ROW(kOpSoftmax),
+    ROWRED_CHUNK_ROW(kOpLayerNormAffine),
 };
 #undef ROWRED_CHUNK_ROW
 
@@ -454,7 +538,7 @@ int chunk_index(int chunks) {
 
 int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args, hipStream_t stream) {
   const int ci = chunk_index(chunks);
-  if (op < 0 || op > 2 || ci < 0) return (int)hipErrorInvalidValue;
+  if (op < 0 || op >= kNumKernelOps || ci < 0 || !kKernels[op][ci]) return (int)hipErrorInvalidValue;
   KernelFn fn = kKernels[op][ci];
   RowArgs a = args;
   void *params[] = {&a};

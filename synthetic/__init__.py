@@ -35,9 +35,9 @@ import numpy as np
 
 SEED_ROOT = 20260905
 OP_IDS = {"layernorm_residual": 0, "rmsnorm": 1, "softmax": 2, "layernorm": 3,
-          "row_sum": 4, "row_minmax": 5}
+          "row_sum": 4, "row_minmax": 5, "layernorm_affine": 6}
 TENSOR_IDS = {"x": 0, "r": 1, "gamma": 2, "beta": 3}
-EPS = {"layernorm_residual": 1e-5, "layernorm": 1e-5, "rmsnorm": 1e-6}
+EPS = {"layernorm_residual": 1e-5, "layernorm": 1e-5, "layernorm_affine": 1e-5, "rmsnorm": 1e-6}
 
 _BLOCK_ELEMS = 1 << 24  # float64 elements drawn per block (128 MiB)
 
@@ -73,9 +73,25 @@ CONFIGS = {
 }
 
 
+# Workloads of the next steps beyond the three core operators: plain
+# LayerNorm at the shape the pages time it (1024x4096) and at the wide-row
+# shape, and affine LayerNorm (gamma ~ 1 + 0.1 N(0,1), beta ~ 0.1 N(0,1)).
+NEXT_CONFIGS = {
+    6: [Case(6, "layernorm", 1024, 4096, "uniform"), Case(6, "layernorm", 16384, 8192, "uniform")],
+    7: [Case(7, "layernorm_affine", 1024, 4096, "uniform"), Case(7, "layernorm_affine", 16384, 8192, "uniform")],
+}
+
+
 def all_cases() -> Iterator[Case]:
     for cfg in sorted(CONFIGS):
         yield from CONFIGS[cfg]
+
+
+def affine_vectors(case: Case):
+    """(gamma, beta) for an affine LayerNorm case, float32 vectors of length width."""
+    g = draw("normal", 1, case.width, seed_sequence(case.cfg, "layernorm", "gamma", 1, case.width))[0]
+    b = draw("normal", 1, case.width, seed_sequence(case.cfg, "layernorm", "beta", 1, case.width))[0]
+    return (np.float32(1.0) + np.float32(0.1) * g).astype(np.float32), (np.float32(0.1) * b).astype(np.float32)
 
 
 def seed_sequence(cfg: int, op: str, tensor: str, rows: int, width: int) -> np.random.SeedSequence:

@@ -260,3 +260,33 @@ def test_xcd_block_remap_is_a_bijection():
         assert sorted(seen) == list(range(G)), G
         for blks in per_xcd.values():
             assert blks == list(range(blks[0], blks[0] + len(blks)))
+
+
+def test_layernorm_entry_argument_checks():
+    lib = R.lib()
+    G = 0x7F3000000000
+    # plain LayerNorm: r may be NULL (rows = 0 stops after the checks)
+    assert lib.rowred_layernorm(X, None, None, None, Y, 0, 64, f(1e-5), None) == R.ROWRED_OK
+    assert lib.rowred_layernorm(X, None, G + 2, None, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_layernorm(X, None, None, G + 1, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_INVALID_ARG
+    # gamma overlapping y
+    assert lib.rowred_layernorm(X, None, Y + 64, None, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_layernorm(X, None, None, Y + 4 * 255, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_layernorm(X, None, None, None, Y, 4, 64, f(-1.0), None) == R.ROWRED_ERR_INVALID_ARG
+    # affine rows are capped at 6144 granules
+    assert lib.rowred_layernorm(X, None, G, None, Y, 2, 32768, f(1e-5), None) == R.ROWRED_ERR_UNSUPPORTED
+    assert lib.rowred_layernorm(X, None, None, None, Y, 0, 32768, f(1e-5), None) == R.ROWRED_OK
+    # explicit plans: affine kernels of >= 7 chunks need <= 512 threads, 16 chunks do not exist
+    c = bad_plan(lanes_per_row=1024, chunks=8, threads=1024)._c()
+    assert lib.rowred_layernorm_run_plan(X, None, G, None, Y, 2, 24576, f(1e-5), ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    c = bad_plan(lanes_per_row=512, chunks=16, threads=512)._c()
+    assert lib.rowred_layernorm_run_plan(X, None, G, None, Y, 2, 24576, f(1e-5), ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    c = bad_plan(lanes_per_row=512, chunks=12, threads=512)._c()
+    assert lib.rowred_layernorm_run_plan(X, None, G, None, Y, 0, 24576, f(1e-5), ctypes.byref(c), None) == R.ROWRED_OK
+
+
+def test_plan_query_layernorm_without_residual():
+    p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=1024, width=4096)
+    assert (p.lanes_per_row, p.chunks) == (256, 4)

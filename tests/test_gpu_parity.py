@@ -271,6 +271,35 @@ def test_layernorm_special_rows():
     assert np.isnan(y[3]).all()
 
 
+@pytest.mark.parametrize("width", [2, 3, 16, 257, 4096])
+def test_layernorm_ill_conditioned_rows(width):
+    """Rows whose spread is far below their magnitude: the centring must stay
+    accurate to FP32 rounding of the centred value itself."""
+    rng = np.random.default_rng(width)
+    rows = 12
+    x = np.empty((rows, width), np.float32)
+    r = np.empty((rows, width), np.float32)
+    n = lambda: rng.standard_normal(width)
+    x[0], r[0] = 1e4 + n(), -1e4 + n()                    # large x and r that cancel
+    x[1], r[1] = 1000 + 1e-3 * n(), 0.0                   # tiny spread on a large mean
+    x[2], r[2] = 1 + 1e-4 * n(), 1e-4 * n()               # variance ~1e-8 << eps
+    x[3], r[3] = 1 + 3e-3 * n(), 0.0                      # variance ~ eps
+    x[4], r[4] = -5e3 + 10 * n(), 5e3 + 10 * n()
+    x[5], r[5] = 1 + 2.0 ** -20 * n(), 2.0 ** -22 * n()
+    x[6], r[6] = 3e7 + n(), -3e7 + n()                    # inputs beyond 2^24: x + r not exact in FP32
+    x[7], r[7] = n() * 1e-15, n() * 1e-15                 # tiny values (squares stay above FLT_MIN)
+    x[8:], r[8:] = rng.uniform(-1, 1, (rows - 8, width)), rng.uniform(-1, 1, (rows - 8, width))
+    for eps in (1e-5, 0.0):
+        y = run_case("layernorm_residual", x, r, eps=eps)
+        ref = oracle.layernorm_residual(x, r, eps)
+        assert_close(y, ref, f"ill-conditioned LN width {width} eps {eps}")
+    xp = (x.astype(np.float64) + r).astype(np.float32)
+    out = Guarded(rows, width)
+    R.rowred_layernorm(dev(xp), None, None, None, out.y, eps=1e-5)
+    torch().cuda.synchronize()
+    assert_close(out.host(), oracle.layernorm(xp, None, eps=1e-5), f"ill-conditioned plain LN width {width}")
+
+
 def test_layernorm_eps_zero_constant_row_is_nan():
     x = np.full((2, 64), 2.0, np.float32)
     x[1] = np.arange(64, dtype=np.float32)
