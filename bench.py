@@ -22,11 +22,12 @@ oracle's throughput on host cores, and per-operator figures.
                                 # workloads 1..7 on cold buffers, + a 256 MiB
                                 # copy per workload for calibration
     python bench.py --all       # one JSON line per core workload (1..5)
-    python bench.py --next      # plain and affine LayerNorm (6, 7)
+    python bench.py --next      # plain and affine LayerNorm, row sum / min-max (6-8)
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -57,9 +58,10 @@ WORKLOAD_NAMES = {
     5: "softmax stress, 8192x32768, 8*N(0,1) + U[-80,80] row offsets, 1% -inf",
     6: "plain LayerNorm (no residual), 1024x4096 and 16384x8192, U[-1,1]",
     7: "affine LayerNorm (gamma, beta), 1024x4096 and 16384x8192, U[-1,1]",
+    8: "row sum and row min/max, 16384x8192 U[-1,1] and 131072x257 N(0,1)",
 }
 CORE = (1, 2, 3, 4, 5)
-NEXT = (6, 7)
+NEXT = (6, 7, 8)
 WORKLOADS = {**synthetic.CONFIGS, **synthetic.NEXT_CONFIGS}
 
 
@@ -67,11 +69,20 @@ def n_inputs(op):
     return 2 if op == "layernorm_residual" else 1
 
 
+def algo_split(case):
+    """(read, write) algorithmic bytes: one read of every input element, one
+    write of every output element; affine LayerNorm also reads gamma and beta
+    once; row sum writes one float per row, row min/max two."""
+    rd = 4 * case.rows * case.width * n_inputs(case.op)
+    if case.op == "layernorm_affine":
+        rd += 8 * case.width
+    if case.op in ("row_sum", "row_minmax"):
+        return rd, 4 * case.rows * (1 if case.op == "row_sum" else 2)
+    return rd, 4 * case.rows * case.width
+
+
 def algo_bytes(case):
-    """One read of every input element, one write of every output element;
-    affine LayerNorm also reads gamma and beta once."""
-    extra = 8 * case.width if case.op == "layernorm_affine" else 0
-    return 4 * case.rows * case.width * (n_inputs(case.op) + 1) + extra
+    return sum(algo_split(case))
 
 
 def kernel_source_hash():
@@ -105,7 +116,11 @@ class CaseBuffers:
         rd = torch.from_numpy(r).cuda() if r is not None else None
         self.x = [xd] + [xd.clone() for _ in range(sets - 1)]
         self.r = ([rd] + [rd.clone() for _ in range(sets - 1)]) if rd is not None else [None] * sets
-        self.y = [torch.empty_like(xd) for _ in range(sets)]
+        if case.op in ("row_sum", "row_minmax"):
+            self.y = [torch.empty(case.rows, device="cuda") for _ in range(sets)]
+            self.y2 = [torch.empty(case.rows, device="cuda") for _ in range(sets)]
+        else:
+            self.y = [torch.empty_like(xd) for _ in range(sets)]
         self.sets = sets
 
     def call(self, i):
@@ -114,13 +129,12 @@ class CaseBuffers:
         op = self.case.op
         if op in ("layernorm", "layernorm_affine"):
             R.rowred_layernorm(self.x[k], None, self.g, self.b, self.y[k], eps=self.case.eps)
+        elif op == "row_sum":
+            R.rowred_row_sum(self.x[k], self.y[k])
+        elif op == "row_minmax":
+            R.rowred_row_minmax(self.x[k], self.y[k], self.y2[k])
         else:
             R.run_op(op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
-
-    def oracle(self, rows):
-        import oracle
-        return oracle.run_op(self.case.op, self.host_x[:rows], self.host_r[:rows] if self.host_r is not None else None,
-                             eps=self.case.eps, gamma=self.host_g, beta=self.host_b)
 
 
 def rotation_sets(case):
@@ -201,7 +215,7 @@ def cpu_baseline(cases, bufs, seconds):
             if time.perf_counter() - t >= budget or reps >= 1000:
                 break
         elapsed += time.perf_counter() - t
-        done_bytes += reps * 4 * rows * c.width * (n_inputs(c.op) + 1)
+        done_bytes += reps * algo_bytes(dataclasses.replace(c, rows=rows))
         sample_desc.append(f"{c.op} {rows}x{c.width} x{reps}")
     return {"value": round(done_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "; ".join(sample_desc) + f" ({elapsed:.1f} s, FP64, row blocks over {threads} threads)"}
@@ -255,6 +269,7 @@ def bench(cfg, steps, warmup, cpu_seconds):
         "ops": ops,
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "wall_s": round(wall, 4),
+        "kernel_source_hash": kernel_source_hash(),
     }
     out["copy_ceiling"] = {"same_bytes_as_dominant": copy_ceiling(algo_bytes(dc)),
                            "1GiB": copy_ceiling(2 ** 30, reps=10)}
@@ -307,6 +322,7 @@ def pmc_pass(cfg):
     cases = WORKLOADS[cfg]
     bufs = [CaseBuffers(c, 1) for c in cases]
     flush = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    print(f"pmc kernel_source_hash {kernel_source_hash()}", flush=True)
     torch.cuda.synchronize()
     for b in bufs:
         flush.fill_(1.0)
@@ -327,7 +343,7 @@ def pmc_pass(cfg):
 # ---------------------------------------------------------------------------
 
 PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {ctr} --output-format csv -d <out_{ctr}> -o run -- "
-           "python3 <repo>/bench.py --pmc --all")
+           "python3 <repo>/bench.py --pmc --all > <log_{ctr}>")
 TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
              "python3 <repo>/bench.py --cpu-seconds 0")
 
@@ -339,7 +355,16 @@ def _csv_rows(path):
     return rows
 
 
-def traffic_summary(fetch_csv, write_csv, out_dir):
+def _logged_hash(log_path):
+    """The kernel source hash a counter pass printed (see pmc_pass)."""
+    if log_path and os.path.exists(log_path):
+        for line in open(log_path, errors="replace"):
+            if line.startswith("pmc kernel_source_hash "):
+                return line.split()[-1]
+    return "unknown"
+
+
+def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=None):
     """Write profiles/pmc_traffic_cfg<N>.txt from the two counter passes of
     `bench.py --pmc --all`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     scaled by what each counter reads for the 256 MiB copy that ends each
@@ -368,7 +393,10 @@ def traffic_summary(fetch_csv, write_csv, out_dir):
         if i != len(expected):
             raise SystemExit(f"{path}: found {i} reduction dispatches, expected {len(expected)}")
     copy_bytes = 2 ** 28  # each side of the calibration copy
-    h = kernel_source_hash()
+    # the sources the counters were taken on (both passes must agree)
+    h = _logged_hash(fetch_log)
+    if _logged_hash(write_log) != h:
+        h = "unknown"
     written = []
     for cfg, cases in per_cfg.items():
         lines = [f"# HBM traffic per dispatch, workload {cfg}: {WORKLOAD_NAMES[cfg]}",
@@ -385,8 +413,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir):
             ws = copy_bytes / (d["WRITE_SIZE_copy"] * 1024)
             rd = d["FETCH_SIZE"] * 1024 * rs
             wr = d["WRITE_SIZE"] * 1024 * ws
-            alg_r = algo_bytes(case) - 4 * case.rows * case.width
-            alg_w = 4 * case.rows * case.width
+            alg_r, alg_w = algo_split(case)
             lines += [f"kernel[{key}]: {d['kernel']}",
                       f"fetch_kib[{key}]: {d['FETCH_SIZE']:.2f} (copy {d['FETCH_SIZE_copy']:.2f}, "
                       f"read_scale {rs:.4f})",
@@ -409,7 +436,7 @@ def trace_summary(stats_csv, bench_json, out_path):
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     lines = [f"# rocprofv3 kernel statistics, workload {b['config']['config_id']}: {b['config']['workload']}",
              "#   " + TRACE_CMD,
-             f"# kernel_source_hash: {kernel_source_hash()}",
+             f"# kernel_source_hash: {b.get('kernel_source_hash', 'unknown')}",
              "# name | calls | total_ns | average_ns | min_ns | max_ns | percentage"]
     for r in rows:
         nm = r["Name"].replace("void rowred::(anonymous namespace)::", "")
@@ -430,16 +457,18 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
-    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6, 7)")
+    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6, 7, 8)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/pmc_traffic_cfg*.txt from two counter passes (no GPU)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_LOG", "WRITE_LOG"),
+                    help="write profiles/pmc_traffic_cfg*.txt from two counter passes and their stdout logs "
+                         "(no GPU)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "BENCH_JSON", "OUT"),
                     help="write a kernel-trace summary (no GPU)")
     args = ap.parse_args(argv)
     if args.traffic_summary:
-        for p in traffic_summary(*args.traffic_summary, os.path.join(ROOT, "profiles")):
+        fc, wc, fl, wl = args.traffic_summary
+        for p in traffic_summary(fc, wc, os.path.join(ROOT, "profiles"), fl, wl):
             print(p)
         return 0
     if args.trace_summary:

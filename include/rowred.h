@@ -77,7 +77,9 @@ enum rowred_status {
 enum rowred_op {
   ROWRED_OP_LAYERNORM_RESIDUAL = 0,
   ROWRED_OP_RMSNORM = 1,
-  ROWRED_OP_SOFTMAX = 2
+  ROWRED_OP_SOFTMAX = 2,
+  ROWRED_OP_ROW_SUM = 3,
+  ROWRED_OP_ROW_MINMAX = 4
 };
 
 /*
@@ -134,6 +136,24 @@ int rowred_rmsnorm(const float *x, float *y, int64_t rows, int64_t width,
  */
 int rowred_softmax(const float *x, float *y, int64_t rows, int64_t width,
                    hipStream_t stream);
+
+/*
+ * Row sum: out[i] = sum_j x_ij, accumulated in FP64 and rounded once to FP32.
+ * Paired row min/max: out_min[i] = min_j x_ij, out_max[i] = max_j x_ij,
+ * exact; NaN entries are skipped (IEEE minNum/maxNum), so an all-NaN row
+ * gives (+inf, -inf).  Sum is the identical-source control and min/max one of
+ * the four operators of "Cooperating-program packing: implementation and
+ * fixed-plan evidence", section "Validation"; "Immutable input reuse in Metal
+ * reductions", section "Fixed-width GPU and dispatch results", times sum.
+ * out, out_min, out_max hold `rows` floats (4-byte aligned) and must not
+ * overlap x or each other.  A row needs at least one element: width == 0 with
+ * rows > 0 -> ROWRED_ERR_INVALID_ARG.  Same loads, geometry and width cap as
+ * the entry points above; the outputs are written by one lane per row.
+ */
+int rowred_row_sum(const float *x, float *out, int64_t rows, int64_t width,
+                   hipStream_t stream);
+int rowred_row_minmax(const float *x, float *out_min, float *out_max,
+                      int64_t rows, int64_t width, hipStream_t stream);
 
 /*
  * Launch geometry.  A row is owned by `lanes_per_row` (L) consecutive lanes
@@ -195,6 +215,13 @@ int rowred_plan_query(int op, const float *x, const float *r, const float *y,
 int rowred_run_plan(int op, const float *x, const float *r, float *y,
                     int64_t rows, int64_t width, float eps,
                     const rowred_plan *plan, hipStream_t stream);
+
+/* Row sum (op ROWRED_OP_ROW_SUM, out1 unused) or row min/max (op
+ * ROWRED_OP_ROW_MINMAX, out0 = min, out1 = max) with an explicit plan (as
+ * rowred_run_plan; ROWRED_POLICY_STAGE_STORES does not apply). */
+int rowred_row_reduce_run_plan(int op, const float *x, float *out0, float *out1,
+                               int64_t rows, int64_t width,
+                               const rowred_plan *plan, hipStream_t stream);
 
 /* rowred_layernorm with an explicit plan (as rowred_run_plan). */
 int rowred_layernorm_run_plan(const float *x, const float *r, const float *gamma,

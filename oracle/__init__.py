@@ -219,6 +219,10 @@ def run_op(op: str, x, r=None, eps=None, threads=None, gamma=None, beta=None):
         return layernorm(x, r, eps=1e-5 if eps is None else eps, gamma=gamma, beta=beta, threads=threads)
     if op == "rmsnorm":
         return rmsnorm(x, eps=1e-6 if eps is None else eps, threads=threads)
+    if op == "row_sum":
+        return row_sum(x, threads=threads)
+    if op == "row_minmax":
+        return row_minmax(x, threads=threads)
     if op == "softmax":
         return softmax(x, threads=threads)
     raise ValueError(f"unknown op {op!r}")

@@ -36,8 +36,10 @@ ROWRED_POLICY_STAGE_STORES = 8
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1
 ROWRED_OP_SOFTMAX = 2
+ROWRED_OP_ROW_SUM = 3
+ROWRED_OP_ROW_MINMAX = 4
 OPS = {"layernorm_residual": ROWRED_OP_LAYERNORM_RESIDUAL, "rmsnorm": ROWRED_OP_RMSNORM,
-       "softmax": ROWRED_OP_SOFTMAX}
+       "softmax": ROWRED_OP_SOFTMAX, "row_sum": ROWRED_OP_ROW_SUM, "row_minmax": ROWRED_OP_ROW_MINMAX}
 
 
 class RowRedError(RuntimeError):
@@ -92,6 +94,9 @@ def lib():
             "rowred_plan_query": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan)],
             "rowred_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
             "rowred_copy": [_P, _P, _I64, _P],
+            "rowred_row_sum": [_P, _P, _I64, _I64, _P],
+            "rowred_row_minmax": [_P, _P, _P, _I64, _I64, _P],
+            "rowred_row_reduce_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan), _P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(L, name)
@@ -206,6 +211,44 @@ def rowred_layernorm_run_plan(x, r, gamma, beta, y, plan: "Plan", rows=None, wid
                                          my[0], rows, width, float(eps), ctypes.byref(c),
                                          _stream(stream, x, r, gamma, beta, y))
     _check(st, "rowred_layernorm_run_plan")
+
+
+def _row_vector(v, name, rows):
+    if v is None:
+        return None
+    if _is_tensor(v):
+        addr, r, w = _matrix(v, name)
+        if r * w != rows:
+            raise ValueError(f"{name} must hold rows={rows} floats")
+        return addr
+    return int(v)
+
+
+def rowred_row_sum(x, out, rows=None, width=None, stream=None):
+    """out[i] = sum_j x[i, j] (FP64 accumulation, FP32 result)."""
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    st = lib().rowred_row_sum(mx[0], _row_vector(out, "out", rows), rows, width, _stream(stream, x, out))
+    _check(st, "rowred_row_sum")
+
+
+def rowred_row_minmax(x, out_min, out_max, rows=None, width=None, stream=None):
+    """out_min[i] = min_j x[i, j], out_max[i] = max_j x[i, j] (NaN skipped)."""
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    st = lib().rowred_row_minmax(mx[0], _row_vector(out_min, "out_min", rows), _row_vector(out_max, "out_max", rows),
+                                 rows, width, _stream(stream, x, out_min, out_max))
+    _check(st, "rowred_row_minmax")
+
+
+def rowred_row_reduce_run_plan(op, x, out0, out1, plan: "Plan", rows=None, width=None, stream=None):
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    c = plan._c()
+    st = lib().rowred_row_reduce_run_plan(_op_id(op), mx[0], _row_vector(out0, "out0", rows),
+                                          _row_vector(out1, "out1", rows), rows, width, ctypes.byref(c),
+                                          _stream(stream, x, out0, out1))
+    _check(st, "rowred_row_reduce_run_plan")
 
 
 def rowred_rmsnorm(x, y, rows=None, width=None, eps=1e-6, stream=None):

@@ -13,7 +13,7 @@
 namespace rowred {
 namespace {
 
-constexpr int kNumOps = 3;
+constexpr int kNumMatrixOps = 3;  // LayerNorm, RMSNorm, softmax: rows x width outputs
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -42,6 +42,7 @@ struct Call {
   const float *x, *r;
   const float *gamma = nullptr, *beta = nullptr;  // LayerNorm only
   float *y;
+  float *y2 = nullptr;  // row max (min/max reduction)
   int64_t rows, width;
   bool r_vec, y_vec;  // r / y share x's address modulo 16
   int window;         // largest number of 16-byte granules a row of x spans
@@ -70,7 +71,7 @@ int max_window(const float *x, int64_t rows, int64_t width) {
 // Checks shared by every entry point.  `need_eps` marks ops with an eps.
 int check_call(int op, const float *x, const float *r, const float *y, int64_t rows, int64_t width, bool need_r,
                bool need_eps, float eps, Call *out) {
-  if (op < 0 || op >= kNumOps) return ROWRED_ERR_INVALID_ARG;
+  if (op < 0 || op >= kNumMatrixOps) return ROWRED_ERR_INVALID_ARG;
   if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   if (need_eps && (!isfinite(eps) || eps < 0.0f)) return ROWRED_ERR_INVALID_ARG;
   out->op = op;
@@ -196,6 +197,7 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
   a.y_vec = c.y_vec ? 1 : 0;
   a.gamma = c.gamma;
   a.beta = c.beta;
+  a.y2 = c.y2;
   // gamma/beta granule k is row granule k when every row starts on a
   // 16-byte boundary and both vectors are 16-byte aligned.
   a.affine_vec = (c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0 && ((uintptr_t)c.gamma & 15) == 0 &&
@@ -217,6 +219,52 @@ int entry(int op, const float *x, const float *r, float *y, int64_t rows, int64_
   st = finish_plan(c, &p);
   if (st != ROWRED_OK) return st;
   return run(c, p, eps, stream);
+}
+
+// Row sum / row min-max: outputs are `rows` floats each.
+int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t rows, int64_t width, Call *out) {
+  if (op != ROWRED_OP_ROW_SUM && op != ROWRED_OP_ROW_MINMAX) return ROWRED_ERR_INVALID_ARG;
+  if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
+  out->op = op;
+  out->x = x;
+  out->r = nullptr;
+  out->y = out0;
+  out->y2 = op == ROWRED_OP_ROW_MINMAX ? out1 : nullptr;
+  out->rows = rows;
+  out->width = width;
+  out->r_vec = out->y_vec = false;
+  out->window = 0;
+  if (rows == 0) return ROWRED_OK;
+  if (width == 0) return ROWRED_ERR_INVALID_ARG;  // a row needs at least one element
+  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (!x || !out0 || (op == ROWRED_OP_ROW_MINMAX && !out1)) return ROWRED_ERR_INVALID_ARG;
+  if (((uintptr_t)x & 3) || ((uintptr_t)out0 & 3) || (out->y2 && ((uintptr_t)out1 & 3))) return ROWRED_ERR_INVALID_ARG;
+  const uintptr_t px = (uintptr_t)x, nx = (uintptr_t)(rows * width * 4), no = (uintptr_t)rows * 4;
+  auto hits = [&](const void *o, const void *b, uintptr_t nb) {
+    return (uintptr_t)o < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)o + no;
+  };
+  if (hits(out0, (const void *)px, nx) || (out->y2 && (hits(out1, (const void *)px, nx) || hits(out1, out0, no))))
+    return ROWRED_ERR_ALIAS;
+  out->window = max_window(x, rows, width);
+  if (out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
+int row_reduce_entry(int op, const float *x, float *out0, float *out1, int64_t rows, int64_t width,
+                     const rowred_plan *plan, hipStream_t stream) {
+  Call c;
+  int st = check_reduce_call(op, x, out0, out1, rows, width, &c);
+  if (st != ROWRED_OK || rows == 0) return st;
+  rowred_plan p;
+  if (plan) {
+    p = *plan;
+  } else {
+    choose_plan(c, &p);
+    if (p.chunks < 0) return ROWRED_ERR_UNSUPPORTED;
+  }
+  st = finish_plan(c, &p);
+  if (st != ROWRED_OK) return st;
+  return run(c, p, 0.0f, stream);
 }
 
 bool op_has_eps(int op) { return op == ROWRED_OP_LAYERNORM_RESIDUAL || op == ROWRED_OP_RMSNORM; }
@@ -278,6 +326,21 @@ ROWRED_API int rowred_layernorm_run_plan(const float *x, const float *r, const f
   return layernorm_entry(x, r, gamma, beta, y, rows, width, eps, plan, stream);
 }
 
+ROWRED_API int rowred_row_sum(const float *x, float *out, int64_t rows, int64_t width, hipStream_t stream) {
+  return row_reduce_entry(ROWRED_OP_ROW_SUM, x, out, nullptr, rows, width, nullptr, stream);
+}
+
+ROWRED_API int rowred_row_minmax(const float *x, float *out_min, float *out_max, int64_t rows, int64_t width,
+                                 hipStream_t stream) {
+  return row_reduce_entry(ROWRED_OP_ROW_MINMAX, x, out_min, out_max, rows, width, nullptr, stream);
+}
+
+ROWRED_API int rowred_row_reduce_run_plan(int op, const float *x, float *out0, float *out1, int64_t rows,
+                                          int64_t width, const rowred_plan *plan, hipStream_t stream) {
+  if (!plan) return ROWRED_ERR_INVALID_ARG;
+  return row_reduce_entry(op, x, out0, out1, rows, width, plan, stream);
+}
+
 ROWRED_API int rowred_rmsnorm(const float *x, float *y, int64_t rows, int64_t width, float eps,
                               hipStream_t stream) {
   return entry(ROWRED_OP_RMSNORM, x, nullptr, y, rows, width, eps, false, true, stream);
@@ -292,7 +355,9 @@ ROWRED_API int rowred_plan_query(int op, const float *x, const float *r, const f
   if (!out) return ROWRED_ERR_INVALID_ARG;
   Call c;
   const bool has_r = op == ROWRED_OP_LAYERNORM_RESIDUAL;  // LayerNorm: the residual is optional here
-  int st = check_call(op, x, has_r ? r : nullptr, y, rows, width, false, false, 0.0f, &c);
+  int st = op == ROWRED_OP_ROW_SUM || op == ROWRED_OP_ROW_MINMAX
+               ? check_reduce_call(op, x, const_cast<float *>(y), const_cast<float *>(r), rows, width, &c)
+               : check_call(op, x, has_r ? r : nullptr, y, rows, width, false, false, 0.0f, &c);
   if (st != ROWRED_OK) return st;
   if (rows == 0 || width == 0) {
     *out = rowred_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};

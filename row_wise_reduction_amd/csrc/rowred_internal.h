@@ -14,7 +14,8 @@ struct RowArgs {
   const float *r;      // residual (LayerNorm) or nullptr
   const float *gamma;  // LayerNorm scale per column or nullptr
   const float *beta;   // LayerNorm shift per column or nullptr
-  float *y;            // rows x width output
+  float *y;            // rows x width output (row sum / row min: rows floats)
+  float *y2;           // row max: rows floats
   int64_t rows;
   int32_t width;
   int32_t lanes_log2;  // log2(L)
@@ -37,9 +38,10 @@ constexpr int kMaxStageChunks = 4;     // chunks per lane the staged stores are 
 // of the x window, plus the two partial granules at the run's ends.
 constexpr size_t stage_lds_bytes(int chunks, int threads) { return ((size_t)threads * chunks + 2) * 16; }
 
-// Kernel operator ids: the three public operators plus affine LayerNorm.
-constexpr int kKernelOpLayerNormAffine = 3;
-constexpr int kNumKernelOps = 4;
+// Kernel operator ids: the public operators (enum rowred_op) plus affine
+// LayerNorm.
+constexpr int kKernelOpLayerNormAffine = 5;
+constexpr int kNumKernelOps = 6;
 
 // Chunk counts for which kernels are instantiated (slots per lane).
 constexpr int kChunkSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16};

@@ -42,7 +42,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kOpLayerNorm = ROWRED_OP_LAYERNORM_RESIDUAL;
 constexpr int kOpRms = ROWRED_OP_RMSNORM;
 constexpr int kOpSoftmax = ROWRED_OP_SOFTMAX;
+constexpr int kOpRowSum = ROWRED_OP_ROW_SUM;
+constexpr int kOpRowMinMax = ROWRED_OP_ROW_MINMAX;
 constexpr int kOpLayerNormAffine = kKernelOpLayerNormAffine;  // LayerNorm with gamma and/or beta
+constexpr bool is_row_scalar(int op) { return op == kOpRowSum || op == kOpRowMinMax; }
 constexpr bool is_layernorm(int op) { return op == kOpLayerNorm || op == kOpLayerNormAffine; }
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -127,6 +130,9 @@ struct SumOp {
 };
 struct MaxOp {
   static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+};
+struct MinOp {
+  static __device__ __forceinline__ float apply(float a, float b) { return fminf(a, b); }
 };
 
 // All-reduce over aligned groups of 2^min(lanes_log2, 6) lanes.  Each step
@@ -251,6 +257,42 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   };
   if (nt_loads) load_rows(std::true_type{});
   else load_rows(std::false_type{});
+  // ---- scalar-per-row reductions: no output map, one lane writes the row.
+  if constexpr (OP == kOpRowSum) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += valid(c, j) ? (double)xv[c][j] : 0.0;
+    double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    sum = row_allreduce<SumOp>(sum, lanes_log2, partials_d);
+    if (live && li == 0) a.y[row] = (float)sum;
+    return;
+  } else if constexpr (OP == kOpRowMinMax) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = __builtin_inff();
+      hi[j] = -__builtin_inff();
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = fminf(lo[j], valid(c, j) ? xv[c][j] : __builtin_inff());
+        hi[j] = fmaxf(hi[j], valid(c, j) ? xv[c][j] : -__builtin_inff());
+      }
+    float mn = fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3]));
+    float mx = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
+    mn = row_allreduce<MinOp>(mn, lanes_log2, partials[0]);
+    mx = row_allreduce<MaxOp>(mx, lanes_log2, partials[1]);
+    if (live && li == 0) {
+      a.y[row] = mn;
+      a.y2[row] = mx;
+    }
+    return;
+  }
+
   if constexpr (!is_layernorm(OP)) {
 #pragma unroll
     for (int c = 0; c < C; ++c)
@@ -522,8 +564,11 @@ const KernelFn kKernels[kNumKernelOps][kNumChunkSizes] = {
     ROWRED_CHUNK_ROW(kOpLayerNorm),
     ROWRED_CHUNK_ROW(kOpRms),
     ROWRED_CHUNK_ROW(kOpSoftmax),
+    ROWRED_CHUNK_ROW(kOpRowSum),
+    ROWRED_CHUNK_ROW(kOpRowMinMax),
     ROWRED_CHUNK_ROW(kOpLayerNormAffine),
 };
+static_assert(kOpLayerNormAffine == 5 && kOpRowSum == 3 && kOpRowMinMax == 4, "kernel table order");
 #undef ROWRED_CHUNK_ROW
 
 static_assert(kNumChunkSizes == 11, "kernel table rows must match kChunkSet");

@@ -75,10 +75,13 @@ CONFIGS = {
 
 # Workloads of the next steps beyond the three core operators: plain
 # LayerNorm at the shape the pages time it (1024x4096) and at the wide-row
-# shape, and affine LayerNorm (gamma ~ 1 + 0.1 N(0,1), beta ~ 0.1 N(0,1)).
+# shape, affine LayerNorm (gamma ~ 1 + 0.1 N(0,1), beta ~ 0.1 N(0,1)), and
+# the row sum / paired min-max reductions at a wide and a short ragged shape.
 NEXT_CONFIGS = {
     6: [Case(6, "layernorm", 1024, 4096, "uniform"), Case(6, "layernorm", 16384, 8192, "uniform")],
     7: [Case(7, "layernorm_affine", 1024, 4096, "uniform"), Case(7, "layernorm_affine", 16384, 8192, "uniform")],
+    8: [Case(8, "row_sum", 16384, 8192, "uniform"), Case(8, "row_minmax", 16384, 8192, "uniform"),
+        Case(8, "row_sum", 131072, 257, "normal"), Case(8, "row_minmax", 131072, 257, "normal")],
 }
 
 

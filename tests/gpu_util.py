@@ -63,3 +63,21 @@ def assert_close(y, ref, what=""):
 
 def print_case(*parts):
     print("CASE", *parts, flush=True)
+
+
+def all_plans(window):
+    """Every explicit plan (lanes, chunks, threads, policy) that covers a row
+    window of `window` granules without a wholly idle lane group."""
+    import row_wise_reduction_amd as R
+    chunks_set = (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16)
+    for L in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        for C in chunks_set:
+            if L * C < window or (L > 1 and L * C >= 2 * window + 4 * L):
+                continue
+            for T in sorted({max(64, L), 256, 1024 if C <= 8 else 512}):
+                if T < L or T % L or T > (1024 if C <= 8 else 512):
+                    continue
+                for policy in (0, 3, 4, 7, 8, 11, 15):
+                    if policy & R.ROWRED_POLICY_STAGE_STORES and (C > 4 or T > 512):
+                        continue
+                    yield R.Plan(lanes_per_row=L, rows_per_group=0, chunks=C, threads=T, grid=0, policy=policy)

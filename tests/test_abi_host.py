@@ -290,3 +290,24 @@ def test_layernorm_entry_argument_checks():
 def test_plan_query_layernorm_without_residual():
     p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=1024, width=4096)
     assert (p.lanes_per_row, p.chunks) == (256, 4)
+
+
+def test_row_reduce_argument_checks():
+    lib = R.lib()
+    O1, O2 = 0x7F4000000000, 0x7F5000000000
+    assert lib.rowred_row_sum(X, O1, 0, 64, None) == R.ROWRED_OK            # nothing to do
+    assert lib.rowred_row_sum(X, O1, 4, 0, None) == R.ROWRED_ERR_INVALID_ARG  # rows need an element
+    assert lib.rowred_row_sum(X, O1, -1, 4, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_sum(X, None, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_sum(X, O1 + 2, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_sum(X, X + 8, 4, 4, None) == R.ROWRED_ERR_ALIAS   # out inside x
+    assert lib.rowred_row_minmax(X, O1, None, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_minmax(X, O1, O1 + 8, 4, 4, None) == R.ROWRED_ERR_ALIAS  # min and max overlap
+    assert lib.rowred_row_minmax(X, O1, X, 4, 4, None) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_row_sum(X, O1, 4, 32769, None) == R.ROWRED_ERR_UNSUPPORTED
+    # staging does not apply to scalar outputs
+    c = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=R.ROWRED_POLICY_STAGE_STORES)._c()
+    assert lib.rowred_row_reduce_run_plan(3, X, O1, None, 8, 127, ctypes.byref(c), None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_reduce_run_plan(1, X, O1, None, 8, 127, ctypes.byref(c), None) == R.ROWRED_ERR_INVALID_ARG
+    p = R.rowred_plan_query("row_minmax", X, O2, O1, rows=1024, width=4096)
+    assert p.lanes_per_row * p.chunks >= p.window and p.policy & R.ROWRED_POLICY_STAGE_STORES == 0
