@@ -9,9 +9,14 @@ softmax on 1024x4096 FP32, inputs U[-1, 1]).  Inputs and outputs are
 resident in HBM before timing starts.  Each operator's K timed calls run on
 its own rotation of >= 3 buffer sets totalling >= 2 GiB, so no call finds its
 data in the 256 MB last-level cache; the K calls are captured in one HIP graph per
-operator so the host's launch cost does not gate 5-10 us kernels.  HIP
-events on the launch stream bracket each graph replay; an operator's average
-call time is its replay time / K.
+operator so the host's launch cost does not gate 5-10 us kernels.  After W
+eager warm-up steps the graphs are replayed, untimed, for 0.2 s; then the
+timed region replays each graph once (exactly K steps), with HIP events on
+the launch stream around each replay: an operator's average call time is
+its replay time / K.  Five more replays give the spread (median, min, max)
+of that measurement; each operator also reports one cold call after a 1 GiB
+flush, a warm rate (K calls on one buffer set, cache-resident where it
+fits) and its fraction of the library's copy moving the same bytes.
 
 `value` is the whole step's algorithmic bytes (one read of each input and
 one write of the output, 4 B per element each) divided by its time.  The
@@ -23,6 +28,8 @@ oracle's throughput on host cores, and per-operator figures.
                                 # copy per workload for calibration
     python bench.py --all       # one JSON line per core workload (1..5)
     python bench.py --next      # plain and affine LayerNorm, row sum / min-max (6-8)
+    python bench.py --reload    # resident vs per-phase reload kernels, workloads 2-5
+    python bench.py --pmc --reload  # its counter pass
 """
 from __future__ import annotations
 
@@ -44,6 +51,8 @@ import synthetic  # noqa: E402
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "HBM GB/s and % of peak, FP32 row LayerNorm/RMSNorm/softmax, µs per call"
 POOL_BYTES = 2 * 2 ** 30  # >= 8x the 256 MB last-level cache
+WARMUP_SECONDS = 0.2  # graph replays before the timed region
+ROUNDS = 5  # repeats of the timed measurement, reported as its spread
 
 # The pages' Apple M1 Max numbers at 1024x4096 (context only, other hardware):
 # "Immutable input reuse in Metal reductions", section "Fixed-width GPU and
@@ -170,30 +179,76 @@ def time_workload(cfg, steps, warmup):
                     b.call(i)
             graphs.append(g)
     torch.cuda.current_stream().wait_stream(stream)
-    for g in graphs:  # untimed replay: first-replay setup out of the timed region
-        g.replay()
-    torch.cuda.synchronize()
+    # Untimed: replay the graphs until >= WARMUP_SECONDS have passed, so the
+    # first replay's setup and the GPU's clock ramp stay out of the timing.
+    t = time.perf_counter()
+    while True:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t >= WARMUP_SECONDS:
+            break
 
-    # Timed region: replay each case's graph between HIP events on the stream
-    # the kernels run on (torch's current stream).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in graphs]
+    # Timed region: exactly `steps` steps -- each case's graph replayed once
+    # between HIP events on the stream the kernels run on (torch's current
+    # stream).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    per_case_ms, total_ms = replay_timed(graphs)
+    wall = time.perf_counter() - t0
+    # The same measurement repeated, outside the reported value: its spread.
+    rounds = [replay_timed(graphs)[0] for _ in range(ROUNDS)]
+    return cases, bufs, sets, per_case_ms, total_ms, wall, rounds
+
+
+def replay_timed(graphs):
+    """Replay each graph once between HIP events; per-graph ms and the span."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in graphs]
     for g, (a, b) in zip(graphs, evs):
         a.record()
         g.replay()
         b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_case_ms = [a.elapsed_time(b) for a, b in evs]
-    total_ms = evs[0][0].elapsed_time(evs[-1][1])
-    return cases, bufs, sets, per_case_ms, total_ms, wall
+    return [a.elapsed_time(b) for a, b in evs], evs[0][0].elapsed_time(evs[-1][1])
 
 
-def cpu_baseline(cases, bufs, seconds):
+def single_and_warm(b, steps, reps=3):
+    """(cold single call us, warm us per call): one eager call after a 1 GiB
+    flush, median of `reps`; and a graph of `steps` calls all on buffer set
+    0, so that inputs that fit the 256 MB last-level cache stay there."""
+    import torch
+    flush = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    cold = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.call(0)
+        e.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(e) * 1e3)
+    del flush
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(steps):
+                b.call(0)
+    torch.cuda.current_stream().wait_stream(stream)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms, _ = replay_timed([g])
+    return float(np.median(cold)), ms[0] * 1e3 / steps
+
+
+def cpu_baseline(cases, bufs, seconds, threads=None):
     """The FP64 oracle on host cores, on a bounded sample of each case."""
     import oracle
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     done_bytes = 0
     elapsed = 0.0
     sample_desc = []
@@ -239,16 +294,23 @@ def read_traffic(cfg, case):
 
 
 def bench(cfg, steps, warmup, cpu_seconds):
-    cases, bufs, sets, per_case_ms, total_ms, wall = time_workload(cfg, steps, warmup)
+    cases, bufs, sets, per_case_ms, total_ms, wall, rounds = time_workload(cfg, steps, warmup)
     step_bytes = sum(algo_bytes(c) for c in cases)
     ms_per_step = total_ms / steps
     value = step_bytes * steps / (total_ms / 1e3) / 1e9
     ops = {}
-    for c, ms in zip(cases, per_case_ms):
+    for i, (c, b, ms) in enumerate(zip(cases, bufs, per_case_ms)):
         us = ms * 1e3 / steps
         gbs = algo_bytes(c) / (us * 1e-6) / 1e9
-        ops[f"{c.op} {c.rows}x{c.width}"] = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1),
-                                             "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        r_us = [r[i] * 1e3 / steps for r in rounds]
+        cold, warm = single_and_warm(b, steps)
+        copy = copy_ceiling(algo_bytes(c))
+        ops[f"{c.op} {c.rows}x{c.width}"] = {
+            "us_per_call": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "frac_of_copy": round(gbs / copy["GB_s"], 4),
+            "rounds_us": {"n": len(r_us), "median": round(float(np.median(r_us)), 3),
+                          "min": round(min(r_us), 3), "max": round(max(r_us), 3)},
+            "single_call_cold_us": round(cold, 3), "warm_us_per_call": round(warm, 3)}
     dom = int(np.argmax(per_case_ms))
     dc = cases[dom]
     dom_us = per_case_ms[dom] * 1e3 / steps
@@ -277,6 +339,7 @@ def bench(cfg, steps, warmup, cpu_seconds):
         out["context_m1max_us"] = M1MAX_CONTEXT_US
     if cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(cases, bufs, cpu_seconds)
+        out["cpu_baseline_1core"] = cpu_baseline(cases, bufs, cpu_seconds / 4, threads=1)
     return out
 
 
@@ -330,6 +393,112 @@ def pmc_pass(cfg):
         torch.cuda.synchronize()
         print(f"pmc dispatch {b.case.op} {b.case.rows}x{b.case.width}", flush=True)
     n = 2 ** 26  # 256 MiB of float32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    flush.fill_(2.0)
+    R.rowred_copy(src, dst)
+    torch.cuda.synchronize()
+    print(f"pmc copy {n * 4} bytes read, {n * 4} bytes written", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# per-phase reload A/B: the reference design's reloads as a diagnostic
+# ---------------------------------------------------------------------------
+
+RELOAD_CFGS = (2, 3, 4, 5)
+# resident: the chooser's plan; reload: the same plan re-reading the row in
+# every phase after the first; reload_cached: that without the non-temporal
+# load hint, so the re-reads may hit in L2.
+RELOAD_VARIANTS = ("resident", "reload", "reload_cached")
+
+
+def variant_plan(case, b, variant):
+    import row_wise_reduction_amd as R
+    p = R.rowred_plan_query(case.op, b.x[0], b.r[0], b.y[0])
+    pol = p.policy
+    if variant != "resident":
+        pol |= R.ROWRED_POLICY_RELOAD
+    if variant == "reload_cached":
+        pol &= ~R.ROWRED_POLICY_NT_LOADS
+    return R.Plan(p.lanes_per_row, 0, p.chunks, p.threads, 0, policy=pol)
+
+
+def plan_call(b, plan, i):
+    import row_wise_reduction_amd as R
+    k = i % b.sets
+    R.rowred_run_plan(b.case.op, b.x[k], b.r[k], b.y[k], plan, eps=b.case.eps or 0.0)
+
+
+def time_reload(cfg, steps, warmup, rounds=3):
+    """us per call of each variant at each case of a workload: one HIP graph
+    of `steps` calls per variant on rotating buffers; the rounds interleave
+    the variants and the minimum over rounds is kept."""
+    import torch
+    ops = {}
+    for case in WORKLOADS[cfg]:
+        b = CaseBuffers(case, rotation_sets(case))
+        plans = {v: variant_plan(case, b, v) for v in RELOAD_VARIANTS}
+        for v in RELOAD_VARIANTS:
+            for i in range(warmup):
+                plan_call(b, plans[v], i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graphs = {}
+        with torch.cuda.stream(stream):
+            for v in RELOAD_VARIANTS:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(steps):
+                        plan_call(b, plans[v], i)
+                graphs[v] = g
+        torch.cuda.current_stream().wait_stream(stream)
+        for g in graphs.values():
+            g.replay()
+        torch.cuda.synchronize()
+        us = {v: [] for v in RELOAD_VARIANTS}
+        for _ in range(rounds):
+            for v, g in graphs.items():
+                a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                e.record()
+                torch.cuda.synchronize()
+                us[v].append(a.elapsed_time(e) * 1e3 / steps)
+        entry = {}
+        for v in RELOAD_VARIANTS:
+            t = min(us[v])
+            entry[v] = {"us_per_call": round(t, 3), "GB_s": round(algo_bytes(case) / (t * 1e-6) / 1e9, 1),
+                        "policy": plans[v].policy, "rounds_us": [round(u, 3) for u in us[v]]}
+        entry["reload_over_resident"] = round(entry["reload"]["us_per_call"] / entry["resident"]["us_per_call"], 3)
+        entry["plan"] = f"L{plans['resident'].lanes_per_row} C{plans['resident'].chunks} T{plans['resident'].threads}"
+        ops[f"{case.op} {case.rows}x{case.width}"] = entry
+        del b, graphs
+        torch.cuda.empty_cache()
+    return {"mode": "reload_ab", "config": {"workload": WORKLOAD_NAMES[cfg], "config_id": cfg}, "steps": steps,
+            "warmup": warmup, "unit": "GB/s", "ops": ops, "kernel_source_hash": kernel_source_hash(),
+            "note": "GB/s counts one read of each input and one write of the output, as for the resident kernels"}
+
+
+def pmc_reload_pass(cfg):
+    """One dispatch of each reload variant per case, each on buffers written
+    just before by a 1 GiB flush, then the 256 MiB calibration copy."""
+    import torch
+
+    import row_wise_reduction_amd as R
+    flush = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    print(f"pmc kernel_source_hash {kernel_source_hash()}", flush=True)
+    for case in WORKLOADS[cfg]:
+        b = CaseBuffers(case, 1)
+        for v in RELOAD_VARIANTS:
+            plan = variant_plan(case, b, v)
+            flush.fill_(1.0)
+            torch.cuda.synchronize()
+            plan_call(b, plan, 0)
+            torch.cuda.synchronize()
+            print(f"pmc dispatch {v} {case.op} {case.rows}x{case.width}", flush=True)
+        del b
+    n = 2 ** 26
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     flush.fill_(2.0)
@@ -428,6 +597,64 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
     return written
 
 
+PMC_RELOAD_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {ctr} --output-format csv -d <out_{ctr}> -o run -- "
+                  "python3 <repo>/bench.py --pmc --reload > <log_{ctr}>")
+
+
+def reload_traffic_summary(fetch_csv, write_csv, out_path, fetch_log=None, write_log=None):
+    """Write the HBM traffic of the resident and reload variants from the two
+    counter passes of `bench.py --pmc --reload`."""
+    expected = [(cfg, c, v) for cfg in RELOAD_CFGS for c in WORKLOADS[cfg] for v in RELOAD_VARIANTS]
+    got = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        i = 0
+        pending = []
+        for row in _csv_rows(path):
+            if row["Counter_Name"] != ctr:
+                continue
+            name = row["Kernel_Name"]
+            if "rows_kernel" in name or "reload_kernel" in name:
+                cfg, case, v = expected[i]
+                want = "rows_kernel" if v == "resident" else "reload_kernel"
+                if want not in name:
+                    raise SystemExit(f"{path}: dispatch {i} is {name}, expected a {want} ({v})")
+                pending.append((case, v, float(row["Counter_Value"])))
+                i += 1
+            elif "copy_kernel" in name:
+                copy_kib = float(row["Counter_Value"])
+                for case, v, kib in pending:
+                    got.setdefault((case, v), {})[ctr] = kib * 1024 * (2 ** 28) / (copy_kib * 1024)
+                pending = []
+        if i != len(expected):
+            raise SystemExit(f"{path}: found {i} reduction dispatches, expected {len(expected)}")
+    h = _logged_hash(fetch_log)
+    if _logged_hash(write_log) != h:
+        h = "unknown"
+    lines = ["# HBM traffic per dispatch: resident kernels vs the per-phase reload variant",
+             "# (reload: every phase after the first reads x, and r, again; reload_cached: the same",
+             "# without the non-temporal load hint).  One dispatch per variant on cold buffers, each",
+             "# counter scaled by what it reads for the 256 MiB copy that ends each workload's pass.",
+             "#   " + PMC_RELOAD_CMD.format(ctr="FETCH_SIZE"),
+             "#   " + PMC_RELOAD_CMD.format(ctr="WRITE_SIZE"),
+             "# reads_algorithmic: one read of each input; reads_requested: what the kernel asks",
+             "# for (x and r once per phase); fetch: HBM bytes read.",
+             f"kernel_source_hash: {h}"]
+    for cfg in RELOAD_CFGS:
+        for case in WORKLOADS[cfg]:
+            alg_r, alg_w = algo_split(case)
+            phases = {"layernorm_residual": 3, "rmsnorm": 2, "softmax": 3}[case.op]
+            for v in RELOAD_VARIANTS:
+                d = got[(case, v)]
+                req = alg_r * (1 if v == "resident" else phases)
+                key = f"{v} {case.op} {case.rows}x{case.width}"
+                lines.append(f"fetch_bytes[{key}]: {d['FETCH_SIZE']:.0f} (reads_algorithmic {alg_r}, "
+                             f"reads_requested {req}, fetch/algorithmic {d['FETCH_SIZE'] / alg_r:.4f})")
+                lines.append(f"write_bytes[{key}]: {d['WRITE_SIZE']:.0f} (algorithmic {alg_w}, "
+                             f"ratio {d['WRITE_SIZE'] / alg_w:.4f})")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    return out_path
+
+
 def trace_summary(stats_csv, bench_json, out_path):
     """Write the rocprofv3 kernel statistics of the default benchmark command
     next to the benchmark's own HIP-event averages."""
@@ -460,6 +687,10 @@ def main(argv=None):
     ap.add_argument("--next", action="store_true", help="one line per next-step workload (6, 7, 8)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
+    ap.add_argument("--reload", action="store_true",
+                    help="resident vs per-phase reload A/B at workloads 2-5 (with --pmc: its counter pass)")
+    ap.add_argument("--reload-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_LOG", "WRITE_LOG"),
+                    help="write profiles/pmc_traffic_reload.txt from the two reload counter passes (no GPU)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_LOG", "WRITE_LOG"),
                     help="write profiles/pmc_traffic_cfg*.txt from two counter passes and their stdout logs "
                          "(no GPU)")
@@ -474,6 +705,10 @@ def main(argv=None):
     if args.trace_summary:
         print(trace_summary(*args.trace_summary))
         return 0
+    if args.reload_summary:
+        fc, wc, fl, wl = args.reload_summary
+        print(reload_traffic_summary(fc, wc, os.path.join(ROOT, "profiles", "pmc_traffic_reload.txt"), fl, wl))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: rows are independent, so N GPUs would each "
                                    "run the same kernel on rows/N; only --gpus 1 is measured"}))
@@ -484,9 +719,17 @@ def main(argv=None):
         return 1
     import row_wise_reduction_amd as R
     R.lib()  # fail loudly if the HIP library is not built
+    if args.pmc and args.reload:
+        for cfg in RELOAD_CFGS:
+            pmc_reload_pass(cfg)
+        return 0
     if args.pmc:
         for cfg in (sorted(WORKLOAD_NAMES) if args.all else [args.config]):
             pmc_pass(cfg)
+        return 0
+    if args.reload:
+        for cfg in RELOAD_CFGS:
+            print(json.dumps(time_reload(cfg, args.steps, args.warmup)), flush=True)
         return 0
     cfgs = list(CORE) if args.all else list(NEXT) if args.next else [args.config]
     for cfg in cfgs:

@@ -187,18 +187,30 @@ enum rowred_policy {
   ROWRED_POLICY_NT_LOADS = 1,   /* loads carry the non-temporal (streaming) hint */
   ROWRED_POLICY_NT_STORES = 2,  /* stores carry the non-temporal hint */
   ROWRED_POLICY_XCD_REMAP = 4,  /* each XCD walks one contiguous range of row blocks */
-  ROWRED_POLICY_STAGE_STORES = 8 /* a workgroup's outputs (its rows are consecutive) are
-                                    assembled in LDS and stored as whole 16-byte granules by
-                                    consecutive threads; needs y at x's 16-byte phase,
-                                    threads <= 512 and chunks <= 4 */
+  ROWRED_POLICY_STAGE_STORES = 8, /* a workgroup's outputs (its rows are consecutive) are
+                                     assembled in LDS and stored as whole 16-byte granules by
+                                     consecutive threads; needs y at x's 16-byte phase,
+                                     threads <= 512 and chunks <= 4 */
+  ROWRED_POLICY_RELOAD = 16       /* diagnostic: every phase after the first reads x (and r)
+                                     again instead of keeping the row in registers, and
+                                     recomputes what it derives from them (the per-phase
+                                     reload of the reference design in "Immutable input reuse
+                                     in Metal reductions", section "What the transformation
+                                     actually preserves").  Same arithmetic, same results,
+                                     more reads.  Matrix operators only (LayerNorm without
+                                     gamma/beta, RMSNorm, softmax), chunks <= 8, LayerNorm at
+                                     7-8 chunks with threads <= 512; never chosen by the
+                                     entry points */
 };
 
 /*
  * Host-only: fill *out with the plan the matching entry point would launch
  * for these arguments (x, r, y are only inspected for their alignment; r may
  * be NULL: for ROWRED_OP_LAYERNORM_RESIDUAL that is the plan of
- * rowred_layernorm without a residual).  No device work, callable without a
- * GPU.  Returns the status the entry point would return before launching.
+ * rowred_layernorm without a residual; for ROWRED_OP_ROW_SUM and
+ * ROWRED_OP_ROW_MINMAX, y is out / out_min and r is out_max, vectors of
+ * `rows` floats).  No device work, callable without a GPU.  Returns the
+ * status the entry point would return before launching.
  */
 int rowred_plan_query(int op, const float *x, const float *r, const float *y,
                       int64_t rows, int64_t width, rowred_plan *out);

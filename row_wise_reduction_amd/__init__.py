@@ -32,6 +32,7 @@ ROWRED_POLICY_NT_LOADS = 1
 ROWRED_POLICY_NT_STORES = 2
 ROWRED_POLICY_XCD_REMAP = 4
 ROWRED_POLICY_STAGE_STORES = 8
+ROWRED_POLICY_RELOAD = 16
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1
@@ -272,11 +273,20 @@ def _op_id(op):
 
 
 def rowred_plan_query(op, x, r, y, rows=None, width=None) -> Plan:
-    """The plan the entry point would launch (host only; no device work)."""
-    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
-    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    """The plan the entry point would launch (host only; no device work).
+    For row_sum / row_minmax, y is the (first) output vector and r the
+    row-max vector of row_minmax."""
+    op = _op_id(op)
+    if op in (OPS["row_sum"], OPS["row_minmax"]):
+        mx = _matrix(x, "x", rows, width)
+        rows, width = _shape([("x", mx)], rows, width)
+        ar, ay = _row_vector(r, "out_max", rows), _row_vector(y, "out", rows)
+    else:
+        mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+        rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+        ar, ay = mr[0], my[0]
     p = _Plan()
-    st = lib().rowred_plan_query(_op_id(op), mx[0], mr[0], my[0], rows, width, ctypes.byref(p))
+    st = lib().rowred_plan_query(op, mx[0], ar, ay, rows, width, ctypes.byref(p))
     _check(st, "rowred_plan_query")
     return Plan(p.lanes_per_row, p.rows_per_group, p.chunks, p.threads, p.grid, p.vector_io, p.window, p.policy,
                 p.reserved)

@@ -108,6 +108,9 @@ int finish_plan(const Call &c, rowred_plan *p) {
   if (!chunks_supported(p->chunks) || !kernel_exists(kop, p->chunks) || T > max_threads_for(kop, p->chunks))
     return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~kPolicyAll) return ROWRED_ERR_INVALID_ARG;
+  if ((p->policy & kPolicyReload) &&
+      (!reload_kernel_exists(kop, p->chunks) || T > reload_max_threads_for(kop, p->chunks)))
+    return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
@@ -138,7 +141,11 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // the window.  Workgroups have max(256, L) threads for small inputs and
 // max(512, L) for large ones.
 //
-// Memory policy: streaming (non-temporal) stores are fastest.  Where rows
+// Memory policy: streaming (non-temporal) loads are 3-9% faster than cached
+// ones at every workload shape except short rows that do not start on
+// 16-byte boundaries (127 and 257 columns, 3-4% slower): neighbouring rows
+// there share their boundary granule, which is read twice, once by each
+// row's lanes.  Streaming (non-temporal) stores are fastest.  Where rows
 // do not start on 16-byte boundaries, the cache lines at row boundaries
 // hold two rows' outputs written by different lanes at different times,
 // and each part leaves as its own partial line write-back (up to 1.46x the
@@ -149,15 +156,22 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // 16-byte phase than x) stores stay cached beyond 2 slots per lane.  The XCD
 // remap (each XCD walks one contiguous range of rows) pays off for aligned
 // rows once the grid runs in several rounds (> 64 MiB per input).
+//
+// Row sum and min/max read only: nothing waits on stores, and idle slots
+// cost more than long stripes.  With at most 4 slots per lane and at least
+// 512 threads, 16384x8192 runs at 78-80 us and 131072x257 at 23-24 us,
+// against 90-100 us and 32-36 us with the 2-slot stripes above (L = 64 x 2
+// slots leaves half of each 257-column row's lanes idle).
 void choose_plan(const Call &c, rowred_plan *p) {
   const int64_t w = c.window;
   const int64_t in_bytes = c.rows * c.width * 4;
   const bool small = in_bytes <= (int64_t(32) << 20);
   const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+  const bool scalar_out = c.op == ROWRED_OP_ROW_SUM || c.op == ROWRED_OP_ROW_MINMAX;
   const bool stage_ok = !rows_aligned && c.y_vec;
   // Staged rows that fit one wavefront (<= 64 lanes x 4 slots) store through
   // LDS, so their lanes can hold more slots.
-  const int64_t max_chunks = (small || (stage_ok && w <= 256)) ? 4 : 2;
+  const int64_t max_chunks = (small || scalar_out || (stage_ok && w <= 256)) ? 4 : 2;
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
   int chunks = round_up_chunks((w + L - 1) / L);
@@ -171,11 +185,12 @@ void choose_plan(const Call &c, rowred_plan *p) {
   }
   p->lanes_per_row = (int32_t)L;
   p->chunks = chunks;
-  const int64_t t_min = small ? 256 : 512;
+  const int64_t t_min = small && !scalar_out ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
-  int policy = kPolicyNtLoads;
-  if (rows_aligned || can_stage || p->chunks <= 2) policy |= kPolicyNtStores;
+  int policy = 0;
+  if (!(can_stage && w <= 256)) policy |= kPolicyNtLoads;
+  if (!scalar_out && (rows_aligned || can_stage || p->chunks <= 2)) policy |= kPolicyNtStores;
   if (can_stage) policy |= kPolicyStageStores;
   if (rows_aligned && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
   p->policy = policy;

@@ -31,7 +31,15 @@ constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;
 constexpr int kPolicyNtStores = ROWRED_POLICY_NT_STORES;
 constexpr int kPolicyXcdRemap = ROWRED_POLICY_XCD_REMAP;
 constexpr int kPolicyStageStores = ROWRED_POLICY_STAGE_STORES;
-constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores;
+constexpr int kPolicyReload = ROWRED_POLICY_RELOAD;
+constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload;
+// The per-phase reload variant exists for the three matrix operators (kernel
+// ops 0-2) at up to 8 chunks.
+constexpr int kMaxReloadChunks = 8;
+constexpr bool reload_kernel_exists(int op, int chunks) { return op >= 0 && op <= 2 && chunks <= kMaxReloadChunks; }
+// LayerNorm's reload kernels rebuild x + r as a pair in the last two phases;
+// from 7 chunks on that needs the registers of a 512-thread workgroup.
+constexpr int reload_max_threads_for(int op, int chunks) { return op == 0 && chunks >= 7 ? 512 : 1024; }
 constexpr int kMaxStageThreads = 512;  // workgroup size the staged stores support
 constexpr int kMaxStageChunks = 4;     // chunks per lane the staged stores are compiled for
 // LDS for a staged workgroup: its rows span at most threads*chunks granules

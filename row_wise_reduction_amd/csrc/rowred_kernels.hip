@@ -169,6 +169,31 @@ __device__ __forceinline__ T row_allreduce(T v, int lanes_log2, T *partials) {
   return v;
 }
 
+// Two row all-reduces that share one LDS exchange and one barrier (paired
+// min/max): both wave partials are written before the barrier.
+template <class R1, class R2>
+__device__ __forceinline__ void row_allreduce_pair(float &v1, float &v2, int lanes_log2, float *p1, float *p2) {
+  v1 = group_allreduce<R1>(v1, lanes_log2 < 6 ? lanes_log2 : 6);
+  v2 = group_allreduce<R2>(v2, lanes_log2 < 6 ? lanes_log2 : 6);
+  if (lanes_log2 > 6) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      p1[wave] = v1;
+      p2[wave] = v2;
+    }
+    __syncthreads();
+    const int per_row_log2 = lanes_log2 - 6;
+    const int first = (wave >> per_row_log2) << per_row_log2;
+    float a1 = p1[first], a2 = p2[first];
+    for (int w = 1; w < (1 << per_row_log2); ++w) {
+      a1 = R1::apply(a1, p1[first + w]);
+      a2 = R2::apply(a2, p2[first + w]);
+    }
+    v1 = a1;
+    v2 = a2;
+  }
+}
+
 // Workgroup -> row block.  The dispatcher deals workgroups to the 8 XCDs in
 // turn; give XCD x the contiguous block range [x*q + min(x, rem), ...).
 __device__ __forceinline__ int64_t row_block(uint32_t bid, uint32_t nblk, bool remap) {
@@ -191,8 +216,10 @@ __device__ __forceinline__ float identity() {
 // time when they share x's address modulo 16 (a.r_vec / a.y_vec), otherwise
 // 4 bytes at a time at the same element positions.
 // ---------------------------------------------------------------------------
-template <int OP, int C>
-__global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a) {
+// `threads` is blockDim.x, read in the kernel itself: there the compiler
+// knows workgroups are uniform and reads it with a scalar load.
+template <int OP, int C, bool RELOAD>
+__device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
   __shared__ float partials[2][16];
   __shared__ double partials_d[16];
 
@@ -200,7 +227,7 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   const int L = 1 << lanes_log2;
   const int li = threadIdx.x & (L - 1);
   const int slot = threadIdx.x >> lanes_log2;
-  const int rows_per_group = blockDim.x >> lanes_log2;
+  const int rows_per_group = threads >> lanes_log2;
   const int width = a.width;
 
   int64_t row = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0) * rows_per_group + slot;
@@ -234,8 +261,15 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   f32x4 xv[C], rv[C];
   auto load_rows = [&](auto nt) {
     constexpr bool NT = decltype(nt)::value;
+    // The two instances of this block are the same instructions except for
+    // the loads' cache hint, which is metadata until late in code generation:
+    // the optimizer would hoist (or sink) the common loads out of the branch
+    // on the policy and drop the non-temporal hint.  Empty asm statements
+    // around the non-temporal loads keep the two copies apart.
+    if constexpr (NT) asm volatile("" ::: "memory");
 #pragma unroll
     for (int c = 0; c < C; ++c) xv[c] = load_g<NT>(xw + min(c * L + li, kmax));
+    if constexpr (NT) asm volatile("" ::: "memory");
     if (has_r) {
       if (a.r_vec) {
         const f32x4 *rw = reinterpret_cast<const f32x4 *>(rrow - off);
@@ -257,6 +291,14 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   };
   if (nt_loads) load_rows(std::true_type{});
   else load_rows(std::false_type{});
+  // Per-phase reload (RELOAD kernels, a diagnostic): read the row again.
+  // The empty asm with a memory clobber keeps the compiler from reusing the
+  // values of the earlier loads.
+  auto reload = [&]() {
+    asm volatile("" ::: "memory");
+    if (nt_loads) load_rows(std::true_type{});
+    else load_rows(std::false_type{});
+  };
   // ---- scalar-per-row reductions: no output map, one lane writes the row.
   if constexpr (OP == kOpRowSum) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -284,8 +326,7 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
       }
     float mn = fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3]));
     float mx = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
-    mn = row_allreduce<MinOp>(mn, lanes_log2, partials[0]);
-    mx = row_allreduce<MaxOp>(mx, lanes_log2, partials[1]);
+    row_allreduce_pair<MinOp, MaxOp>(mn, mx, lanes_log2, partials[0], partials[1]);
     if (live && li == 0) {
       a.y[row] = mn;
       a.y2[row] = mx;
@@ -293,12 +334,14 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
     return;
   }
 
-  if constexpr (!is_layernorm(OP)) {
+  // The stripe of x, with the reduction's identity outside the row.
+  auto fill_stripe = [&]() {
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) s[4 * c + j] = valid(c, j) ? xv[c][j] : identity<OP>();
-  }
+  };
+  if constexpr (!is_layernorm(OP)) fill_stripe();
 
   // ---- phases.
   if constexpr (OP == kOpRms) {
@@ -308,6 +351,10 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
     float ss = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     ss = row_allreduce<SumOp>(ss, lanes_log2, partials[0]);
     const float scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
+    if constexpr (RELOAD) {
+      reload();
+      fill_stripe();
+    }
 #pragma unroll
     for (int i = 0; i < 4 * C; ++i) s[i] *= scale;
   } else if constexpr (OP == kOpSoftmax) {
@@ -316,15 +363,26 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
     for (int i = 4; i < 4 * C; ++i) mx[i & 3] = fmaxf(mx[i & 3], s[i]);
     float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    auto exp_stripe = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4 * C; ++i) s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);  // exp(x - m); -inf -> 0
+    };
+    if constexpr (RELOAD) {
+      reload();
+      fill_stripe();
+    }
+    exp_stripe();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4 * C; ++i) {
-      s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);  // exp(x - m); -inf -> 0
-      acc[i & 3] += s[i];
-    }
+    for (int i = 0; i < 4 * C; ++i) acc[i & 3] += s[i];
     float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
     const float inv = __builtin_amdgcn_rcpf(sum);
+    if constexpr (RELOAD) {
+      reload();
+      fill_stripe();
+      exp_stripe();
+    }
 #pragma unroll
     for (int i = 0; i < 4 * C; ++i) s[i] *= inv;
   } else {  // LayerNorm
@@ -342,37 +400,52 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
     //    second is tiny.
     // From here on every error is relative; variance and output are FP32.
     float hi[4 * C], lo[4 * C];
+    auto combine = [&]() {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float xv_ = valid(c, j) ? xv[c][j] : 0.0f;
+          const float rv_ = valid(c, j) ? rv[c][j] : 0.0f;
+          const float h = xv_ + rv_;
+          const float bb = h - xv_;
+          const float l = (xv_ - (h - bb)) + (rv_ - bb);  // exact: h + l == xv_ + rv_
+          hi[4 * c + j] = h;
+          lo[4 * c + j] = l;
+        }
+    };
+    combine();
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     float acc_lo = 0.0f;
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float xv_ = valid(c, j) ? xv[c][j] : 0.0f;
-        const float rv_ = valid(c, j) ? rv[c][j] : 0.0f;
-        const float h = xv_ + rv_;
-        const float bb = h - xv_;
-        const float l = (xv_ - (h - bb)) + (rv_ - bb);  // exact: h + l == xv_ + rv_
-        hi[4 * c + j] = h;
-        lo[4 * c + j] = l;
-        acc[j] += (double)h;
-        acc_lo += l;
+        acc[j] += (double)hi[4 * c + j];
+        acc_lo += lo[4 * c + j];
       }
     double sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo;
     sum = row_allreduce<SumOp>(sum, lanes_log2, partials_d);
     const double mean = sum / (double)width;
     const float m_hi = (float)mean;
     const float m_lo = (float)(mean - (double)m_hi);
+    auto centre = [&]() {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * c + j;
+          s[i] = valid(c, j) ? (hi[i] - m_hi) + (lo[i] - m_lo) : 0.0f;  // outside the row: 0
+        }
+    };
+    if constexpr (RELOAD) {
+      reload();
+      combine();
+    }
+    centre();
     float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * c + j;
-        const float d = valid(c, j) ? (hi[i] - m_hi) + (lo[i] - m_lo) : 0.0f;  // outside the row: 0
-        s[i] = d;
-        sq[j] = fmaf(d, d, sq[j]);
-      }
+    for (int i = 0; i < 4 * C; ++i) sq[i & 3] = fmaf(s[i], s[i], sq[i & 3]);
     float var = (sq[0] + sq[1]) + (sq[2] + sq[3]);
     // Affine LayerNorm: gamma and beta hold one value per column.  They are
     // cached loads (every row reuses them).  With few chunks they go out
@@ -406,6 +479,11 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
     if constexpr (kEarlyAffine) load_affine();
     var = row_allreduce<SumOp>(var, lanes_log2, partials[1]);
     const float rstd = __builtin_amdgcn_rsqf(fmaf(var, a.inv_width, a.eps));
+    if constexpr (RELOAD) {
+      reload();
+      combine();
+      centre();
+    }
     if constexpr (kEarlyAffine) {
 #pragma unroll
       for (int c = 0; c < C; ++c)
@@ -507,7 +585,7 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
       f32x4 *yg = reinterpret_cast<f32x4 *>(a.y + e_begin - fb);  // 16-byte aligned: y shares x's phase
       auto store_run = [&](auto nt) {
         constexpr bool NT = decltype(nt)::value;
-        for (int g = threadIdx.x; g < n_granules; g += blockDim.x) {
+        for (int g = threadIdx.x; g < n_granules; g += threads) {
           const f32x4 v = stage[g];
           const int64_t e0 = e_begin - fb + 4 * (int64_t)g;
           if (e0 >= e_begin && e0 + 4 <= e_end) {
@@ -527,6 +605,18 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   if (!live) return;
   if (a.policy & kPolicyNtStores) store_rows(std::true_type{});
   else store_rows(std::false_type{});
+}
+
+template <int OP, int C>
+__global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a) {
+  row_body<OP, C, false>(a, blockDim.x);
+}
+
+// The per-phase reload variant (ROWRED_POLICY_RELOAD): same arithmetic, the
+// row read again in every phase after the first.
+template <int OP, int C>
+__global__ void __launch_bounds__(reload_max_threads_for(OP, C)) reload_kernel(RowArgs a) {
+  row_body<OP, C, true>(a, blockDim.x);
 }
 
 // Plain streaming copy: 4 slots of 16 bytes per lane, loads before stores.
@@ -573,6 +663,25 @@ static_assert(kOpLayerNormAffine == 5 && kOpRowSum == 3 && kOpRowMinMax == 4, "k
 
 static_assert(kNumChunkSizes == 11, "kernel table rows must match kChunkSet");
 
+template <int OP, int C>
+constexpr KernelFn reload_or_null() {
+  if constexpr (reload_kernel_exists(OP, C)) return reload_kernel<OP, C>;
+  else return nullptr;
+}
+
+#define ROWRED_RELOAD_ROW(OP)                                                                         \
+  {reload_or_null<OP, 1>(), reload_or_null<OP, 2>(),  reload_or_null<OP, 3>(),  reload_or_null<OP, 4>(), \
+   reload_or_null<OP, 5>(), reload_or_null<OP, 6>(),  reload_or_null<OP, 7>(),  reload_or_null<OP, 8>(), \
+   reload_or_null<OP, 10>(), reload_or_null<OP, 12>(), reload_or_null<OP, 16>()}
+
+// [matrix operator][chunk index in kChunkSet]
+const KernelFn kReloadKernels[3][kNumChunkSizes] = {
+    ROWRED_RELOAD_ROW(kOpLayerNorm),
+    ROWRED_RELOAD_ROW(kOpRms),
+    ROWRED_RELOAD_ROW(kOpSoftmax),
+};
+#undef ROWRED_RELOAD_ROW
+
 int chunk_index(int chunks) {
   for (int i = 0; i < kNumChunkSizes; ++i)
     if (kChunkSet[i] == chunks) return i;
@@ -583,8 +692,11 @@ int chunk_index(int chunks) {
 
 int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args, hipStream_t stream) {
   const int ci = chunk_index(chunks);
-  if (op < 0 || op >= kNumKernelOps || ci < 0 || !kKernels[op][ci]) return (int)hipErrorInvalidValue;
-  KernelFn fn = kKernels[op][ci];
+  if (op < 0 || op >= kNumKernelOps || ci < 0) return (int)hipErrorInvalidValue;
+  const bool reload = (args.policy & kPolicyReload) != 0;
+  if (reload && op > 2) return (int)hipErrorInvalidValue;
+  KernelFn fn = reload ? kReloadKernels[op][ci] : kKernels[op][ci];
+  if (!fn) return (int)hipErrorInvalidValue;
   RowArgs a = args;
   void *params[] = {&a};
   const size_t lds = (a.policy & kPolicyStageStores) ? stage_lds_bytes(chunks, threads) : 0;

@@ -90,10 +90,11 @@ def test_plan_for_workload_shapes():
     # the shapes of the five workloads, aligned buffers
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
     st = R.ROWRED_POLICY_STAGE_STORES
-    cases = {(131072, 127): (16, 3, nl | ns | st), (131072, 257): (32, 3, nl | ns | st),
+    # short ragged rows (staged, <= 256 granules) keep cached loads
+    cases = {(131072, 127): (16, 3, ns | st), (131072, 257): (32, 3, ns | st),
              (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
-             (17, 257): (32, 3, nl | ns | st)}
+             (17, 257): (32, 3, ns | st)}
     for (rows, width), (L, C, pol) in cases.items():
         p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
@@ -104,8 +105,9 @@ def test_plan_memory_policy():
     st = R.ROWRED_POLICY_STAGE_STORES
     # small, every row on a 16-byte boundary: streaming, no remap, no staging
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=4096).policy == nl | ns
-    # rows share boundary lines: outputs staged in LDS, streaming stores
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == nl | ns | st
+    # rows share boundary lines: outputs staged in LDS, streaming stores;
+    # short rows keep cached loads (each boundary granule is read twice)
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == ns | st
     assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns | st
     # shared lines but y at another phase (no staging), > 2 slots per lane: cached stores
     assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=64, width=127).policy == nl
@@ -205,6 +207,26 @@ def test_run_plan_rejects_bad_plans(kw):
     c = bad_plan(**kw)._c()
     st = R.lib().rowred_run_plan(1, X, None, Y, 8, 4096, f(1e-6), ctypes.byref(c), None)
     assert st == R.ROWRED_ERR_INVALID_ARG, kw
+
+
+def test_reload_policy_preconditions():
+    m = R.ROWRED_POLICY_RELOAD
+    lib = R.lib()
+    # reload kernels exist for the matrix operators at <= 8 chunks
+    c10 = bad_plan(lanes_per_row=64, chunks=10, threads=256, policy=m)._c()
+    assert lib.rowred_run_plan(1, X, None, Y, 8, 2500, f(1e-6), ctypes.byref(c10), None) == R.ROWRED_ERR_INVALID_ARG
+    # not for the scalar-output reductions, nor affine LayerNorm
+    c2 = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=m)._c()
+    O1 = 0x7F4000000000
+    assert lib.rowred_row_reduce_run_plan(3, X, O1, None, 8, 127, ctypes.byref(c2), None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_layernorm_run_plan(X, None, O1, None, Y, 8, 127, f(1e-5), ctypes.byref(c2), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    # LayerNorm at 7-8 chunks: at most 512 threads
+    c8 = bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=m)._c()
+    assert lib.rowred_run_plan(0, X, X, Y, 8, 32768, f(1e-5), ctypes.byref(c8), None) == R.ROWRED_ERR_INVALID_ARG
+    # unknown policy bits stay rejected
+    c32 = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=32)._c()
+    assert lib.rowred_run_plan(1, X, None, Y, 8, 127, f(1e-6), ctypes.byref(c32), None) == R.ROWRED_ERR_INVALID_ARG
 
 
 def test_stage_policy_preconditions():

@@ -4,6 +4,7 @@
   in VGPRs, so no hidden memory traffic;
 * VGPR counts fit the workgroup sizes the kernels are launched with;
 * 16-byte loads and stores are used; no MFMA (nothing here is a contraction);
+* the non-temporal load policy selects its own copy of the row loads;
 * no packed-FP32 VALU instructions;
 * barriers only where cross-wave partials are folded or outputs are
   staged in LDS.
@@ -52,7 +53,9 @@ def demangle(n):
 
 def test_every_kernel_is_spill_free(asm):
     meta = kernel_meta(asm)
-    assert len(meta) == 5 * 11 + 10 + 1  # five operators, affine LayerNorm (no 16-chunk kernel), copy
+    # five operators, affine LayerNorm (no 16-chunk kernel), the reload
+    # variant of the three matrix operators at 1-8 chunks, copy
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -95,19 +98,65 @@ def test_loads_are_issued_before_the_first_wait(asm):
     assert body[:first_wait].count("global_load_dwordx4") == 5
 
 
+def x4_loads(body):
+    """(non-temporal, cached) 16-byte global loads of a kernel body."""
+    lines = [ln.strip() for ln in body.splitlines() if "global_load_dwordx4" in ln]
+    nt = sum(1 for ln in lines if ln.endswith(" nt"))
+    return nt, len(lines) - nt
+
+
+def test_nt_load_policy_reaches_the_row_loads(asm):
+    # Every row load exists twice, once with the non-temporal hint and once
+    # without, selected by ROWRED_POLICY_NT_LOADS (affine LayerNorm adds its
+    # cached gamma/beta loads).
+    for name in kernel_meta(asm):
+        dn = demangle(name)
+        kind = "rows_kernel<" if "rows_kernel<" in dn else "reload_kernel<" if "reload_kernel<" in dn else None
+        if not kind:
+            continue
+        op = int(dn.split(kind)[1].split(",")[0])
+        chunks = int(dn.split(kind)[1].split(",")[1].split(">")[0])
+        nt, cached = x4_loads(kernel_body(asm, name))
+        assert nt > 0, dn
+        extra = 2 * chunks if op == 5 else 0
+        assert cached == nt + extra, (dn, nt, cached)
+
+
+def test_reload_kernels_read_the_row_once_per_phase(asm):
+    # With x 16-byte phase-aligned to y, RMSNorm reads the row twice,
+    # softmax and LayerNorm three times (LayerNorm also reads r each time,
+    # 16 bytes or 4 bytes at a time depending on its alignment).  Counted
+    # in the non-temporal copy of the loads.
+    for name in kernel_meta(asm):
+        dn = demangle(name)
+        if "reload_kernel<" not in dn:
+            continue
+        op = int(dn.split("reload_kernel<")[1].split(",")[0])
+        chunks = int(dn.split("reload_kernel<")[1].split(",")[1].split(">")[0])
+        phases = {0: 3, 1: 2, 2: 3}[op]
+        nt, _ = x4_loads(kernel_body(asm, name))
+        # x in every phase; LayerNorm adds r's 16-byte loads
+        want = phases * chunks * (2 if op == 0 else 1)
+        assert nt == want, (dn, nt, want)
+        # the resident kernel of the same shape reads each granule once
+        resident = name.replace("13reload_kernel", "11rows_kernel")  # mangled: length-prefixed names
+        assert x4_loads(kernel_body(asm, resident))[0] == chunks * (2 if op == 0 else 1), dn
+
+
 def test_barriers_only_where_partials_are_folded(asm):
     copy = [n for n in kernel_meta(asm) if "copy_kernel" in n][0]
     assert "s_barrier" not in kernel_body(asm, copy)
     for name in kernel_meta(asm):
-        if "rows_kernel" in name:
-            # RMSNorm and row sum fold once, softmax, LayerNorm and min/max
-            # twice; matrix-output kernels of at most 4 chunks add one for
-            # the staged stores.
+        dn = demangle(name)
+        kind = "rows_kernel<" if "rows_kernel<" in dn else "reload_kernel<" if "reload_kernel<" in dn else None
+        if kind:
+            # RMSNorm, row sum and paired min/max (one shared exchange) fold
+            # once, softmax and LayerNorm twice; matrix-output kernels of at
+            # most 4 chunks add one for the staged stores.  Reloading adds none.
             n = kernel_body(asm, name).count("s_barrier")
-            dn = demangle(name)
-            op = int(dn.split("rows_kernel<")[1].split(",")[0])
-            chunks = int(dn.split("rows_kernel<")[1].split(",")[1].split(">")[0])
-            folds = {0: 2, 1: 1, 2: 2, 3: 1, 4: 2, 5: 2}[op]
+            op = int(dn.split(kind)[1].split(",")[0])
+            chunks = int(dn.split(kind)[1].split(",")[1].split(">")[0])
+            folds = {0: 2, 1: 1, 2: 2, 3: 1, 4: 1, 5: 2}[op]
             staged = chunks <= 4 and op not in (3, 4)
             want = folds + (1 if staged else 0)
             assert n == want, (dn, n)
