@@ -27,7 +27,7 @@ oracle's throughput on host cores, and per-operator figures.
                                 # workloads 1..7 on cold buffers, + a 256 MiB
                                 # copy per workload for calibration
     python bench.py --all       # one JSON line per core workload (1..5)
-    python bench.py --next      # plain and affine LayerNorm, row sum / min-max (6-8)
+    python bench.py --next      # plain and affine LayerNorm, row sum / min-max, any width (6-9)
     python bench.py --reload    # resident vs per-phase reload kernels, workloads 2-5
     python bench.py --pmc --reload  # its counter pass
 """
@@ -68,9 +68,12 @@ WORKLOAD_NAMES = {
     6: "plain LayerNorm (no residual), 1024x4096 and 16384x8192, U[-1,1]",
     7: "affine LayerNorm (gamma, beta), 1024x4096 and 16384x8192, U[-1,1]",
     8: "row sum and row min/max, 16384x8192 U[-1,1] and 131072x257 N(0,1)",
+    9: "any width (_ws entry points): softmax 64x1048576, RMSNorm 1024x131072, residual LayerNorm 256x262144, "
+       "row sum 16x4194304, softmax 7x1537",
 }
 CORE = (1, 2, 3, 4, 5)
-NEXT = (6, 7, 8)
+NEXT = (6, 7, 8, 9)
+WS_WORKLOADS = (9,)  # run through the _ws entry points (caller workspace)
 WORKLOADS = {**synthetic.CONFIGS, **synthetic.NEXT_CONFIGS}
 
 
@@ -97,7 +100,8 @@ def algo_bytes(case):
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in ("row_wise_reduction_amd/csrc/rowred_kernels.hip", "row_wise_reduction_amd/csrc/rowred_api.cpp",
-              "row_wise_reduction_amd/csrc/rowred_internal.h"):
+              "row_wise_reduction_amd/csrc/rowred_internal.h", "row_wise_reduction_amd/csrc/rowred_device.h",
+              "row_wise_reduction_amd/csrc/rowred_split.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -131,12 +135,20 @@ class CaseBuffers:
         else:
             self.y = [torch.empty_like(xd) for _ in range(sets)]
         self.sets = sets
+        self.ws = None
+        if case.cfg in WS_WORKLOADS:
+            import row_wise_reduction_amd as R
+            # calls are stream-ordered, so one workspace serves every set
+            op = "layernorm_residual" if case.op.startswith("layernorm") else case.op
+            self.ws = R.new_workspace(op, case.rows, case.width)
 
     def call(self, i):
         import row_wise_reduction_amd as R
         k = i % self.sets
         op = self.case.op
-        if op in ("layernorm", "layernorm_affine"):
+        if self.ws is not None:
+            self.call_ws(k)
+        elif op in ("layernorm", "layernorm_affine"):
             R.rowred_layernorm(self.x[k], None, self.g, self.b, self.y[k], eps=self.case.eps)
         elif op == "row_sum":
             R.rowred_row_sum(self.x[k], self.y[k])
@@ -144,6 +156,30 @@ class CaseBuffers:
             R.rowred_row_minmax(self.x[k], self.y[k], self.y2[k])
         else:
             R.run_op(op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
+
+
+    def call_ws(self, k):
+        import row_wise_reduction_amd as R
+        op, ws = self.case.op, self.ws
+        if op.startswith("layernorm"):
+            R.rowred_layernorm_ws(self.x[k], self.r[k], self.g, self.b, self.y[k], ws, eps=self.case.eps)
+        elif op == "rmsnorm":
+            R.rowred_rmsnorm_ws(self.x[k], self.y[k], ws, eps=self.case.eps)
+        elif op == "softmax":
+            R.rowred_softmax_ws(self.x[k], self.y[k], ws)
+        elif op == "row_sum":
+            R.rowred_row_sum_ws(self.x[k], self.y[k], ws)
+        else:
+            R.rowred_row_minmax_ws(self.x[k], self.y[k], self.y2[k], ws)
+
+
+def dispatches_per_call(case):
+    """Kernel dispatches one call of the case makes: the split path (the _ws
+    entry points beyond the register-resident window) runs statistics, merge
+    and, for matrix outputs, apply kernels."""
+    if case.cfg not in WS_WORKLOADS or (case.width + 3) // 4 <= 8192:  # aligned buffers: window = ceil(width/4)
+        return 1
+    return 2 if case.op in ("row_sum", "row_minmax") else 3
 
 
 def rotation_sets(case):
@@ -538,7 +574,9 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
     `bench.py --pmc --all`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     scaled by what each counter reads for the 256 MiB copy that ends each
     workload's pass."""
-    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]]
+    # one entry per reduction dispatch: a split call is 2 or 3 dispatches
+    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]
+                for _ in range(dispatches_per_call(c))]
     per_cfg = {}
     for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         i = 0
@@ -547,7 +585,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
             if row["Counter_Name"] != ctr:
                 continue
             name = row["Kernel_Name"]
-            if "rows_kernel" in name:
+            if "rows_kernel" in name or "seg_" in name:
                 cfg, case = expected[i]
                 pending.append((cfg, case, float(row["Counter_Value"]), name))
                 i += 1
@@ -555,9 +593,11 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
                 copy_kib = float(row["Counter_Value"])
                 for cfg, case, kib, kname in pending:
                     d = per_cfg.setdefault(cfg, {}).setdefault(f"{case.op} {case.rows}x{case.width}", {})
-                    d[ctr] = kib
+                    d[ctr] = d.get(ctr, 0.0) + kib
                     d[ctr + "_copy"] = copy_kib
-                    d["kernel"] = kname
+                    short = kname.replace("void rowred::(anonymous namespace)::", "").split("(")[0]
+                    if short not in d.setdefault("kernels", []):
+                        d["kernels"].append(short)
                 pending = []
         if i != len(expected):
             raise SystemExit(f"{path}: found {i} reduction dispatches, expected {len(expected)}")
@@ -568,7 +608,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
         h = "unknown"
     written = []
     for cfg, cases in per_cfg.items():
-        lines = [f"# HBM traffic per dispatch, workload {cfg}: {WORKLOAD_NAMES[cfg]}",
+        lines = [f"# HBM traffic per call (all its dispatches), workload {cfg}: {WORKLOAD_NAMES[cfg]}",
                  "# Two counter passes over the same program, one dispatch per kernel on cold buffers:",
                  "#   " + PMC_CMD.format(ctr="FETCH_SIZE"),
                  "#   " + PMC_CMD.format(ctr="WRITE_SIZE"),
@@ -583,7 +623,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
             rd = d["FETCH_SIZE"] * 1024 * rs
             wr = d["WRITE_SIZE"] * 1024 * ws
             alg_r, alg_w = algo_split(case)
-            lines += [f"kernel[{key}]: {d['kernel']}",
+            lines += [f"kernel[{key}]: {' + '.join(d['kernels'])}",
                       f"fetch_kib[{key}]: {d['FETCH_SIZE']:.2f} (copy {d['FETCH_SIZE_copy']:.2f}, "
                       f"read_scale {rs:.4f})",
                       f"write_kib[{key}]: {d['WRITE_SIZE']:.2f} (copy {d['WRITE_SIZE_copy']:.2f}, "
@@ -684,7 +724,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
-    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6, 7, 8)")
+    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-9)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
     ap.add_argument("--reload", action="store_true",

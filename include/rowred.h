@@ -43,7 +43,7 @@
  * held in registers across the phases, so width is capped: the 16-byte slot
  * window of a row (ceil((width + misalignment) / 4)) must not exceed 8192,
  * i.e. width <= 32768 for 16-byte-aligned rows; wider rows give
- * ROWRED_ERR_UNSUPPORTED.
+ * ROWRED_ERR_UNSUPPORTED (the _ws entry points at the end take any width).
  *
  * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
  * accepted; a LayerNorm row with zero variance then gives NaN (0/0), as
@@ -56,6 +56,7 @@
 #ifndef ROWRED_H
 #define ROWRED_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -191,7 +192,7 @@ enum rowred_policy {
                                      assembled in LDS and stored as whole 16-byte granules by
                                      consecutive threads; needs y at x's 16-byte phase,
                                      threads <= 512 and chunks <= 4 */
-  ROWRED_POLICY_RELOAD = 16       /* diagnostic: every phase after the first reads x (and r)
+  ROWRED_POLICY_RELOAD = 16,      /* diagnostic: every phase after the first reads x (and r)
                                      again instead of keeping the row in registers, and
                                      recomputes what it derives from them (the per-phase
                                      reload of the reference design in "Immutable input reuse
@@ -201,6 +202,10 @@ enum rowred_policy {
                                      gamma/beta, RMSNorm, softmax), chunks <= 8, LayerNorm at
                                      7-8 chunks with threads <= 512; never chosen by the
                                      entry points */
+  ROWRED_POLICY_REVERSE = 32      /* split plans only (rowred_split_plan): the apply kernel
+                                     walks the (row, segment) pairs in reverse order, so
+                                     that it first reads again what the statistics kernel
+                                     read last; measured no faster, never chosen */
 };
 
 /*
@@ -251,6 +256,93 @@ const char *rowred_status_string(int status);
  * 16-byte aligned, n a multiple of 4, else ROWRED_ERR_INVALID_ARG.
  */
 int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Any width, and rows split across workgroups: the _ws entry points.
+ *
+ * The entry points above keep a whole row in one workgroup's registers, so
+ * rows wider than 8192 16-byte granules are ROWRED_ERR_UNSUPPORTED, and a
+ * matrix of few rows keeps few compute units busy.  "Immutable input reuse
+ * in Metal reductions" leaves rows beyond the private stripe open (section
+ * "Next decisions and open questions": mixed cache/reload choices) and times
+ * few-row shapes such as 7x1537 (section "Fixed-width GPU and dispatch
+ * results").  The _ws entry points compute the same operators, same
+ * arguments, for any width:
+ *   - when the row fits the register-resident kernels they run those (the
+ *     workspace is then not touched);
+ *   - otherwise each row's window of 16-byte granules is cut into segments
+ *     of T*C granules, one workgroup per (row, segment), in three kernels:
+ *     per-segment statistics into the workspace, a fixed-order merge per row,
+ *     and (LayerNorm, RMSNorm, softmax) an apply kernel that reads its
+ *     segment again and writes it.  x (and r) are read twice, the second time
+ *     from cache where it fits (the first pass uses cached loads).
+ * Merges: LayerNorm combines per-segment (sum, sum of squares about the
+ * segment mean) with the pairwise update of Chan, Golub and LeVeque, which is
+ * exactly the biased two-pass variance about the row mean of "Residual
+ * LayerNorm shared-Tile materialization search", section "Structural
+ * finding"; softmax combines (max m_k, sum of exp(x - m_k)) as
+ * m = max m_k, s = sum s_k exp(m_k - m); RMSNorm and row sum add, min/max
+ * take min and max.  Results agree with the entry points above within the
+ * same tolerance (different summation order); for a fixed plan they are
+ * bitwise reproducible.  IEEE special cases behave as above (an all -inf
+ * softmax row is NaN, a NaN poisons its row, min/max skip NaN).
+ *
+ * workspace: device memory of at least rowred_workspace_size() bytes,
+ * 16-byte aligned, owned by the caller, not overlapping any operand; its
+ * contents need no initialisation and are garbage afterwards.  Calls that
+ * run concurrently need separate workspaces.  A NULL, misaligned or short
+ * workspace -> ROWRED_ERR_INVALID_ARG when the split kernels are needed;
+ * overlap -> ROWRED_ERR_ALIAS.  Everything else as for the entry points
+ * above (sizes, alignment, aliasing, eps, stream, no allocation).
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes enough for the _ws entry point of `op` (enum rowred_op;
+ * ROWRED_OP_LAYERNORM_RESIDUAL stands for rowred_layernorm_ws) at any
+ * alignment of x: rows * (S + 1) * 16 with S segments per row.  0 when
+ * rows or width is 0.  Host only. */
+int rowred_workspace_size(int op, int64_t rows, int64_t width, size_t *bytes);
+
+int rowred_layernorm_ws(const float *x, const float *r, const float *gamma, const float *beta, float *y,
+                        int64_t rows, int64_t width, float eps, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+int rowred_rmsnorm_ws(const float *x, float *y, int64_t rows, int64_t width, float eps, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+int rowred_softmax_ws(const float *x, float *y, int64_t rows, int64_t width, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+int rowred_row_sum_ws(const float *x, float *out, int64_t rows, int64_t width, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+int rowred_row_minmax_ws(const float *x, float *out_min, float *out_max, int64_t rows, int64_t width,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Geometry of the split kernels: workgroups of `threads` lanes, each lane
+ * holding `chunks` 16-byte slots of its segment, so a segment is
+ * threads * chunks granules. */
+typedef struct rowred_split_plan {
+  int32_t threads;         /* 64, 128, 256, 512 or 1024 */
+  int32_t chunks;          /* 1, 2 or 4 */
+  int32_t policy;          /* ROWRED_POLICY_NT_LOADS / NT_STORES (apply kernel), ROWRED_POLICY_REVERSE */
+  int32_t window;          /* derived: largest granule window of a row */
+  int64_t block_rows;      /* rows per pass of the kernels (0: all rows in one pass, which the
+                              _ws entry points use); passes run one after another on the stream,
+                              so a block's second read can find its first in the last-level cache */
+  int64_t segments;        /* derived: S = ceil(window / (threads * chunks)) */
+  int64_t grid;            /* derived: block_rows * S workgroups per kernel launch */
+  int64_t workspace_bytes; /* derived: (block_rows * S + block_rows) * 16 */
+} rowred_split_plan;
+
+/* Host only.  threads == 0 in *plan: fill in the plan the _ws entry points
+ * use when they split; otherwise check the given threads / chunks / policy
+ * (ROWRED_ERR_INVALID_ARG if not allowed) and fill the derived fields. */
+int rowred_split_plan_query(int op, const float *x, int64_t rows, int64_t width, rowred_split_plan *plan);
+
+/* Run the split kernels with an explicit plan, at any width (for sweeps and
+ * tests).  op: enum rowred_op; r, gamma, beta only with
+ * ROWRED_OP_LAYERNORM_RESIDUAL (each optional); y2 only with
+ * ROWRED_OP_ROW_MINMAX (y = out_min, y2 = out_max); y = out for
+ * ROWRED_OP_ROW_SUM. */
+int rowred_split_run_plan(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y,
+                          float *y2, int64_t rows, int64_t width, float eps, const rowred_split_plan *plan,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

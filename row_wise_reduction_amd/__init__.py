@@ -33,6 +33,7 @@ ROWRED_POLICY_NT_STORES = 2
 ROWRED_POLICY_XCD_REMAP = 4
 ROWRED_POLICY_STAGE_STORES = 8
 ROWRED_POLICY_RELOAD = 16
+ROWRED_POLICY_REVERSE = 32
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1
@@ -73,6 +74,28 @@ class Plan:
                      self.vector_io, self.window, self.policy, self.reserved)
 
 
+class _SplitPlan(ctypes.Structure):
+    _fields_ = [("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("block_rows", ctypes.c_int64), ("segments", ctypes.c_int64),
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+@dataclass
+class SplitPlan:
+    threads: int = 0
+    chunks: int = 0
+    policy: int = 0
+    window: int = 0
+    block_rows: int = 0
+    segments: int = 0
+    grid: int = 0
+    workspace_bytes: int = 0
+
+    def _c(self) -> _SplitPlan:
+        return _SplitPlan(self.threads, self.chunks, self.policy, self.window, self.block_rows, self.segments,
+                          self.grid, self.workspace_bytes)
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -98,6 +121,15 @@ def lib():
             "rowred_row_sum": [_P, _P, _I64, _I64, _P],
             "rowred_row_minmax": [_P, _P, _P, _I64, _I64, _P],
             "rowred_row_reduce_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan), _P],
+            "rowred_workspace_size": [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
+            "rowred_layernorm_ws": [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, ctypes.c_size_t, _P],
+            "rowred_rmsnorm_ws": [_P, _P, _I64, _I64, ctypes.c_float, _P, ctypes.c_size_t, _P],
+            "rowred_softmax_ws": [_P, _P, _I64, _I64, _P, ctypes.c_size_t, _P],
+            "rowred_row_sum_ws": [_P, _P, _I64, _I64, _P, ctypes.c_size_t, _P],
+            "rowred_row_minmax_ws": [_P, _P, _P, _I64, _I64, _P, ctypes.c_size_t, _P],
+            "rowred_split_plan_query": [ctypes.c_int, _P, _I64, _I64, ctypes.POINTER(_SplitPlan)],
+            "rowred_split_run_plan": [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float,
+                                      ctypes.POINTER(_SplitPlan), _P, ctypes.c_size_t, _P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(L, name)
@@ -300,6 +332,109 @@ def rowred_run_plan(op, x, r, y, plan: Plan, rows=None, width=None, eps=0.0, str
     st = lib().rowred_run_plan(_op_id(op), mx[0], mr[0], my[0], rows, width, float(eps), ctypes.byref(c),
                                _stream(stream, x, r, y))
     _check(st, "rowred_run_plan")
+
+
+# ----------------------------------------------------------------------------
+# any width / split rows (caller-provided workspace)
+# ----------------------------------------------------------------------------
+
+def _workspace(ws):
+    """(address, bytes) of a workspace tensor, or (address, bytes) passed as
+    a pair of ints."""
+    if ws is None:
+        return None, 0
+    if _is_tensor(ws):
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise TypeError("workspace must be a contiguous CUDA (HIP) tensor")
+        return ws.data_ptr(), ws.numel() * ws.element_size()
+    addr, nbytes = ws
+    return int(addr), int(nbytes)
+
+
+def rowred_workspace_size(op, rows, width) -> int:
+    """Workspace bytes the _ws entry point of `op` needs at this shape."""
+    n = ctypes.c_size_t()
+    _check(lib().rowred_workspace_size(_op_id(op), int(rows), int(width), ctypes.byref(n)), "rowred_workspace_size")
+    return n.value
+
+
+def new_workspace(op, rows, width):
+    """A torch uint8 CUDA tensor of rowred_workspace_size bytes (at least 16).
+    torch allocations are 256-byte aligned."""
+    import torch
+    return torch.empty(max(16, rowred_workspace_size(op, rows, width)), dtype=torch.uint8, device="cuda")
+
+
+def rowred_layernorm_ws(x, r, gamma, beta, y, workspace, rows=None, width=None, eps=1e-5, stream=None):
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    wa, wn = _workspace(workspace)
+    st = lib().rowred_layernorm_ws(mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width), my[0],
+                                   rows, width, float(eps), wa, wn, _stream(stream, x, r, gamma, beta, y))
+    _check(st, "rowred_layernorm_ws")
+
+
+def rowred_rmsnorm_ws(x, y, workspace, rows=None, width=None, eps=1e-6, stream=None):
+    mx, my = _matrix(x, "x", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("y", my)], rows, width)
+    wa, wn = _workspace(workspace)
+    _check(lib().rowred_rmsnorm_ws(mx[0], my[0], rows, width, float(eps), wa, wn, _stream(stream, x, y)),
+           "rowred_rmsnorm_ws")
+
+
+def rowred_softmax_ws(x, y, workspace, rows=None, width=None, stream=None):
+    mx, my = _matrix(x, "x", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("y", my)], rows, width)
+    wa, wn = _workspace(workspace)
+    _check(lib().rowred_softmax_ws(mx[0], my[0], rows, width, wa, wn, _stream(stream, x, y)), "rowred_softmax_ws")
+
+
+def rowred_row_sum_ws(x, out, workspace, rows=None, width=None, stream=None):
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    wa, wn = _workspace(workspace)
+    _check(lib().rowred_row_sum_ws(mx[0], _row_vector(out, "out", rows), rows, width, wa, wn, _stream(stream, x, out)),
+           "rowred_row_sum_ws")
+
+
+def rowred_row_minmax_ws(x, out_min, out_max, workspace, rows=None, width=None, stream=None):
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    wa, wn = _workspace(workspace)
+    _check(lib().rowred_row_minmax_ws(mx[0], _row_vector(out_min, "out_min", rows),
+                                      _row_vector(out_max, "out_max", rows), rows, width, wa, wn,
+                                      _stream(stream, x, out_min, out_max)), "rowred_row_minmax_ws")
+
+
+def rowred_split_plan_query(op, x, rows=None, width=None, plan: SplitPlan = None) -> SplitPlan:
+    """The split plan the _ws entry points use (plan None), or `plan` checked
+    and completed."""
+    mx = _matrix(x, "x", rows, width)
+    rows, width = _shape([("x", mx)], rows, width)
+    c = (plan or SplitPlan())._c()
+    _check(lib().rowred_split_plan_query(_op_id(op), mx[0], rows, width, ctypes.byref(c)), "rowred_split_plan_query")
+    return SplitPlan(c.threads, c.chunks, c.policy, c.window, c.block_rows, c.segments, c.grid, c.workspace_bytes)
+
+
+def rowred_split_run_plan(op, x, r, gamma, beta, y, y2, plan: SplitPlan, workspace, rows=None, width=None, eps=0.0,
+                          stream=None):
+    """The split kernels with an explicit plan.  For row_sum / row_minmax, y
+    (and y2) are row vectors."""
+    op = _op_id(op)
+    mx, mr = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width)
+    if op in (ROWRED_OP_ROW_SUM, ROWRED_OP_ROW_MINMAX):
+        rows, width = _shape([("x", mx)], rows, width)
+        ay, ay2 = _row_vector(y, "y", rows), _row_vector(y2, "y2", rows)
+    else:
+        my = _matrix(y, "y", rows, width)
+        rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+        ay, ay2 = my[0], _row_vector(y2, "y2", rows)
+    wa, wn = _workspace(workspace)
+    c = plan._c()
+    st = lib().rowred_split_run_plan(op, mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width),
+                                     ay, ay2, rows, width, float(eps), ctypes.byref(c), wa, wn,
+                                     _stream(stream, x, r, gamma, beta, y, y2, workspace))
+    _check(st, "rowred_split_run_plan")
 
 
 def rowred_copy(x, y, n=None, stream=None):

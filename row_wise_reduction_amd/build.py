@@ -21,8 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librowred.so")
 ASM = os.path.join(PKG, "_build", "rowred_kernels-gfx950.s")
 
-SOURCES = [os.path.join(CSRC, "rowred_kernels.hip"), os.path.join(CSRC, "rowred_api.cpp")]
-HEADERS = [os.path.join(CSRC, "rowred_internal.h"), os.path.join(INCLUDE, "rowred.h")]
+DEVICE_SOURCES = [os.path.join(CSRC, "rowred_kernels.hip"), os.path.join(CSRC, "rowred_split.hip")]
+SOURCES = DEVICE_SOURCES + [os.path.join(CSRC, "rowred_api.cpp")]
+HEADERS = [os.path.join(CSRC, "rowred_internal.h"), os.path.join(CSRC, "rowred_device.h"),
+           os.path.join(INCLUDE, "rowred.h")]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,10 +54,17 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
 
 
 def device_asm(path: str = ASM) -> str:
-    """Write the gfx950 assembly of the kernels (for resource/ISA checks)."""
+    """Write the gfx950 assembly of every kernel source, concatenated into
+    one file (for resource/ISA checks)."""
     os.makedirs(os.path.dirname(path), exist_ok=True)
-    cmd = [HIPCC, *COMMON, "--cuda-device-only", "-S", "-o", path, SOURCES[0]]
-    _run(cmd)
+    parts = []
+    for i, src in enumerate(DEVICE_SOURCES):
+        part = f"{path}.{i}"
+        _run([HIPCC, *COMMON, "--cuda-device-only", "-S", "-o", part, src])
+        parts.append(open(part).read())
+        os.remove(part)
+    with open(path, "w") as f:
+        f.write("\n".join(parts))
     return path
 
 

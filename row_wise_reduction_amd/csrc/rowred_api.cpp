@@ -70,7 +70,7 @@ int max_window(const float *x, int64_t rows, int64_t width) {
 
 // Checks shared by every entry point.  `need_eps` marks ops with an eps.
 int check_call(int op, const float *x, const float *r, const float *y, int64_t rows, int64_t width, bool need_r,
-               bool need_eps, float eps, Call *out) {
+               bool need_eps, float eps, Call *out, bool cap = true) {
   if (op < 0 || op >= kNumMatrixOps) return ROWRED_ERR_INVALID_ARG;
   if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   if (need_eps && (!isfinite(eps) || eps < 0.0f)) return ROWRED_ERR_INVALID_ARG;
@@ -92,7 +92,7 @@ int check_call(int op, const float *x, const float *r, const float *y, int64_t r
   out->y_vec = ((uintptr_t)y & 15) == ax;
   out->r_vec = r && ((uintptr_t)r & 15) == ax;
   out->window = max_window(x, rows, width);
-  if (out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
+  if (cap && out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
   return ROWRED_OK;
 }
 
@@ -237,7 +237,8 @@ int entry(int op, const float *x, const float *r, float *y, int64_t rows, int64_
 }
 
 // Row sum / row min-max: outputs are `rows` floats each.
-int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t rows, int64_t width, Call *out) {
+int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t rows, int64_t width, Call *out,
+                      bool cap = true) {
   if (op != ROWRED_OP_ROW_SUM && op != ROWRED_OP_ROW_MINMAX) return ROWRED_ERR_INVALID_ARG;
   if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   out->op = op;
@@ -261,7 +262,7 @@ int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t 
   if (hits(out0, (const void *)px, nx) || (out->y2 && (hits(out1, (const void *)px, nx) || hits(out1, out0, no))))
     return ROWRED_ERR_ALIAS;
   out->window = max_window(x, rows, width);
-  if (out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
+  if (cap && out->window > kMaxWindow) return ROWRED_ERR_UNSUPPORTED;
   return ROWRED_OK;
 }
 
@@ -317,6 +318,159 @@ int layernorm_entry(const float *x, const float *r, const float *gamma, const fl
   st = finish_plan(c, &p);
   if (st != ROWRED_OK) return st;
   return run(c, p, eps, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Split rows (the _ws entry points).
+// ---------------------------------------------------------------------------
+
+// Window at the worst 16-byte phase: the chooser and the workspace size do
+// not depend on where x starts.
+int64_t worst_window(int64_t width) { return (width + 6) / 4; }
+
+// Split geometry, from sweeps of every (threads, chunks) and policy at
+// 64x1048576, 1024x131072, 256x262144, 4096x65536 (matrix outputs) and
+// 16x4194304 (row sum), each call on buffers rotated through >= 2 GiB:
+//   * 256 threads x 2 slots per segment is best or within 3% of it for the
+//     normalisations, 512 x 2 for row sum / min-max (10% ahead of 256 x 2);
+//   * the apply kernel wants streaming loads and stores (cached stores are
+//     10-20% slower); walking the pairs backwards or in blocks of rows (so
+//     that the second read finds the first in the last-level cache) did not
+//     pay: each extra pass of the three kernels costs ~3 us of launch and
+//     drain, and blocks of 64-256 MiB gained at most 3-8%.
+// Narrow rows take smaller segments, down to 64 granules, until every row
+// has a few; the first geometry that gives the chip rows * S >=
+// kSplitTargetGroups workgroups is taken (segments wider than the row are
+// skipped), else the smallest.
+constexpr int64_t kSplitTargetGroups = 1024;
+constexpr int kSplitGeometries[][2] = {{512, 2}, {256, 2}, {256, 1}, {128, 1}, {64, 1}};
+constexpr int kNumSplitGeometries = sizeof(kSplitGeometries) / sizeof(kSplitGeometries[0]);
+
+void choose_split(int op, int64_t rows, int64_t width, rowred_split_plan *p) {
+  const int64_t w = worst_window(width);
+  const bool scalar_out = op == ROWRED_OP_ROW_SUM || op == ROWRED_OP_ROW_MINMAX;
+  int pick = kNumSplitGeometries - 1;
+  for (int i = scalar_out ? 0 : 1; i < kNumSplitGeometries; ++i) {
+    const int64_t G = (int64_t)kSplitGeometries[i][0] * kSplitGeometries[i][1];
+    if (G > w) continue;
+    if (rows * ((w + G - 1) / G) >= kSplitTargetGroups) {
+      pick = i;
+      break;
+    }
+  }
+  *p = rowred_split_plan{};
+  p->threads = kSplitGeometries[pick][0];
+  p->chunks = kSplitGeometries[pick][1];
+  p->policy = kPolicyNtLoads | kPolicyNtStores;
+}
+
+// Validate an explicit or chosen split plan and fill its derived fields.
+int finish_split(const Call &c, rowred_split_plan *p) {
+  const int64_t T = p->threads;
+  if (!is_pow2(T) || T < 64 || T > 1024) return ROWRED_ERR_INVALID_ARG;
+  if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~kSplitPolicyAll) return ROWRED_ERR_INVALID_ARG;
+  if (p->block_rows < 0) return ROWRED_ERR_INVALID_ARG;
+  const int64_t G = T * p->chunks;
+  const int64_t br = p->block_rows == 0 || p->block_rows > c.rows ? c.rows : p->block_rows;
+  p->block_rows = br;
+  p->window = c.window;
+  p->segments = (c.window + G - 1) / G;
+  if (p->segments > INT32_MAX || br > INT64_MAX / p->segments) return ROWRED_ERR_UNSUPPORTED;
+  p->grid = br * p->segments;
+  if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  p->workspace_bytes = (p->grid + br) * 16;
+  return ROWRED_OK;
+}
+
+// Kernel operator of a split call: LayerNorm (any of r, gamma, beta) 0,
+// RMSNorm 1, softmax 2, row sum 3, row min/max 4.
+int split_op(const Call &c) { return c.op; }
+
+int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ((uintptr_t)ws & 15)) return ROWRED_ERR_INVALID_ARG;
+  if ((int64_t)ws_bytes < p.workspace_bytes) return ROWRED_ERR_INVALID_ARG;
+  // the workspace overlaps none of the operands
+  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)p.workspace_bytes;
+  auto hit = [&](const void *b, int64_t nb) {
+    return b && nb > 0 && (uintptr_t)b < w1 && w0 < (uintptr_t)b + (uintptr_t)nb;
+  };
+  const int64_t mat = c.rows * c.width * 4;
+  const bool scalar = c.op == ROWRED_OP_ROW_SUM || c.op == ROWRED_OP_ROW_MINMAX;
+  const int64_t out_bytes = scalar ? c.rows * 4 : mat;
+  if (hit(c.x, mat) || hit(c.r, mat) || hit(c.y, out_bytes) || hit(c.y2, c.rows * 4) || hit(c.gamma, c.width * 4) ||
+      hit(c.beta, c.width * 4))
+    return ROWRED_ERR_ALIAS;
+  SegArgs a;
+  a.gamma = c.gamma;
+  a.beta = c.beta;
+  a.ws = static_cast<double *>(ws);
+  a.width = (int32_t)c.width;
+  a.segments = (int32_t)p.segments;
+  a.lanes_log2 = ilog2(p.threads);
+  a.seg_granules = p.threads * p.chunks;
+  a.eps = eps;
+  a.inv_width = 1.0f / (float)c.width;
+  a.policy = p.policy;
+  a.r_vec = c.r_vec ? 1 : 0;
+  a.y_vec = c.y_vec ? 1 : 0;
+  // Row blocks run one after another; offsetting every operand by whole
+  // rows keeps r and y at x's 16-byte phase.  The workspace is reused.
+  for (int64_t r0 = 0; r0 < c.rows; r0 += p.block_rows) {
+    const int64_t n = c.rows - r0 < p.block_rows ? c.rows - r0 : p.block_rows;
+    const int64_t e0 = r0 * c.width;
+    a.x = c.x + e0;
+    a.r = c.r ? c.r + e0 : nullptr;
+    a.y = scalar ? c.y + r0 : c.y + e0;
+    a.y2 = c.y2 ? c.y2 + r0 : nullptr;
+    a.rows = n;
+    const int err = launch_split(split_op(c), p.chunks, n * p.segments, p.threads, a, stream);
+    if (err != 0) return ROWRED_ERR_HIP;
+  }
+  return ROWRED_OK;
+}
+
+// Checks of a _ws call: those of the register-resident entry points without
+// the width cap.  gamma / beta only with LayerNorm.
+int check_ws_call(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y, float *y2,
+                  int64_t rows, int64_t width, float eps, Call *c) {
+  if (op == ROWRED_OP_ROW_SUM || op == ROWRED_OP_ROW_MINMAX) {
+    if (r || gamma || beta) return ROWRED_ERR_INVALID_ARG;
+    return check_reduce_call(op, x, y, y2, rows, width, c, false);
+  }
+  if (op != ROWRED_OP_LAYERNORM_RESIDUAL && (r || gamma || beta)) return ROWRED_ERR_INVALID_ARG;
+  if (y2) return ROWRED_ERR_INVALID_ARG;
+  int st = check_call(op, x, r, y, rows, width, false, op_has_eps(op), eps, c, false);
+  if (st != ROWRED_OK || rows == 0 || width == 0) return st;
+  return op == ROWRED_OP_LAYERNORM_RESIDUAL ? attach_affine(c, gamma, beta) : ROWRED_OK;
+}
+
+// A _ws call: the register-resident kernels when the row fits them, else
+// (or with an explicit split plan) the split kernels.
+int ws_entry(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y, float *y2,
+             int64_t rows, int64_t width, float eps, const rowred_split_plan *plan, void *ws, size_t ws_bytes,
+             hipStream_t stream) {
+  Call c;
+  int st = check_ws_call(op, x, r, gamma, beta, y, y2, rows, width, eps, &c);
+  if (st != ROWRED_OK || rows == 0 || width == 0) return st;
+  if (!plan && c.window <= kMaxWindow) {
+    rowred_plan p;
+    choose_plan(c, &p);
+    if (p.chunks >= 0) {
+      st = finish_plan(c, &p);
+      if (st != ROWRED_OK) return st;
+      return run(c, p, eps, stream);
+    }
+  }
+  rowred_split_plan p;
+  if (plan) {
+    p = *plan;
+  } else {
+    choose_split(op, rows, width, &p);
+  }
+  st = finish_split(c, &p);
+  if (st != ROWRED_OK) return st;
+  return run_split(c, p, eps, ws, ws_bytes, stream);
 }
 
 }  // namespace
@@ -396,12 +550,88 @@ ROWRED_API int rowred_run_plan(int op, const float *x, const float *r, float *y,
   return run(c, p, eps, stream);
 }
 
+ROWRED_API int rowred_workspace_size(int op, int64_t rows, int64_t width, size_t *bytes) {
+  if (!bytes) return ROWRED_ERR_INVALID_ARG;
+  if (op < 0 || op > ROWRED_OP_ROW_MINMAX || rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (rows == 0 || width == 0) return ROWRED_OK;
+  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  rowred_split_plan p;
+  choose_split(op, rows, width, &p);
+  const int64_t G = (int64_t)p.threads * p.chunks;
+  const int64_t S = (worst_window(width) + G - 1) / G;
+  if (rows > INT64_MAX / 16 / (S + 1)) return ROWRED_ERR_UNSUPPORTED;
+  *bytes = (size_t)(rows * (S + 1) * 16);
+  return ROWRED_OK;
+}
+
+ROWRED_API int rowred_layernorm_ws(const float *x, const float *r, const float *gamma, const float *beta, float *y,
+                                   int64_t rows, int64_t width, float eps, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return ws_entry(ROWRED_OP_LAYERNORM_RESIDUAL, x, r, gamma, beta, y, nullptr, rows, width, eps, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_rmsnorm_ws(const float *x, float *y, int64_t rows, int64_t width, float eps, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return ws_entry(ROWRED_OP_RMSNORM, x, nullptr, nullptr, nullptr, y, nullptr, rows, width, eps, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_softmax_ws(const float *x, float *y, int64_t rows, int64_t width, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return ws_entry(ROWRED_OP_SOFTMAX, x, nullptr, nullptr, nullptr, y, nullptr, rows, width, 0.0f, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_row_sum_ws(const float *x, float *out, int64_t rows, int64_t width, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return ws_entry(ROWRED_OP_ROW_SUM, x, nullptr, nullptr, nullptr, out, nullptr, rows, width, 0.0f, nullptr,
+                  workspace, workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_row_minmax_ws(const float *x, float *out_min, float *out_max, int64_t rows, int64_t width,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ws_entry(ROWRED_OP_ROW_MINMAX, x, nullptr, nullptr, nullptr, out_min, out_max, rows, width, 0.0f, nullptr,
+                  workspace, workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_split_plan_query(int op, const float *x, int64_t rows, int64_t width,
+                                       rowred_split_plan *plan) {
+  if (!plan || op < 0 || op > ROWRED_OP_ROW_MINMAX || rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
+  if (rows == 0 || width == 0) {
+    *plan = rowred_split_plan{};
+    return ROWRED_OK;
+  }
+  if (!x || ((uintptr_t)x & 3)) return ROWRED_ERR_INVALID_ARG;
+  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  Call c;
+  c.op = op;
+  c.x = x;
+  c.r = nullptr;
+  c.y = nullptr;
+  c.rows = rows;
+  c.width = width;
+  c.r_vec = c.y_vec = false;
+  c.window = max_window(x, rows, width);
+  if (plan->threads == 0) choose_split(op, rows, width, plan);
+  return finish_split(c, plan);
+}
+
+ROWRED_API int rowred_split_run_plan(int op, const float *x, const float *r, const float *gamma, const float *beta,
+                                     float *y, float *y2, int64_t rows, int64_t width, float eps,
+                                     const rowred_split_plan *plan, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!plan) return ROWRED_ERR_INVALID_ARG;
+  return ws_entry(op, x, r, gamma, beta, y, y2, rows, width, eps, plan, workspace, workspace_bytes, stream);
+}
+
 ROWRED_API const char *rowred_status_string(int status) {
   switch (status) {
     case ROWRED_OK: return "ok";
     case ROWRED_ERR_INVALID_ARG: return "invalid argument (size, pointer, eps or plan)";
     case ROWRED_ERR_ALIAS: return "output overlaps an input";
-    case ROWRED_ERR_UNSUPPORTED: return "row too wide for a register-resident pass";
+    case ROWRED_ERR_UNSUPPORTED: return "row too wide for a register-resident pass (the _ws entry points take any width)";
     case ROWRED_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

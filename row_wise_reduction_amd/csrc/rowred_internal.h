@@ -75,4 +75,43 @@ int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &ar
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Split rows: a row's granule window is cut into segments of T*C granules,
+// one workgroup of T threads per (row, segment).  A statistics kernel writes
+// one record of two doubles per (row, segment) to the workspace; an apply
+// kernel (matrix operators) merges its row's records in a fixed order,
+// reads its segment again and writes it; a merge kernel (row sum, min/max)
+// folds each row's records into the outputs.
+// ---------------------------------------------------------------------------
+struct SegArgs {
+  const float *x;
+  const float *r;
+  const float *gamma;
+  const float *beta;
+  float *y;
+  float *y2;
+  double *ws;          // rows * segments records of two doubles, 16-byte aligned
+  int64_t rows;
+  int32_t width;
+  int32_t segments;    // S
+  int32_t lanes_log2;  // log2(T): all threads of a workgroup serve one segment
+  int32_t seg_granules;  // G = T * C granules per segment
+  float eps;
+  float inv_width;
+  int32_t policy;      // ROWRED_POLICY_NT_LOADS / NT_STORES (apply kernel), ROWRED_POLICY_REVERSE
+  int32_t r_vec;
+  int32_t y_vec;
+};
+
+// Chunk counts (16-byte slots per lane) of the split kernels.
+constexpr int kSplitChunkSet[] = {1, 2, 4};
+constexpr int kNumSplitChunks = 3;
+constexpr int kPolicyReverse = ROWRED_POLICY_REVERSE;
+constexpr int kSplitPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyReverse;
+
+// Enqueue the statistics kernel (op: LayerNorm 0, RMSNorm 1, softmax 2, row
+// sum 3, row min/max 4) and then the apply (ops 0-2) or merge (ops 3-4)
+// kernel.  grid = rows * segments.  Returns the first launch's hipError_t.
+int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream);
+
 }  // namespace rowred

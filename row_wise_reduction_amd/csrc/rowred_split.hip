@@ -1,0 +1,431 @@
+// rowred_split.hip -- split-row kernels: rows wider than one workgroup's
+// registers can hold, and shapes with too few rows to fill the chip.
+//
+// A row's window of 16-byte granules (as in the row kernels) is cut into S
+// segments of G = T*C granules.  Workgroup (row, k) owns segment k; its lane
+// li holds granules k*G + c*T + li (c < C), so consecutive lanes read
+// consecutive granules.
+//
+//   seg_stats_kernel  loads its segment (cached loads: the segment is read
+//                     again by the apply kernel), reduces it and writes one
+//                     record of two doubles to the workspace.
+//   seg_merge_kernel  one wavefront per row folds the row's S records in a
+//                     fixed order: into the outputs (row sum, row min/max)
+//                     or into one row record (LayerNorm, RMSNorm, softmax).
+//   seg_apply_kernel  reads its segment again, applies the row record and
+//                     stores.  No collective, no barrier.
+//
+// Records (segment k holding n_k of the row's elements):
+//   LayerNorm  (sum_k of x + r, M2_k = sum of squares about the segment mean)
+//              merged with the pairwise update of Chan, Golub and LeVeque:
+//              mean = sum / n, M2 = sum_k (M2_k + n_k (sum_k / n_k - mean)^2).
+//              It equals the sum of squares about the row mean, so the
+//              variance is still the biased two-pass one of "Residual
+//              LayerNorm shared-Tile materialization search" (section
+//              "Structural finding").
+//   RMSNorm    (sum of x^2, 0)
+//   softmax    (m_k = max, s_k = sum of exp(x - m_k)); m = max m_k and
+//              s = sum of s_k exp(m_k - m): the max / exp-sum / normalise
+//              phases of "Immutable input reuse in Metal reductions" (section
+//              "What the transformation actually preserves") per segment.
+//   row sum    (sum, 0) in FP64;  row min/max  (min, max), NaN skipped.
+// The row record: LayerNorm (mean, M2), RMSNorm (sum of squares, 0),
+// softmax (m, s).
+//
+// Reading a row once per kernel pass instead of keeping it in registers is
+// the mixed cache/reload choice "Immutable input reuse in Metal reductions"
+// leaves open (section "Next decisions and open questions") for rows beyond
+// the private stripe; the segments give short rows' shapes such as 7x1537
+// ("Fixed-width GPU and dispatch results") more than 7 workgroups.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rowred_device.h"
+#include "rowred_internal.h"
+
+namespace rowred {
+namespace {
+
+struct Rec {
+  double v0, v1;
+};
+
+// (row, segment) of this workgroup; the apply kernel may walk them backwards.
+__device__ __forceinline__ void segment_of(const SegArgs &a, bool reverse, int64_t &row, int &seg) {
+  uint32_t b = blockIdx.x;
+  if (reverse) b = gridDim.x - 1 - b;
+  const uint32_t q = b / (uint32_t)a.segments;
+  row = q;
+  seg = (int)(b - q * (uint32_t)a.segments);
+}
+
+// Elements of a row (first element `off` floats into its first granule)
+// that fall in granules [k*G, (k+1)*G).
+__device__ __forceinline__ int64_t segment_count(int64_t k, int64_t G, int off, int width) {
+  const int64_t lo = 4 * k * G - off, hi = 4 * (k + 1) * G - off;
+  const int64_t a = lo > 0 ? lo : 0, b = hi < width ? hi : (int64_t)width;
+  return b > a ? b - a : 0;
+}
+
+// Where one workgroup's segment lies.
+struct SegView {
+  const float *xrow, *rrow;
+  int off, kmax, g0, T, li, width;
+  __device__ __forceinline__ int granule(int c) const { return g0 + c * T + li; }
+  __device__ __forceinline__ int elem(int c, int j) const { return 4 * granule(c) + j - off; }
+  __device__ __forceinline__ bool valid(int c, int j) const { return (unsigned)elem(c, j) < (unsigned)width; }
+};
+
+__device__ __forceinline__ SegView make_view(const SegArgs &a, int64_t row, int seg, int T, int C) {
+  SegView v;
+  const int64_t base = row * (int64_t)a.width;
+  v.xrow = a.x + base;
+  v.rrow = a.r ? a.r + base : nullptr;
+  v.off = (int)(((uintptr_t)v.xrow >> 2) & 3);
+  v.kmax = ((a.width + v.off + 3) >> 2) - 1;
+  v.T = T;
+  v.g0 = seg * T * C;
+  v.li = threadIdx.x;
+  v.width = a.width;
+  return v;
+}
+
+// Loads of a segment: granules past the row's last one load the last one
+// again (unconditional loads, masked by position), as in the row kernels.
+// Empty asm statements keep the non-temporal copy of this block apart from
+// the cached one (otherwise the optimizer merges them and drops the hint).
+template <bool NT, int C>
+__device__ __forceinline__ void load_segment(const SegArgs &a, const SegView &v, bool has_r, f32x4 (&xv)[C],
+                                             f32x4 (&rv)[C]) {
+  if constexpr (NT) asm volatile("" ::: "memory");
+  const f32x4 *xw = reinterpret_cast<const f32x4 *>(v.xrow - v.off);
+#pragma unroll
+  for (int c = 0; c < C; ++c) xv[c] = load_g<NT>(xw + min(v.granule(c), v.kmax));
+  if (has_r) {
+    if (a.r_vec) {
+      const f32x4 *rw = reinterpret_cast<const f32x4 *>(v.rrow - v.off);
+#pragma unroll
+      for (int c = 0; c < C; ++c) rv[c] = load_g<NT>(rw + min(v.granule(c), v.kmax));
+    } else {
+      const int emax = v.width - 1;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rv[c][j] = load_g<NT>(v.rrow + max(0, min(v.elem(c, j), emax)));
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) rv[c] = f32x4(0.0f);
+  }
+  if constexpr (NT) asm volatile("" ::: "memory");
+}
+
+// x + r as an exact pair hi + lo (Knuth's TwoSum); 0 outside the row.
+template <int C>
+__device__ __forceinline__ void two_sum(const SegView &v, const f32x4 (&xv)[C], const f32x4 (&rv)[C],
+                                        float (&hi)[4 * C], float (&lo)[4 * C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = v.valid(c, j) ? xv[c][j] : 0.0f;
+      const float r = v.valid(c, j) ? rv[c][j] : 0.0f;
+      const float h = x + r;
+      const float bb = h - x;
+      hi[4 * c + j] = h;
+      lo[4 * c + j] = (x - (h - bb)) + (r - bb);
+    }
+}
+
+__device__ __forceinline__ Rec *records(const SegArgs &a) { return reinterpret_cast<Rec *>(a.ws); }
+// One row record per row, after the rows * S segment records.
+__device__ __forceinline__ Rec *row_records(const SegArgs &a) { return records(a) + a.rows * (int64_t)a.segments; }
+
+// ---------------------------------------------------------------------------
+// Statistics of one segment.
+// ---------------------------------------------------------------------------
+template <int OP, int C>
+__global__ void __launch_bounds__(1024) seg_stats_kernel(SegArgs a) {
+  __shared__ float partials[2][16];
+  __shared__ double partials_d[16];
+  const int T = blockDim.x;
+  const int lanes_log2 = a.lanes_log2;
+  int64_t row;
+  int seg;
+  segment_of(a, false, row, seg);
+  const SegView v = make_view(a, row, seg, T, C);
+  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  f32x4 xv[C], rv[C];
+  load_segment<false, C>(a, v, has_r, xv, rv);
+
+  double v0 = 0.0, v1 = 0.0;
+  if constexpr (OP == kOpRowSum) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += v.valid(c, j) ? (double)xv[c][j] : 0.0;
+    v0 = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials_d);
+  } else if constexpr (OP == kOpRowMinMax) {
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mn = fminf(mn, v.valid(c, j) ? xv[c][j] : __builtin_inff());
+        mx = fmaxf(mx, v.valid(c, j) ? xv[c][j] : -__builtin_inff());
+      }
+    row_allreduce_pair<MinOp, MaxOp>(mn, mx, lanes_log2, partials[0], partials[1]);
+    v0 = mn;
+    v1 = mx;
+  } else if constexpr (OP == kOpRms) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = v.valid(c, j) ? xv[c][j] : 0.0f;
+        acc[j] = fmaf(x, x, acc[j]);
+      }
+    v0 = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
+  } else if constexpr (OP == kOpSoftmax) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, v.valid(c, j) ? xv[c][j] : -__builtin_inff());
+    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    // -inf entries weigh 0 even in a segment whose max is -inf (where
+    // x - m would be NaN); NaN and +inf entries give NaN, as in one pass.
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = xv[c][j];
+        const bool zero = !v.valid(c, j) || x == -__builtin_inff();
+        acc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
+      }
+    v0 = m;
+    v1 = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[1]);
+  } else {  // LayerNorm: sum and sum of squares about the segment's own mean
+    float hi[4 * C], lo[4 * C];
+    two_sum<C>(v, xv, rv, hi, lo);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) {
+      acc[i & 3] += (double)hi[i];
+      acc_lo += lo[i];
+    }
+    const double sum =
+        row_allreduce<SumOp>(((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo, lanes_log2, partials_d);
+    const int64_t n = segment_count(seg, (int64_t)T * C, v.off, a.width);
+    const double mean = n > 0 ? sum / (double)n : 0.0;
+    const float m_hi = (float)mean;
+    const float m_lo = (float)(mean - (double)m_hi);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        const float d = v.valid(c, j) ? (hi[i] - m_hi) + (lo[i] - m_lo) : 0.0f;
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+    v0 = sum;
+    v1 = row_allreduce<SumOp>((sq[0] + sq[1]) + (sq[2] + sq[3]), lanes_log2, partials[0]);
+  }
+  if (threadIdx.x == 0) records(a)[row * a.segments + seg] = Rec{v0, v1};
+}
+
+// ---------------------------------------------------------------------------
+// Fold a row's records: one wavefront per row, lanes stride over the
+// records, then the wavefront butterfly.  Wavefronts past the last row
+// return at once (no barrier in this kernel).
+// ---------------------------------------------------------------------------
+template <int OP>
+__global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int S = a.segments;
+  const Rec *rec = records(a) + row * S;
+  if constexpr (OP == kOpRowSum) {
+    double s = 0.0;
+    for (int k = lane; k < S; k += 64) s += rec[k].v0;
+    s = group_allreduce<SumOp>(s, 6);
+    if (lane == 0) a.y[row] = (float)s;
+  } else if constexpr (OP == kOpRowMinMax) {
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int k = lane; k < S; k += 64) {
+      mn = fminf(mn, (float)rec[k].v0);
+      mx = fmaxf(mx, (float)rec[k].v1);
+    }
+    mn = group_allreduce<MinOp>(mn, 6);
+    mx = group_allreduce<MaxOp>(mx, 6);
+    if (lane == 0) {
+      a.y[row] = mn;
+      a.y2[row] = mx;
+    }
+  } else if constexpr (OP == kOpRms) {
+    double s = 0.0;
+    for (int k = lane; k < S; k += 64) s += rec[k].v0;
+    s = group_allreduce<SumOp>(s, 6);
+    if (lane == 0) row_records(a)[row] = Rec{s, 0.0};
+  } else if constexpr (OP == kOpSoftmax) {
+    float m = -__builtin_inff();
+    for (int k = lane; k < S; k += 64) m = fmaxf(m, (float)rec[k].v0);
+    m = group_allreduce<MaxOp>(m, 6);
+    // An all -inf row has m = -inf and s_k = 0 everywhere: 0 * exp(NaN)
+    // makes s NaN, and the row NaN, as in one pass.
+    float s = 0.0f;
+    for (int k = lane; k < S; k += 64)
+      s += (float)rec[k].v1 * __builtin_amdgcn_exp2f(((float)rec[k].v0 - m) * kLog2e);
+    s = group_allreduce<SumOp>(s, 6);
+    if (lane == 0) row_records(a)[row] = Rec{(double)m, (double)s};
+  } else {  // LayerNorm
+    const int off = (int)((((uintptr_t)a.x >> 2) + row * (int64_t)a.width) & 3);
+    double s = 0.0;
+    for (int k = lane; k < S; k += 64) s += rec[k].v0;
+    s = group_allreduce<SumOp>(s, 6);
+    const double mean = s / (double)a.width;
+    double m2 = 0.0;
+    for (int k = lane; k < S; k += 64) {
+      const int64_t n = segment_count(k, a.seg_granules, off, a.width);
+      if (n > 0) {
+        const double dm = rec[k].v0 / (double)n - mean;
+        m2 += rec[k].v1 + (double)n * dm * dm;
+      }
+    }
+    m2 = group_allreduce<SumOp>(m2, 6);
+    if (lane == 0) row_records(a)[row] = Rec{mean, m2};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Apply the row record to one segment and store it.
+// ---------------------------------------------------------------------------
+template <int OP, int C>
+__global__ void __launch_bounds__(1024) seg_apply_kernel(SegArgs a) {
+  const int T = blockDim.x;
+  int64_t row;
+  int seg;
+  segment_of(a, (a.policy & kPolicyReverse) != 0, row, seg);
+  const SegView v = make_view(a, row, seg, T, C);
+  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  f32x4 xv[C], rv[C];
+  if (a.policy & kPolicyNtLoads) load_segment<true, C>(a, v, has_r, xv, rv);
+  else load_segment<false, C>(a, v, has_r, xv, rv);
+  const Rec rr = row_records(a)[row];
+
+  float s[4 * C];
+  if constexpr (OP == kOpRms) {
+    const float scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v0, a.inv_width, a.eps));
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[4 * c + j] = xv[c][j] * scale;
+  } else if constexpr (OP == kOpSoftmax) {
+    const float m = (float)rr.v0;
+    const float inv = __builtin_amdgcn_rcpf((float)rr.v1);
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[4 * c + j] = __builtin_amdgcn_exp2f((xv[c][j] - m) * kLog2e) * inv;
+  } else {  // LayerNorm, optionally affine
+    const double mean = rr.v0;
+    const float m_hi = (float)mean;
+    const float m_lo = (float)(mean - (double)m_hi);
+    const float rstd = __builtin_amdgcn_rsqf(fmaf((float)rr.v1, a.inv_width, a.eps));
+    float hi[4 * C], lo[4 * C];
+    two_sum<C>(v, xv, rv, hi, lo);
+    const bool affine = a.gamma != nullptr || a.beta != nullptr;
+    const int emax = a.width - 1;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        float y = ((hi[i] - m_hi) + (lo[i] - m_lo)) * rstd;
+        if (affine) {
+          const int e = max(0, min(v.elem(c, j), emax));
+          const float g = a.gamma ? a.gamma[e] : 1.0f;
+          const float b = a.beta ? a.beta[e] : 0.0f;
+          y = fmaf(y, g, b);
+        }
+        s[i] = y;
+      }
+  }
+
+  auto store = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    float *yrow = a.y + row * (int64_t)a.width;
+    if (a.y_vec) {
+      f32x4 *yw = reinterpret_cast<f32x4 *>(yrow - v.off);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int k = v.granule(c);
+        const int e0 = 4 * k - v.off;
+        if (e0 >= 0 && e0 + 4 <= a.width) {
+          store_g<NT>(yw + k, f32x4{s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]});
+        } else if (k <= v.kmax) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((unsigned)(e0 + j) < (unsigned)a.width) store_g<NT>(yrow + e0 + j, s[4 * c + j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v.valid(c, j)) store_g<NT>(yrow + v.elem(c, j), s[4 * c + j]);
+    }
+  };
+  if (a.policy & kPolicyNtStores) store(std::true_type{});
+  else store(std::false_type{});
+}
+
+using SegFn = void (*)(SegArgs);
+
+#define ROWRED_SPLIT_ROW(K, OP) {K<OP, 1>, K<OP, 2>, K<OP, 4>}
+const SegFn kStats[5][kNumSplitChunks] = {
+    ROWRED_SPLIT_ROW(seg_stats_kernel, kOpLayerNorm), ROWRED_SPLIT_ROW(seg_stats_kernel, kOpRms),
+    ROWRED_SPLIT_ROW(seg_stats_kernel, kOpSoftmax),   ROWRED_SPLIT_ROW(seg_stats_kernel, kOpRowSum),
+    ROWRED_SPLIT_ROW(seg_stats_kernel, kOpRowMinMax),
+};
+const SegFn kApply[3][kNumSplitChunks] = {
+    ROWRED_SPLIT_ROW(seg_apply_kernel, kOpLayerNorm),
+    ROWRED_SPLIT_ROW(seg_apply_kernel, kOpRms),
+    ROWRED_SPLIT_ROW(seg_apply_kernel, kOpSoftmax),
+};
+#undef ROWRED_SPLIT_ROW
+const SegFn kMerge[5] = {seg_merge_kernel<kOpLayerNorm>, seg_merge_kernel<kOpRms>, seg_merge_kernel<kOpSoftmax>,
+                         seg_merge_kernel<kOpRowSum>, seg_merge_kernel<kOpRowMinMax>};
+static_assert(kNumSplitChunks == 3 && kSplitChunkSet[0] == 1 && kSplitChunkSet[1] == 2 && kSplitChunkSet[2] == 4,
+              "split kernel tables follow kSplitChunkSet");
+
+constexpr int kMergeThreads = 256;  // four rows (wavefronts) per workgroup
+
+}  // namespace
+
+int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {
+  const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : -1;
+  if (op < 0 || op > 4 || ci < 0) return (int)hipErrorInvalidValue;
+  SegArgs a = args;
+  void *params[] = {&a};
+  int err = (int)hipLaunchKernel(reinterpret_cast<const void *>(kStats[op][ci]), dim3((uint32_t)grid),
+                                 dim3(threads), params, 0, stream);
+  if (err) return err;
+  const int64_t merge_grid = (a.rows + kMergeThreads / 64 - 1) / (kMergeThreads / 64);
+  err = (int)hipLaunchKernel(reinterpret_cast<const void *>(kMerge[op]), dim3((uint32_t)merge_grid),
+                             dim3(kMergeThreads), params, 0, stream);
+  if (err || op > 2) return err;
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(kApply[op][ci]), dim3((uint32_t)grid), dim3(threads),
+                              params, 0, stream);
+}
+
+}  // namespace rowred

@@ -333,3 +333,89 @@ def test_row_reduce_argument_checks():
     assert lib.rowred_row_reduce_run_plan(1, X, O1, None, 8, 127, ctypes.byref(c), None) == R.ROWRED_ERR_INVALID_ARG
     p = R.rowred_plan_query("row_minmax", X, O2, O1, rows=1024, width=4096)
     assert p.lanes_per_row * p.chunks >= p.window and p.policy & R.ROWRED_POLICY_STAGE_STORES == 0
+
+
+# ---------------------------------------------------------------------------
+# any width / split rows
+# ---------------------------------------------------------------------------
+
+SPLIT_OPS = ["layernorm_residual", "rmsnorm", "softmax", "row_sum", "row_minmax"]
+
+
+@pytest.mark.parametrize("op", SPLIT_OPS)
+@pytest.mark.parametrize("rows,width", [(1, 1), (7, 1537), (3, 32769), (64, 1 << 20), (1024, 131072), (1, 100003),
+                                        (16384, 8192), (5, 255)])
+def test_workspace_size_covers_every_alignment(op, rows, width):
+    need = R.rowred_workspace_size(op, rows, width)
+    for mis in range(4):
+        p = R.rowred_split_plan_query(op, X + 4 * mis, rows, width)
+        G = p.threads * p.chunks
+        assert p.window == window(X + 4 * mis, rows, width)
+        assert p.segments == -(-p.window // G) and p.grid == rows * p.segments
+        assert p.workspace_bytes == (p.grid + rows) * 16 <= need
+        assert p.threads in (64, 128, 256, 512, 1024) and p.chunks in (1, 2, 4)
+        # the chooser never cuts a row into segments wider than the row, unless
+        # the smallest one already is
+        assert G <= max(p.window + 3, 64)
+
+
+def test_workspace_size_empty_and_errors():
+    assert R.rowred_workspace_size("softmax", 0, 100) == 0
+    assert R.rowred_workspace_size("softmax", 100, 0) == 0
+    n = ctypes.c_size_t()
+    assert R.lib().rowred_workspace_size(7, 4, 4, ctypes.byref(n)) == R.ROWRED_ERR_INVALID_ARG
+    assert R.lib().rowred_workspace_size(1, -1, 4, ctypes.byref(n)) == R.ROWRED_ERR_INVALID_ARG
+    assert R.lib().rowred_workspace_size(1, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(threads=96), dict(threads=32), dict(threads=2048), dict(chunks=3),
+                                dict(chunks=8), dict(policy=R.ROWRED_POLICY_STAGE_STORES),
+                                dict(policy=R.ROWRED_POLICY_XCD_REMAP)])
+def test_split_plan_rejects(kw):
+    base = dict(threads=256, chunks=2, policy=0)
+    base.update(kw)
+    with pytest.raises(R.RowRedError) as e:
+        R.rowred_split_plan_query("softmax", X, 8, 100000, plan=R.SplitPlan(**base))
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+
+
+def test_ws_entry_argument_checks():
+    lib = R.lib()
+    W = 0x7F6000000000  # a workspace address far from the operands
+    rows, width = 4, 40000  # beyond the register-resident window: needs the split kernels
+    need = R.rowred_workspace_size("rmsnorm", rows, width)
+    # nothing to do
+    assert lib.rowred_rmsnorm_ws(X, Y, 0, width, f(1e-6), None, 0, None) == R.ROWRED_OK
+    # no, misaligned or short workspace
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), None, 0, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), W + 8, need, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), W, need - 16, None) == R.ROWRED_ERR_INVALID_ARG
+    # workspace inside x, inside y
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), X + 4096, need, None) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), Y, need, None) == R.ROWRED_ERR_ALIAS
+    # y inside x, bad eps
+    assert lib.rowred_rmsnorm_ws(X, X + 16, rows, width, f(1e-6), W, need, None) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(-1.0), W, need, None) == R.ROWRED_ERR_INVALID_ARG
+    # row sum needs an element per row; min/max needs both outputs
+    O1, O2 = 0x7F4000000000, 0x7F5000000000
+    assert lib.rowred_row_sum_ws(X, O1, rows, 0, W, need, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_minmax_ws(X, O1, None, rows, width, W, need, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_minmax_ws(X, O1, O2, rows, width, O2, need, None) == R.ROWRED_ERR_ALIAS
+    # gamma/beta overlapping y
+    assert lib.rowred_layernorm_ws(X, None, Y + 64, None, Y, rows, width, f(1e-5), W, need, None) == \
+        R.ROWRED_ERR_ALIAS
+    # residual / affine only with LayerNorm; y2 only with min/max
+    p = R.SplitPlan(threads=256, chunks=2, policy=0)._c()
+    assert lib.rowred_split_run_plan(1, X, RR, None, None, Y, None, rows, width, f(1e-6), ctypes.byref(p), W, need,
+                                     None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_split_run_plan(2, X, None, RR, None, Y, None, rows, width, f(0), ctypes.byref(p), W, need,
+                                     None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_split_run_plan(0, X, None, None, None, Y, O1, rows, width, f(1e-5), ctypes.byref(p), W, need,
+                                     None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_split_run_plan(3, X, RR, None, None, O1, None, rows, width, f(0), ctypes.byref(p), W, need,
+                                     None) == R.ROWRED_ERR_INVALID_ARG
+    bad = R.SplitPlan(threads=256, chunks=3, policy=0)._c()
+    assert lib.rowred_split_run_plan(1, X, None, None, None, Y, None, rows, width, f(1e-6), ctypes.byref(bad), W,
+                                     need, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_split_run_plan(1, X, None, None, None, Y, None, rows, width, f(1e-6), None, W, need,
+                                     None) == R.ROWRED_ERR_INVALID_ARG

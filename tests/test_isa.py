@@ -54,8 +54,9 @@ def demangle(n):
 def test_every_kernel_is_spill_free(asm):
     meta = kernel_meta(asm)
     # five operators, affine LayerNorm (no 16-chunk kernel), the reload
-    # variant of the three matrix operators at 1-8 chunks, copy
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1
+    # variant of the three matrix operators at 1-8 chunks, copy; split rows:
+    # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -160,3 +161,33 @@ def test_barriers_only_where_partials_are_folded(asm):
             staged = chunks <= 4 and op not in (3, 4)
             want = folds + (1 if staged else 0)
             assert n == want, (dn, n)
+
+
+def test_split_kernels(asm):
+    """Statistics kernels read with cached loads (the apply kernel reads the
+    segment again and should find it in cache); apply kernels carry a
+    non-temporal and a cached copy of their segment loads and no barrier; merge
+    kernels work per wavefront, without barriers; statistics kernels fold
+    across waves once per reduction (LayerNorm and softmax twice)."""
+    seen = {"seg_stats_kernel": 0, "seg_apply_kernel": 0, "seg_merge_kernel": 0}
+    for name in kernel_meta(asm):
+        dn = demangle(name)
+        kind = next((k for k in seen if k + "<" in dn), None)
+        if not kind:
+            continue
+        seen[kind] += 1
+        body = kernel_body(asm, name)
+        nt, cached = x4_loads(body)
+        op = int(dn.split(kind + "<")[1].split(",")[0].split(">")[0])
+        if kind == "seg_stats_kernel":
+            assert nt == 0 and cached > 0, dn
+            assert body.count("s_barrier") == {0: 2, 1: 1, 2: 2, 3: 1, 4: 1}[op], dn
+        elif kind == "seg_apply_kernel":
+            # plus at most one cached 16-byte load: the row record
+            assert nt > 0 and cached - nt in (0, 1), (dn, nt, cached)
+            assert "s_barrier" not in body, dn
+            assert "global_store_dwordx4" in body, dn
+        else:
+            assert "s_barrier" not in body and "global_load_dword" in body, dn
+    assert seen == {"seg_stats_kernel": 15, "seg_apply_kernel": 9, "seg_merge_kernel": 5}
+
