@@ -134,7 +134,7 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // stripes with many lanes per row win: at most 2 slots (8 floats) per lane --
 // the pages' 8-float stripe at 4096 columns -- or 4 slots for inputs of at
 // most 32 MiB, which run in a single round of waves where fewer, fatter
-// waves amortise the wave start-up, and for rows of at most 256 granules
+// waves amortise the wave start-up (8 slots for some of them, below), and for rows of at most 256 granules
 // whose outputs are staged in LDS (below), where 4 slots per lane measured
 // 4-8% faster than 2 (at 1537 columns 2 slots stay 10% faster).  L is the smallest power of two meeting
 // that bound (at most 1024), chunks the smallest instantiated count covering
@@ -171,7 +171,16 @@ void choose_plan(const Call &c, rowred_plan *p) {
   const bool stage_ok = !rows_aligned && c.y_vec;
   // Staged rows that fit one wavefront (<= 64 lanes x 4 slots) store through
   // LDS, so their lanes can hold more slots.
-  const int64_t max_chunks = (small || scalar_out || (stage_ok && w <= 256)) ? 4 : 2;
+  int64_t max_chunks = (small || scalar_out || (stage_ok && w <= 256)) ? 4 : 2;
+  // Single-round inputs of 8-32 MiB per input with two input streams
+  // (residual LayerNorm), or of 16-32 MiB with rows of >= 1024 granules,
+  // keep more loads in flight per lane with 8 slots: 5-10% and 0-6% faster
+  // at 1024x4096, 2048x2048, 4096x1024, 8192x512 and 512x8192 (measured on
+  // 16-byte-aligned rows; below 8 MiB 8 slots were up to 17% slower).
+  const bool two_inputs = c.r != nullptr && c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
+  if (small && !scalar_out && !stage_ok &&
+      ((two_inputs && in_bytes >= (int64_t(8) << 20)) || (w >= 1024 && in_bytes >= (int64_t(16) << 20))))
+    max_chunks = 8;
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
   int chunks = round_up_chunks((w + L - 1) / L);

@@ -92,7 +92,7 @@ def test_plan_for_workload_shapes():
     st = R.ROWRED_POLICY_STAGE_STORES
     # short ragged rows (staged, <= 256 granules) keep cached loads
     cases = {(131072, 127): (16, 3, ns | st), (131072, 257): (32, 3, ns | st),
-             (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (256, 4, nl | ns),
+             (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
              (17, 257): (32, 3, ns | st)}
     for (rows, width), (L, C, pol) in cases.items():
@@ -311,7 +311,7 @@ def test_layernorm_entry_argument_checks():
 
 def test_plan_query_layernorm_without_residual():
     p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=1024, width=4096)
-    assert (p.lanes_per_row, p.chunks) == (256, 4)
+    assert (p.lanes_per_row, p.chunks) == (128, 8)
 
 
 def test_row_reduce_argument_checks():
