@@ -371,6 +371,7 @@ def bench(cfg, steps, warmup, cpu_seconds):
     }
     out["copy_ceiling"] = {"same_bytes_as_dominant": copy_ceiling(algo_bytes(dc)),
                            "1GiB": copy_ceiling(2 ** 30, reps=10)}
+    out["launch_floor_us"] = launch_floor()
     if cfg == 2:
         out["context_m1max_us"] = M1MAX_CONTEXT_US
     if cpu_seconds > 0:
@@ -410,6 +411,30 @@ def copy_ceiling(nbytes, reps=20):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
     return {"bytes_per_call": 8 * n, "us_per_call": round(us, 3), "GB_s": round(8 * n / (us * 1e-6) / 1e9, 1)}
+
+
+def launch_floor(reps=50):
+    """us per call of the library's copy moving one 16-byte granule, timed
+    like the reductions (a graph of `reps` calls after warm-up replays): the
+    fixed cost of one kernel launch, ramp and drain in this method."""
+    import torch
+
+    import row_wise_reduction_amd as R
+    src = torch.ones(4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                R.rowred_copy(src, dst)
+    torch.cuda.current_stream().wait_stream(stream)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    ms, _ = replay_timed([g])
+    return round(ms[0] * 1e3 / reps, 3)
 
 
 def pmc_pass(cfg):
@@ -550,7 +575,7 @@ def pmc_reload_pass(cfg):
 PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {ctr} --output-format csv -d <out_{ctr}> -o run -- "
            "python3 <repo>/bench.py --pmc --all > <log_{ctr}>")
 TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-             "python3 <repo>/bench.py --cpu-seconds 0")
+             "python3 <repo>/bench.py{args} --cpu-seconds 0")
 
 
 def _csv_rows(path):
@@ -702,7 +727,8 @@ def trace_summary(stats_csv, bench_json, out_path):
     rows = list(csv.DictReader(open(stats_csv)))
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     lines = [f"# rocprofv3 kernel statistics, workload {b['config']['config_id']}: {b['config']['workload']}",
-             "#   " + TRACE_CMD,
+             "#   " + TRACE_CMD.format(args=("" if b["config"]["config_id"] == 2 else f" --config {b['config']['config_id']}")
+                                   + ("" if b["steps"] == 50 else f" --steps {b['steps']}")),
              f"# kernel_source_hash: {b.get('kernel_source_hash', 'unknown')}",
              "# name | calls | total_ns | average_ns | min_ns | max_ns | percentage"]
     for r in rows:

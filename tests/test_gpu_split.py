@@ -215,3 +215,47 @@ def test_row_blocks(op):
     for br in (1, 3, 6):
         got = run(op, x, r, g, b, plan=R.SplitPlan(threads=256, chunks=2, policy=3, block_rows=br), shift=shift)
         assert np.array_equal(np.asarray(got).view(np.uint32), np.asarray(whole).view(np.uint32)), (op, br)
+
+
+def test_graph_capture_and_replay():
+    """The three split kernels of each _ws call captured in one HIP graph
+    with one shared workspace (no memset nodes: the workspace needs no
+    clearing), replayed several times with eager work and synchronisation
+    in between; every replay equals the eager results bitwise."""
+    t = torch()
+    rows, width = 5, 40001
+    x = synthetic.random_matrix(404, rows, width, "normal")
+    r = synthetic.random_matrix(405, rows, width, "normal", tensor="r")
+    xd, rd = shifted_input(x, 1), shifted_input(r, 1)
+    ws = t.empty(1 << 20, dtype=t.uint8, device="cuda")
+    outs = [t.empty(rows, width, device="cuda") for _ in range(3)] + [t.empty(rows, device="cuda") for _ in range(3)]
+
+    def calls():
+        R.rowred_layernorm_ws(xd, rd, None, None, outs[0], ws, eps=1e-5)
+        R.rowred_rmsnorm_ws(xd, outs[1], ws, eps=1e-6)
+        R.rowred_softmax_ws(xd, outs[2], ws)
+        R.rowred_row_sum_ws(xd, outs[3], ws)
+        R.rowred_row_minmax_ws(xd, outs[4], outs[5], ws)
+
+    calls()
+    t.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    assert_close(eager[0].cpu().numpy(), oracle.layernorm_residual(x, r, 1e-5), "graph ln")
+    assert_close(eager[2].cpu().numpy(), oracle.softmax(x), "graph softmax")
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            calls()
+    t.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert t.equal(o.view(t.int32), e.view(t.int32)), (rep, i)
+        calls()  # eager work between replays, through the same workspace
+        t.cuda.synchronize()
