@@ -108,6 +108,14 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m row_wise_reduction_amd.build` "
                               "(or __graft_entry__.build())")
+        # torch ships its own copy of the HIP runtime under the same soname.
+        # Loaded first, it is the one this library binds to; loaded after
+        # this library, it would be a second runtime in the process, and
+        # torch's streams would be invalid handles to ours.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         sigs = {
             "rowred_layernorm_residual": [_P, _P, _P, _I64, _I64, ctypes.c_float, _P],

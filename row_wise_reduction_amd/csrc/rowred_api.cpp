@@ -392,10 +392,6 @@ int finish_split(const Call &c, rowred_split_plan *p) {
   return ROWRED_OK;
 }
 
-// Kernel operator of a split call: LayerNorm (any of r, gamma, beta) 0,
-// RMSNorm 1, softmax 2, row sum 3, row min/max 4.
-int split_op(const Call &c) { return c.op; }
-
 int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws || ((uintptr_t)ws & 15)) return ROWRED_ERR_INVALID_ARG;
   if ((int64_t)ws_bytes < p.workspace_bytes) return ROWRED_ERR_INVALID_ARG;
@@ -433,7 +429,9 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
     a.y = scalar ? c.y + r0 : c.y + e0;
     a.y2 = c.y2 ? c.y2 + r0 : nullptr;
     a.rows = n;
-    const int err = launch_split(split_op(c), p.chunks, n * p.segments, p.threads, a, stream);
+    // kernel operator = the public op: LayerNorm (any of r, gamma, beta) 0,
+    // RMSNorm 1, softmax 2, row sum 3, row min/max 4
+    const int err = launch_split(c.op, p.chunks, n * p.segments, p.threads, a, stream);
     if (err != 0) return ROWRED_ERR_HIP;
   }
   return ROWRED_OK;
