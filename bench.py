@@ -74,7 +74,7 @@ WORKLOAD_NAMES = {
 CORE = (1, 2, 3, 4, 5)
 NEXT = (6, 7, 8, 9)
 WS_WORKLOADS = (9,)  # run through the _ws entry points (caller workspace)
-WORKLOADS = {**synthetic.CONFIGS, **synthetic.NEXT_CONFIGS}
+WORKLOADS = {**synthetic.CORE_WORKLOADS, **synthetic.NEXT_WORKLOADS}
 
 
 def n_inputs(op):

@@ -63,7 +63,7 @@ class Case:
         return f"cfg{self.cfg}-{self.op}-{self.rows}x{self.width}"
 
 
-CONFIGS = {
+CORE_WORKLOADS = {
     1: [Case(1, "layernorm_residual", 17, 257, "uniform"),
         Case(1, "layernorm_residual", 1, 127, "uniform")],
     2: [Case(2, op, 1024, 4096, "uniform") for op in ("softmax", "rmsnorm", "layernorm_residual")],
@@ -79,7 +79,7 @@ CONFIGS = {
 # the row sum / paired min-max reductions at a wide and a short ragged shape,
 # and rows beyond one workgroup's registers (1M, 128K, 256K and 4M columns)
 # plus the pages' few-row shape 7x1537.
-NEXT_CONFIGS = {
+NEXT_WORKLOADS = {
     6: [Case(6, "layernorm", 1024, 4096, "uniform"), Case(6, "layernorm", 16384, 8192, "uniform")],
     7: [Case(7, "layernorm_affine", 1024, 4096, "uniform"), Case(7, "layernorm_affine", 16384, 8192, "uniform")],
     8: [Case(8, "row_sum", 16384, 8192, "uniform"), Case(8, "row_minmax", 16384, 8192, "uniform"),
@@ -91,8 +91,8 @@ NEXT_CONFIGS = {
 
 
 def all_cases() -> Iterator[Case]:
-    for cfg in sorted(CONFIGS):
-        yield from CONFIGS[cfg]
+    for cfg in sorted(CORE_WORKLOADS):
+        yield from CORE_WORKLOADS[cfg]
 
 
 def affine_vectors(case: Case):

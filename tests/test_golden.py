@@ -75,8 +75,8 @@ def test_generator_distributions():
     s2 = synthetic.draw("stress", 64, 32768, synthetic.seed_sequence(5, "softmax", "x", 64, 32768))
     assert np.array_equal(s, s2)
     # different tensors get different streams
-    a = synthetic.case_input(synthetic.CONFIGS[1][0], "x")
-    b = synthetic.case_input(synthetic.CONFIGS[1][0], "r")
+    a = synthetic.case_input(synthetic.CORE_WORKLOADS[1][0], "x")
+    b = synthetic.case_input(synthetic.CORE_WORKLOADS[1][0], "r")
     assert not np.array_equal(a, b)
 
 

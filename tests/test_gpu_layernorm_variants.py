@@ -85,7 +85,7 @@ def test_variants_every_plan(variant, width):
     assert n >= 3
 
 
-@pytest.mark.parametrize("case", [c for cfg in sorted(synthetic.NEXT_CONFIGS) for c in synthetic.NEXT_CONFIGS[cfg]
+@pytest.mark.parametrize("case", [c for cfg in sorted(synthetic.NEXT_WORKLOADS) for c in synthetic.NEXT_WORKLOADS[cfg]
                                   if c.op in ("layernorm", "layernorm_affine")], ids=lambda c: c.name)
 def test_next_workloads_full_size(case):
     print_case(case.name)

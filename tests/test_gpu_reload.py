@@ -55,7 +55,7 @@ def test_reload_matches_resident_bitwise(op, width):
     assert n >= 1
 
 
-@pytest.mark.parametrize("case", [synthetic.CONFIGS[4][0], synthetic.CONFIGS[5][0]], ids=lambda c: c.name)
+@pytest.mark.parametrize("case", [synthetic.CORE_WORKLOADS[4][0], synthetic.CORE_WORKLOADS[5][0]], ids=lambda c: c.name)
 def test_reload_full_size(case):
     """The chooser's plan with the reload bit at a full workload shape:
     bitwise the resident result."""

@@ -97,7 +97,7 @@ def test_every_plan(width):
     assert n >= 3
 
 
-@pytest.mark.parametrize("case", synthetic.NEXT_CONFIGS[8], ids=lambda c: c.name)
+@pytest.mark.parametrize("case", synthetic.NEXT_WORKLOADS[8], ids=lambda c: c.name)
 def test_full_size(case):
     print_case(case.name)
     x = synthetic.case_input(case, "x")
