@@ -27,7 +27,7 @@ oracle's throughput on host cores, and per-operator figures.
                                 # workloads 1..7 on cold buffers, + a 256 MiB
                                 # copy per workload for calibration
     python bench.py --all       # one JSON line per core workload (1..5)
-    python bench.py --next      # plain and affine LayerNorm, row sum / min-max, any width (6-9)
+    python bench.py --next      # plain and affine LayerNorm, row sum / min-max, any width (6-10)
     python bench.py --reload    # resident vs per-phase reload kernels, workloads 2-5
     python bench.py --pmc --reload  # its counter pass
 """
@@ -70,9 +70,11 @@ WORKLOAD_NAMES = {
     8: "row sum and row min/max, 16384x8192 U[-1,1] and 131072x257 N(0,1)",
     9: "any width (_ws entry points): softmax 64x1048576, RMSNorm 1024x131072, residual LayerNorm 256x262144, "
        "row sum 16x4194304, softmax 7x1537",
+    10: "many wide rows (plain entry points, looped kernels): softmax 4096x65536, RMSNorm 2048x131072, "
+        "residual LayerNorm 1024x65536, row sum 2048x131072",
 }
 CORE = (1, 2, 3, 4, 5)
-NEXT = (6, 7, 8, 9)
+NEXT = (6, 7, 8, 9, 10)
 WS_WORKLOADS = (9,)  # run through the _ws entry points (caller workspace)
 WORKLOADS = {**synthetic.CORE_WORKLOADS, **synthetic.NEXT_WORKLOADS}
 
@@ -101,7 +103,7 @@ def kernel_source_hash():
     h = hashlib.sha256()
     for p in ("row_wise_reduction_amd/csrc/rowred_kernels.hip", "row_wise_reduction_amd/csrc/rowred_api.cpp",
               "row_wise_reduction_amd/csrc/rowred_internal.h", "row_wise_reduction_amd/csrc/rowred_device.h",
-              "row_wise_reduction_amd/csrc/rowred_split.hip"):
+              "row_wise_reduction_amd/csrc/rowred_split.hip", "row_wise_reduction_amd/csrc/rowred_looped.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -610,7 +612,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
             if row["Counter_Name"] != ctr:
                 continue
             name = row["Kernel_Name"]
-            if "rows_kernel" in name or "seg_" in name:
+            if "rows_kernel" in name or "seg_" in name or "looped_kernel" in name:
                 cfg, case = expected[i]
                 pending.append((cfg, case, float(row["Counter_Value"]), name))
                 i += 1
@@ -750,7 +752,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
-    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-9)")
+    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-10)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
     ap.add_argument("--reload", action="store_true",

@@ -39,11 +39,14 @@
  *
  * Sizes: rows < 0 or width < 0 -> ROWRED_ERR_INVALID_ARG.  rows == 0 or
  * width == 0 -> ROWRED_OK with nothing launched (pointers may then be NULL).
- * A NULL or misaligned pointer otherwise -> ROWRED_ERR_INVALID_ARG.  A row is
- * held in registers across the phases, so width is capped: the 16-byte slot
- * window of a row (ceil((width + misalignment) / 4)) must not exceed 8192,
- * i.e. width <= 32768 for 16-byte-aligned rows; wider rows give
- * ROWRED_ERR_UNSUPPORTED (the _ws entry points at the end take any width).
+ * A NULL or misaligned pointer otherwise -> ROWRED_ERR_INVALID_ARG.  A row
+ * whose 16-byte slot window (ceil((width + misalignment) / 4)) is at most
+ * 8192 (width <= 32768 for 16-byte-aligned rows) is held in registers across
+ * the phases and read once; a wider row is walked twice by one workgroup
+ * (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is read
+ * twice.  That suits many rows; for few wide rows the _ws entry points at the
+ * end split each row over many workgroups.  width > INT32_MAX ->
+ * ROWRED_ERR_UNSUPPORTED.
  *
  * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
  * accepted; a LayerNorm row with zero variance then gives NaN (0/0), as
@@ -71,7 +74,7 @@ enum rowred_status {
   ROWRED_OK = 0,
   ROWRED_ERR_INVALID_ARG = 1, /* bad size, pointer, eps or plan */
   ROWRED_ERR_ALIAS = 2,       /* y overlaps an input */
-  ROWRED_ERR_UNSUPPORTED = 3, /* row too wide for one register-resident pass */
+  ROWRED_ERR_UNSUPPORTED = 3, /* a size beyond the limits stated below (32-bit widths, launch grid) */
   ROWRED_ERR_HIP = 4          /* the HIP runtime refused the launch */
 };
 
@@ -109,8 +112,9 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
  * comparison and measurement".  gamma and beta hold `width` floats each
  * (4-byte aligned, read only, must not overlap y).  With all three NULL
  * this is the no-affine LayerNorm of the same page's "Validation" section.
- * With gamma or beta the row cap is 6144 granules (24576 floats for 16-byte
- * aligned rows); wider rows give ROWRED_ERR_UNSUPPORTED.
+ * With gamma or beta, rows of more than 6144 granules (24576 floats for
+ * 16-byte aligned rows) take the looped kernels (gamma/beta need registers
+ * the wider register-resident kernels do not have).
  */
 int rowred_layernorm(const float *x, const float *r, const float *gamma,
                      const float *beta, float *y, int64_t rows, int64_t width,
@@ -202,10 +206,17 @@ enum rowred_policy {
                                      gamma/beta, RMSNorm, softmax), chunks <= 8, LayerNorm at
                                      7-8 chunks with threads <= 512; never chosen by the
                                      entry points */
-  ROWRED_POLICY_REVERSE = 32      /* split plans only (rowred_split_plan): the apply kernel
+  ROWRED_POLICY_REVERSE = 32,     /* split plans only (rowred_split_plan): the apply kernel
                                      walks the (row, segment) pairs in reverse order, so
                                      that it first reads again what the statistics kernel
                                      read last; measured no faster, never chosen */
+  ROWRED_POLICY_LOOPED = 64       /* rows of any width: lanes_per_row == threads, one row per
+                                     workgroup, which walks the row in tiles of threads * chunks
+                                     granules (chunks 2 or 4; LayerNorm 2) twice -- statistics
+                                     with cached loads, then map and store (row sum and min/max:
+                                     once).  NT_LOADS / NT_STORES apply to the second walk; no
+                                     other bit may be set.  The entry points choose it for rows
+                                     wider than 8192 granules */
 };
 
 /*
@@ -260,16 +271,17 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
 /* ------------------------------------------------------------------------
  * Any width, and rows split across workgroups: the _ws entry points.
  *
- * The entry points above keep a whole row in one workgroup's registers, so
- * rows wider than 8192 16-byte granules are ROWRED_ERR_UNSUPPORTED, and a
- * matrix of few rows keeps few compute units busy.  "Immutable input reuse
+ * The entry points above give each row one workgroup: rows wider than 8192
+ * 16-byte granules are walked twice by it, and a matrix of few wide rows
+ * keeps few compute units busy.  "Immutable input reuse
  * in Metal reductions" leaves rows beyond the private stripe open (section
  * "Next decisions and open questions": mixed cache/reload choices) and times
  * few-row shapes such as 7x1537 (section "Fixed-width GPU and dispatch
  * results").  The _ws entry points compute the same operators, same
  * arguments, for any width:
- *   - when the row fits the register-resident kernels they run those (the
- *     workspace is then not touched);
+ *   - when the row fits the register-resident kernels they run those, and
+ *     for rows wider than that with at least 2048 rows the looped kernels
+ *     (ROWRED_POLICY_LOOPED) -- the workspace is then not touched;
  *   - otherwise each row's window of 16-byte granules is cut into segments
  *     of T*C granules, one workgroup per (row, segment), in three kernels:
  *     per-segment statistics into the workspace, a fixed-order merge per row,

@@ -34,6 +34,7 @@ ROWRED_POLICY_XCD_REMAP = 4
 ROWRED_POLICY_STAGE_STORES = 8
 ROWRED_POLICY_RELOAD = 16
 ROWRED_POLICY_REVERSE = 32
+ROWRED_POLICY_LOOPED = 64
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1

@@ -70,7 +70,7 @@ int max_window(const float *x, int64_t rows, int64_t width) {
 
 // Checks shared by every entry point.  `need_eps` marks ops with an eps.
 int check_call(int op, const float *x, const float *r, const float *y, int64_t rows, int64_t width, bool need_r,
-               bool need_eps, float eps, Call *out, bool cap = true) {
+               bool need_eps, float eps, Call *out, bool cap = false) {
   if (op < 0 || op >= kNumMatrixOps) return ROWRED_ERR_INVALID_ARG;
   if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   if (need_eps && (!isfinite(eps) || eps < 0.0f)) return ROWRED_ERR_INVALID_ARG;
@@ -100,7 +100,23 @@ int check_call(int op, const float *x, const float *r, const float *y, int64_t r
 int kernel_op(const Call &c) { return (c.gamma || c.beta) ? kKernelOpLayerNormAffine : c.op; }
 
 // Fill grid / rows_per_group / window and check every plan constraint.
+// A looped plan (ROWRED_POLICY_LOOPED): one row per workgroup, any width.
+int finish_looped_plan(const Call &c, rowred_plan *p) {
+  const int64_t L = p->lanes_per_row, T = p->threads;
+  if (L != T || !is_pow2(T) || T < 64 || T > 1024) return ROWRED_ERR_INVALID_ARG;
+  if (!looped_kernel_exists(kernel_op(c), p->chunks)) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyLooped | kPolicyNtLoads | kPolicyNtStores)) return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
+  p->window = c.window;
+  p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
+  p->rows_per_group = 1;
+  p->grid = c.rows;
+  if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
 int finish_plan(const Call &c, rowred_plan *p) {
+  if (p->policy & kPolicyLooped) return finish_looped_plan(c, p);
   const int64_t L = p->lanes_per_row, T = p->threads;
   if (!is_pow2(L) || L > 1024) return ROWRED_ERR_INVALID_ARG;
   if (T < 64 || T > 1024 || T % 64 != 0 || T % L != 0) return ROWRED_ERR_INVALID_ARG;
@@ -162,7 +178,24 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // 512 threads, 16384x8192 runs at 78-80 us and 131072x257 at 23-24 us,
 // against 90-100 us and 32-36 us with the 2-slot stripes above (L = 64 x 2
 // slots leaves half of each 257-column row's lanes idle).
+// Rows wider than the register-resident kernels hold (or affine LayerNorm
+// beyond its 6144-granule kernels) loop over the row: 1024 lanes, tiles of
+// 4 slots per lane (2 for LayerNorm), streaming loads and stores in the
+// second walk.
+void choose_looped(const Call &c, rowred_plan *p) {
+  const int kop = kernel_op(c);
+  *p = rowred_plan{};
+  p->lanes_per_row = 1024;
+  p->threads = 1024;
+  p->chunks = looped_kernel_exists(kop, 4) ? 4 : 2;
+  p->policy = kPolicyLooped | kPolicyNtLoads | kPolicyNtStores;
+}
+
 void choose_plan(const Call &c, rowred_plan *p) {
+  if (c.window > kMaxWindow) {
+    choose_looped(c, p);
+    return;
+  }
   const int64_t w = c.window;
   const int64_t in_bytes = c.rows * c.width * 4;
   const bool small = in_bytes <= (int64_t(32) << 20);
@@ -191,6 +224,10 @@ void choose_plan(const Call &c, rowred_plan *p) {
     L /= 2;
     chunks = round_up_chunks((w + L - 1) / L);
     if (chunks < 0) break;
+  }
+  if (chunks < 0) {  // affine LayerNorm beyond its widest register-resident kernel
+    choose_looped(c, p);
+    return;
   }
   p->lanes_per_row = (int32_t)L;
   p->chunks = chunks;
@@ -228,7 +265,9 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
                   ((uintptr_t)c.beta & 15) == 0)
                      ? 1
                      : 0;
-  const int err = launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);
+  const int err = (plan.policy & kPolicyLooped)
+                      ? launch_looped(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
+                      : launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);
   return err == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
 }
 
@@ -247,7 +286,7 @@ int entry(int op, const float *x, const float *r, float *y, int64_t rows, int64_
 
 // Row sum / row min-max: outputs are `rows` floats each.
 int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t rows, int64_t width, Call *out,
-                      bool cap = true) {
+                      bool cap = false) {
   if (op != ROWRED_OP_ROW_SUM && op != ROWRED_OP_ROW_MINMAX) return ROWRED_ERR_INVALID_ARG;
   if (rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   out->op = op;
@@ -452,15 +491,23 @@ int check_ws_call(int op, const float *x, const float *r, const float *gamma, co
   return op == ROWRED_OP_LAYERNORM_RESIDUAL ? attach_affine(c, gamma, beta) : ROWRED_OK;
 }
 
-// A _ws call: the register-resident kernels when the row fits them, else
-// (or with an explicit split plan) the split kernels.
+// Rows beyond the register-resident window: with at least this many rows
+// the looped kernels (one workgroup per row, no workspace) fill the chip and
+// beat the split kernels (softmax 4096x65536: 0.88x the time, residual
+// LayerNorm 1024x65536: 0.94x); with fewer the split kernels win, by up to
+// 6x on 16 rows (measured on MI355X).
+constexpr int64_t kLoopedMinRows = 2048;
+
+// A _ws call: the register-resident kernels when the row fits them, the
+// looped kernels for many wide rows, else (or with an explicit split plan)
+// the split kernels.
 int ws_entry(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y, float *y2,
              int64_t rows, int64_t width, float eps, const rowred_split_plan *plan, void *ws, size_t ws_bytes,
              hipStream_t stream) {
   Call c;
   int st = check_ws_call(op, x, r, gamma, beta, y, y2, rows, width, eps, &c);
   if (st != ROWRED_OK || rows == 0 || width == 0) return st;
-  if (!plan && c.window <= kMaxWindow) {
+  if (!plan && (c.window <= kMaxWindow || c.rows >= kLoopedMinRows)) {
     rowred_plan p;
     choose_plan(c, &p);
     if (p.chunks >= 0) {
@@ -638,7 +685,7 @@ ROWRED_API const char *rowred_status_string(int status) {
     case ROWRED_OK: return "ok";
     case ROWRED_ERR_INVALID_ARG: return "invalid argument (size, pointer, eps or plan)";
     case ROWRED_ERR_ALIAS: return "output overlaps an input";
-    case ROWRED_ERR_UNSUPPORTED: return "row too wide for a register-resident pass (the _ws entry points take any width)";
+    case ROWRED_ERR_UNSUPPORTED: return "size beyond the library's limits (width above INT32_MAX or launch grid too large)";
     case ROWRED_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

@@ -32,7 +32,9 @@ constexpr int kPolicyNtStores = ROWRED_POLICY_NT_STORES;
 constexpr int kPolicyXcdRemap = ROWRED_POLICY_XCD_REMAP;
 constexpr int kPolicyStageStores = ROWRED_POLICY_STAGE_STORES;
 constexpr int kPolicyReload = ROWRED_POLICY_RELOAD;
-constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload;
+constexpr int kPolicyLooped = ROWRED_POLICY_LOOPED;
+constexpr int kPolicyAll =
+    kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload | kPolicyLooped;
 // The per-phase reload variant exists for the three matrix operators (kernel
 // ops 0-2) at up to 8 chunks.
 constexpr int kMaxReloadChunks = 8;
@@ -71,6 +73,16 @@ constexpr bool kernel_exists(int op, int chunks) { return !(op == kKernelOpLayer
 // argument.
 int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &args,
                 hipStream_t stream);
+
+// Enqueue the looped kernel (rows wider than the register-resident window,
+// ROWRED_POLICY_LOOPED): one workgroup of `threads` lanes per row, tiles of
+// threads * chunks granules (chunks 2 or 4), grid = rows.
+int launch_looped(int op, int chunks, int64_t rows, int threads, const RowArgs &args, hipStream_t stream);
+// LayerNorm (plain, residual or affine) loops at 2 chunks only: its x and r
+// tiles, two deep, need the registers.
+constexpr bool looped_kernel_exists(int op, int chunks) {
+  return chunks == 2 || (chunks == 4 && op != 0 && op != kKernelOpLayerNormAffine);
+}
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);

@@ -77,8 +77,9 @@ CORE_WORKLOADS = {
 # LayerNorm at the shape the pages time it (1024x4096) and at the wide-row
 # shape, affine LayerNorm (gamma ~ 1 + 0.1 N(0,1), beta ~ 0.1 N(0,1)), and
 # the row sum / paired min-max reductions at a wide and a short ragged shape,
-# and rows beyond one workgroup's registers (1M, 128K, 256K and 4M columns)
-# plus the pages' few-row shape 7x1537.
+# rows beyond one workgroup's registers (1M, 128K, 256K and 4M columns) plus
+# the pages' few-row shape 7x1537 through the workspace entry points, and
+# many wide rows (64K and 128K columns) through the plain entry points.
 NEXT_WORKLOADS = {
     6: [Case(6, "layernorm", 1024, 4096, "uniform"), Case(6, "layernorm", 16384, 8192, "uniform")],
     7: [Case(7, "layernorm_affine", 1024, 4096, "uniform"), Case(7, "layernorm_affine", 16384, 8192, "uniform")],
@@ -87,6 +88,8 @@ NEXT_WORKLOADS = {
     9: [Case(9, "softmax", 64, 1 << 20, "normal"), Case(9, "rmsnorm", 1024, 1 << 17, "uniform"),
         Case(9, "layernorm_residual", 256, 1 << 18, "uniform"), Case(9, "row_sum", 16, 1 << 22, "uniform"),
         Case(9, "softmax", 7, 1537, "normal")],
+    10: [Case(10, "softmax", 4096, 1 << 16, "normal"), Case(10, "rmsnorm", 2048, 1 << 17, "uniform"),
+         Case(10, "layernorm_residual", 1024, 1 << 16, "uniform"), Case(10, "row_sum", 2048, 1 << 17, "uniform")],
 }
 
 

@@ -152,9 +152,12 @@ def test_size_errors():
     assert raw("rowred_rmsnorm", None, None, 0, 4, f(1e-6), None) == R.ROWRED_OK
     assert raw("rowred_softmax", None, None, 7, 0, None) == R.ROWRED_OK
     assert raw("rowred_layernorm_residual", None, None, None, 0, 0, f(1e-5), None) == R.ROWRED_OK
-    # too wide for one register-resident pass
-    assert raw("rowred_softmax", X, Y, 4, 32769, None) == R.ROWRED_ERR_UNSUPPORTED
-    assert raw("rowred_softmax", X + 4, Y + 4, 4, 32768, None) == R.ROWRED_ERR_UNSUPPORTED
+    # rows wider than one register-resident pass loop over the row instead
+    lp = R.ROWRED_POLICY_LOOPED
+    for xx, yy, w in ((X, Y, 32769), (X + 4, Y + 4, 32768), (X, Y, 1 << 20)):
+        p = R.rowred_plan_query("softmax", xx, None, yy, rows=4, width=w)
+        assert p.policy & lp and p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
+    # widths beyond 32-bit element indices within a row
     assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
 
 
@@ -295,8 +298,6 @@ def test_layernorm_entry_argument_checks():
     assert lib.rowred_layernorm(X, None, Y + 64, None, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_ALIAS
     assert lib.rowred_layernorm(X, None, None, Y + 4 * 255, Y, 4, 64, f(1e-5), None) == R.ROWRED_ERR_ALIAS
     assert lib.rowred_layernorm(X, None, None, None, Y, 4, 64, f(-1.0), None) == R.ROWRED_ERR_INVALID_ARG
-    # affine rows are capped at 6144 granules
-    assert lib.rowred_layernorm(X, None, G, None, Y, 2, 32768, f(1e-5), None) == R.ROWRED_ERR_UNSUPPORTED
     assert lib.rowred_layernorm(X, None, None, None, Y, 0, 32768, f(1e-5), None) == R.ROWRED_OK
     # explicit plans: affine kernels of >= 7 chunks need <= 512 threads, 16 chunks do not exist
     c = bad_plan(lanes_per_row=1024, chunks=8, threads=1024)._c()
@@ -326,7 +327,8 @@ def test_row_reduce_argument_checks():
     assert lib.rowred_row_minmax(X, O1, None, 4, 4, None) == R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_row_minmax(X, O1, O1 + 8, 4, 4, None) == R.ROWRED_ERR_ALIAS  # min and max overlap
     assert lib.rowred_row_minmax(X, O1, X, 4, 4, None) == R.ROWRED_ERR_ALIAS
-    assert lib.rowred_row_sum(X, O1, 4, 32769, None) == R.ROWRED_ERR_UNSUPPORTED
+    p = R.rowred_plan_query("row_sum", X, None, O1, rows=4, width=32769)
+    assert p.policy & R.ROWRED_POLICY_LOOPED and p.grid == 4
     # staging does not apply to scalar outputs
     c = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=R.ROWRED_POLICY_STAGE_STORES)._c()
     assert lib.rowred_row_reduce_run_plan(3, X, O1, None, 8, 127, ctypes.byref(c), None) == R.ROWRED_ERR_INVALID_ARG
@@ -419,3 +421,29 @@ def test_ws_entry_argument_checks():
                                      need, None) == R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_split_run_plan(1, X, None, None, None, Y, None, rows, width, f(1e-6), None, W, need,
                                      None) == R.ROWRED_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(lanes_per_row=512, threads=1024), dict(lanes_per_row=1024, threads=1024, chunks=3),
+                                dict(lanes_per_row=1024, threads=1024, chunks=8),
+                                dict(lanes_per_row=96, threads=96, chunks=2),
+                                dict(lanes_per_row=1024, threads=1024, chunks=2,
+                                     policy=R.ROWRED_POLICY_LOOPED | R.ROWRED_POLICY_STAGE_STORES),
+                                dict(lanes_per_row=1024, threads=1024, chunks=2,
+                                     policy=R.ROWRED_POLICY_LOOPED | R.ROWRED_POLICY_XCD_REMAP)])
+def test_looped_plan_rejects(kw):
+    base = dict(lanes_per_row=1024, rows_per_group=0, chunks=4, threads=1024, grid=0,
+                policy=R.ROWRED_POLICY_LOOPED)
+    base.update(kw)
+    c = R.Plan(**base)._c()
+    assert R.lib().rowred_run_plan(1, X, None, Y, 4, 100000, f(1e-6), ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+
+
+def test_looped_layernorm_needs_two_chunks():
+    c = R.Plan(lanes_per_row=1024, rows_per_group=0, chunks=4, threads=1024, grid=0,
+               policy=R.ROWRED_POLICY_LOOPED)._c()
+    assert R.lib().rowred_run_plan(0, X, RR, Y, 4, 100000, f(1e-5), ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    p = R.rowred_plan_query("layernorm_residual", X, RR, Y, rows=4, width=100000)
+    assert p.chunks == 2 and p.policy & R.ROWRED_POLICY_LOOPED
+

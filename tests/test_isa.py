@@ -56,7 +56,8 @@ def test_every_kernel_is_spill_free(asm):
     # five operators, affine LayerNorm (no 16-chunk kernel), the reload
     # variant of the three matrix operators at 1-8 chunks, copy; split rows:
     # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5
+    # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -190,4 +191,25 @@ def test_split_kernels(asm):
         else:
             assert "s_barrier" not in body and "global_load_dword" in body, dn
     assert seen == {"seg_stats_kernel": 15, "seg_apply_kernel": 9, "seg_merge_kernel": 5}
+
+
+def test_looped_kernels(asm):
+    """Looped kernels: no scratch; the statistics walk uses cached loads and
+    the second walk (matrix outputs) has a non-temporal copy; one collective
+    per statistic (LayerNorm and softmax two), no barrier in the loops."""
+    seen = 0
+    for name in kernel_meta(asm):
+        dn = demangle(name)
+        if "looped_kernel<" not in dn:
+            continue
+        seen += 1
+        body = kernel_body(asm, name)
+        op = int(dn.split("looped_kernel<")[1].split(",")[0])
+        nt, cached = x4_loads(body)
+        if op in (3, 4):
+            assert nt == 0 and cached > 0, dn
+        else:
+            assert nt > 0 and cached > nt, (dn, nt, cached)
+        assert body.count("s_barrier") == {0: 2, 1: 1, 2: 2, 3: 1, 4: 1}[op], dn
+    assert seen == 9
 
