@@ -697,6 +697,6 @@ ROWRED_API int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stre
   if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return ROWRED_ERR_INVALID_ARG;
   if (n > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
   if (overlaps(x, y, n * 4)) return ROWRED_ERR_ALIAS;
-  if ((n / 4 + 1023) / 1024 > INT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  if ((n / 4 + 63) / 64 > INT32_MAX) return ROWRED_ERR_UNSUPPORTED;  // 64-lane workgroups, one slot per lane
   return launch_copy(x, y, n / 4, stream) == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
 }
