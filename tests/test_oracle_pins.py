@@ -119,6 +119,10 @@ def test_row_sum_and_minmax_worked():
     assert np.array_equal(lo, [1.0, -7.0]) and np.array_equal(hi, [4.0, 2.0])
     lo, hi = oracle.row_minmax(np.zeros((2, 0), np.float32))
     assert np.array_equal(lo, [np.inf, np.inf]) and np.array_equal(hi, [-np.inf, -np.inf])
+    # NaN entries are skipped (minNum/maxNum); an all-NaN row is like the empty row
+    nan = np.nan
+    lo, hi = oracle.row_minmax(np.array([[nan, 3, -2, nan], [nan, nan, nan, nan]], np.float32))
+    assert np.array_equal(lo, [-2.0, np.inf]) and np.array_equal(hi, [3.0, -np.inf])
 
 
 # --------------------------------------------------------------------------
