@@ -72,10 +72,12 @@ WORKLOAD_NAMES = {
        "row sum 16x4194304, softmax 7x1537",
     10: "many wide rows (plain entry points, looped kernels): softmax 4096x65536, RMSNorm 2048x131072, "
         "residual LayerNorm 1024x65536, row sum 2048x131072",
+    11: "many wide rows (_ws entry points: exchange kernels, row sum looped): softmax 4096x65536, "
+        "RMSNorm 2048x131072, residual LayerNorm 1024x65536, row sum 2048x131072",
 }
 CORE = (1, 2, 3, 4, 5)
-NEXT = (6, 7, 8, 9, 10)
-WS_WORKLOADS = (9,)  # run through the _ws entry points (caller workspace)
+NEXT = (6, 7, 8, 9, 10, 11)
+WS_WORKLOADS = (9, 11)  # run through the _ws entry points (caller workspace)
 WORKLOADS = {**synthetic.CORE_WORKLOADS, **synthetic.NEXT_WORKLOADS}
 
 
@@ -173,15 +175,6 @@ class CaseBuffers:
             R.rowred_row_sum_ws(self.x[k], self.y[k], ws)
         else:
             R.rowred_row_minmax_ws(self.x[k], self.y[k], self.y2[k], ws)
-
-
-def dispatches_per_call(case):
-    """Kernel dispatches one call of the case makes: the split path (the _ws
-    entry points beyond the register-resident window) runs statistics, merge
-    and, for matrix outputs, apply kernels."""
-    if case.cfg not in WS_WORKLOADS or (case.width + 3) // 4 <= 8192:  # aligned buffers: window = ceil(width/4)
-        return 1
-    return 2 if case.op in ("row_sum", "row_minmax") else 3
 
 
 def rotation_sets(case):
@@ -596,38 +589,50 @@ def _logged_hash(log_path):
     return "unknown"
 
 
+# Kernels of the library's reduction paths (the streaming copy aside).
+LIBRARY_KERNELS = ("rows_kernel", "seg_", "looped_kernel", "exchange_clear_kernel")
+
+
 def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=None):
     """Write profiles/pmc_traffic_cfg<N>.txt from the two counter passes of
     `bench.py --pmc --all`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     scaled by what each counter reads for the 256 MiB copy that ends each
     workload's pass."""
-    # one entry per reduction dispatch: a split call is 2 or 3 dispatches
-    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]
-                for _ in range(dispatches_per_call(c))]
+    # One call per case, each after a flush fill: the library dispatches
+    # between two other kernels are one call (1 to 3 dispatches).
+    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]]
     per_cfg = {}
     for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         i = 0
-        pending = []
+        pending = []   # calls since the last copy: [cfg, case, KiB, kernel names]
+        in_call = False
         for row in _csv_rows(path):
             if row["Counter_Name"] != ctr:
                 continue
             name = row["Kernel_Name"]
-            if "rows_kernel" in name or "seg_" in name or "looped_kernel" in name:
-                cfg, case = expected[i]
-                pending.append((cfg, case, float(row["Counter_Value"]), name))
-                i += 1
+            if any(k in name for k in LIBRARY_KERNELS):
+                if not in_call:
+                    if i >= len(expected):
+                        raise SystemExit(f"{path}: more calls than the {len(expected)} cases")
+                    pending.append([*expected[i], 0.0, []])
+                    i += 1
+                    in_call = True
+                pending[-1][2] += float(row["Counter_Value"])
+                short = name.replace("void rowred::(anonymous namespace)::", "").split("(")[0]
+                pending[-1][3].append(short)
             elif "copy_kernel" in name:
                 copy_kib = float(row["Counter_Value"])
-                for cfg, case, kib, kname in pending:
+                for cfg, case, kib, names in pending:
                     d = per_cfg.setdefault(cfg, {}).setdefault(f"{case.op} {case.rows}x{case.width}", {})
-                    d[ctr] = d.get(ctr, 0.0) + kib
+                    d[ctr] = kib
                     d[ctr + "_copy"] = copy_kib
-                    short = kname.replace("void rowred::(anonymous namespace)::", "").split("(")[0]
-                    if short not in d.setdefault("kernels", []):
-                        d["kernels"].append(short)
+                    d["kernels"] = names
                 pending = []
+                in_call = False
+            else:
+                in_call = False
         if i != len(expected):
-            raise SystemExit(f"{path}: found {i} reduction dispatches, expected {len(expected)}")
+            raise SystemExit(f"{path}: found {i} calls, expected {len(expected)}")
     copy_bytes = 2 ** 28  # each side of the calibration copy
     # the sources the counters were taken on (both passes must agree)
     h = _logged_hash(fetch_log)

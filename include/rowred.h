@@ -210,13 +210,21 @@ enum rowred_policy {
                                      walks the (row, segment) pairs in reverse order, so
                                      that it first reads again what the statistics kernel
                                      read last; measured no faster, never chosen */
-  ROWRED_POLICY_LOOPED = 64       /* rows of any width: lanes_per_row == threads, one row per
+  ROWRED_POLICY_LOOPED = 64,      /* rows of any width: lanes_per_row == threads, one row per
                                      workgroup, which walks the row in tiles of threads * chunks
                                      granules (chunks 2 or 4; LayerNorm 2) twice -- statistics
                                      with cached loads, then map and store (row sum and min/max:
                                      once).  NT_LOADS / NT_STORES apply to the second walk; no
                                      other bit may be set.  The entry points choose it for rows
                                      wider than 8192 granules */
+  ROWRED_POLICY_EXCHANGE = 128    /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
+                                     instead of three.  Each (row, segment) workgroup keeps its
+                                     segment in registers, publishes its statistics to the
+                                     workspace and waits for the row's other segments, so x (and
+                                     r) are read once.  Needs S <= 64; chunks may also be 8
+                                     (threads <= 512; not LayerNorm).
+                                     NT_LOADS / NT_STORES apply to its loads and stores;
+                                     REVERSE may not be set */
 };
 
 /*
@@ -279,15 +287,22 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
  * few-row shapes such as 7x1537 (section "Fixed-width GPU and dispatch
  * results").  The _ws entry points compute the same operators, same
  * arguments, for any width:
- *   - when the row fits the register-resident kernels they run those, and
- *     for rows wider than that with at least 2048 rows the looped kernels
- *     (ROWRED_POLICY_LOOPED) -- the workspace is then not touched;
+ *   - when the row fits the register-resident kernels they run those;
  *   - otherwise each row's window of 16-byte granules is cut into segments
- *     of T*C granules, one workgroup per (row, segment), in three kernels:
- *     per-segment statistics into the workspace, a fixed-order merge per row,
- *     and (LayerNorm, RMSNorm, softmax) an apply kernel that reads its
- *     segment again and writes it.  x (and r) are read twice, the second time
- *     from cache where it fits (the first pass uses cached loads).
+ *     of T*C granules, one workgroup per (row, segment).  LayerNorm, RMSNorm
+ *     and softmax rows that take at most 64 segments (up to about a million
+ *     columns) run the exchange kernels (ROWRED_POLICY_EXCHANGE): each
+ *     workgroup keeps its segment in registers, and the row's workgroups
+ *     swap their statistics through the workspace, so x (and r) are read
+ *     once;
+ *   - other rows wider than the register-resident window, with at least
+ *     2048 rows, run the looped kernels (ROWRED_POLICY_LOOPED) -- the
+ *     workspace is then not touched;
+ *   - the rest run three kernels: per-segment statistics into the
+ *     workspace, a fixed-order merge per row, and (LayerNorm, RMSNorm,
+ *     softmax) an apply kernel that reads its segment again and writes it.
+ *     x (and r) are read twice, the second time from cache where it fits
+ *     (the first pass uses cached loads).
  * Merges: LayerNorm combines per-segment (sum, sum of squares about the
  * segment mean) with the pairwise update of Chan, Golub and LeVeque, which is
  * exactly the biased two-pass variance about the row mean of "Residual
@@ -301,8 +316,13 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
  *
  * workspace: device memory of at least rowred_workspace_size() bytes,
  * 16-byte aligned, owned by the caller, not overlapping any operand; its
- * contents need no initialisation and are garbage afterwards.  Calls that
- * run concurrently need separate workspaces.  A NULL, misaligned or short
+ * contents need no initialisation (the exchange kernels' words are zeroed by
+ * a small kernel of their own, enqueued first) and are garbage afterwards.
+ * Calls that run concurrently need separate workspaces.  An exchange
+ * workgroup waits only for workgroups of its own row, which the hardware
+ * dispatches no later than those of later rows, so every wait ends; each is
+ * bounded all the same, and one that gives up (not observed) writes NaN to
+ * its row and a nonzero value to the workspace's first 8 bytes.  A NULL, misaligned or short
  * workspace -> ROWRED_ERR_INVALID_ARG when the split kernels are needed;
  * overlap -> ROWRED_ERR_ALIAS.  Everything else as for the entry points
  * above (sizes, alignment, aliasing, eps, stream, no allocation).
@@ -331,7 +351,7 @@ int rowred_row_minmax_ws(const float *x, float *out_min, float *out_max, int64_t
  * threads * chunks granules. */
 typedef struct rowred_split_plan {
   int32_t threads;         /* 64, 128, 256, 512 or 1024 */
-  int32_t chunks;          /* 1, 2 or 4 */
+  int32_t chunks;          /* 1, 2 or 4 (8 with ROWRED_POLICY_EXCHANGE) */
   int32_t policy;          /* ROWRED_POLICY_NT_LOADS / NT_STORES (apply kernel), ROWRED_POLICY_REVERSE */
   int32_t window;          /* derived: largest granule window of a row */
   int64_t block_rows;      /* rows per pass of the kernels (0: all rows in one pass, which the

@@ -35,6 +35,7 @@ ROWRED_POLICY_STAGE_STORES = 8
 ROWRED_POLICY_RELOAD = 16
 ROWRED_POLICY_REVERSE = 32
 ROWRED_POLICY_LOOPED = 64
+ROWRED_POLICY_EXCHANGE = 128
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1

@@ -412,18 +412,86 @@ void choose_split(int op, int64_t rows, int64_t width, rowred_split_plan *p) {
   p->policy = kPolicyNtLoads | kPolicyNtStores;
 }
 
+// Exchange geometry (one-kernel split rows), from sweeps of (threads, chunks)
+// x policy at 64x1048576, 1024x131072, 256x262144, 4096x65536, 2048x131072,
+// 1024x65536 and few-row shapes (7x1537, 16x32768, 64x65536, 8x65536), each
+// call on buffers rotated through >= 2 GiB.  A workgroup pays a fixed
+// latency (its loads, then the wait for its row's other segments) that only
+// more bytes per workgroup amortise:
+//   * 256 threads x 8 slots (RMSNorm, softmax) and 256 x 4 (LayerNorm, whose
+//     x and r need the registers) are best or within 4% at every wide shape;
+//     2 slots per lane were 1.5-2x slower;
+//   * rows too wide for 64 of those segments take 512 threads (LayerNorm
+//     512, then 1024);
+//   * rows narrower than two such segments take the first of 256 x 4,
+//     256 x 2, 128 x 2, 64 x 2 whose segment is at most half the row (else
+//     64 x 1): few-row shapes are latency bound and gain from more, shorter
+//     segments;
+//   * streaming loads and stores, as everywhere on rows read once.
+// `window`: the row's 16-byte granules (the x at hand's, or the worst phase's
+// for sizing).  False when no geometry cuts the row into at most
+// kMaxExchangeSegments.
+constexpr int kExchangeWide[2][3][2] = {{{256, 4}, {512, 4}, {1024, 4}},   // LayerNorm
+                                        {{256, 8}, {512, 8}, {0, 0}}};     // RMSNorm, softmax
+constexpr int kExchangeNarrow[][2] = {{256, 4}, {256, 2}, {128, 2}, {64, 2}, {64, 1}};
+
+bool choose_exchange(int op, int64_t window, rowred_split_plan *p) {
+  if (op > ROWRED_OP_SOFTMAX) return false;
+  const int64_t w = window;
+  const auto &wide = kExchangeWide[op == ROWRED_OP_LAYERNORM_RESIDUAL ? 0 : 1];
+  int T = 0, C = 0;
+  if (w >= 2 * (int64_t)wide[0][0] * wide[0][1]) {
+    for (const auto &g : wide) {
+      if (g[0] && (w + (int64_t)g[0] * g[1] - 1) / ((int64_t)g[0] * g[1]) <= kMaxExchangeSegments) {
+        T = g[0];
+        C = g[1];
+        break;
+      }
+    }
+    if (!T) return false;
+  } else {
+    T = 64;
+    C = 1;
+    for (const auto &g : kExchangeNarrow) {
+      if (2 * (int64_t)g[0] * g[1] <= w) {
+        T = g[0];
+        C = g[1];
+        break;
+      }
+    }
+  }
+  *p = rowred_split_plan{};
+  p->threads = T;
+  p->chunks = C;
+  p->policy = kPolicyExchange | kPolicyNtLoads | kPolicyNtStores;
+  return true;
+}
+
+// The split plan of a _ws call: exchange where it applies, else the three
+// split kernels.
+void choose_ws_split(int op, int64_t rows, int64_t width, int64_t window, rowred_split_plan *p) {
+  if (!choose_exchange(op, window, p)) choose_split(op, rows, width, p);
+}
+
 // Validate an explicit or chosen split plan and fill its derived fields.
 int finish_split(const Call &c, rowred_split_plan *p) {
   const int64_t T = p->threads;
   if (!is_pow2(T) || T < 64 || T > 1024) return ROWRED_ERR_INVALID_ARG;
-  if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4) return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~kSplitPolicyAll) return ROWRED_ERR_INVALID_ARG;
+  const bool exchange = (p->policy & kPolicyExchange) != 0;
+  if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4 && !(exchange && p->chunks == 8))
+    return ROWRED_ERR_INVALID_ARG;
+  if (exchange && (T > exchange_max_threads(p->chunks) || !exchange_kernel_exists(c.op, p->chunks)))
+    return ROWRED_ERR_INVALID_ARG;
+  if (exchange && ((p->policy & kPolicyReverse) || c.op > ROWRED_OP_SOFTMAX)) return ROWRED_ERR_INVALID_ARG;
   if (p->block_rows < 0) return ROWRED_ERR_INVALID_ARG;
   const int64_t G = T * p->chunks;
   const int64_t br = p->block_rows == 0 || p->block_rows > c.rows ? c.rows : p->block_rows;
   p->block_rows = br;
   p->window = c.window;
   p->segments = (c.window + G - 1) / G;
+  static_assert(kMaxExchangeSegments <= 64, "lane k of the smallest workgroup reads segment k's slot");
+  if (exchange && p->segments > kMaxExchangeSegments) return ROWRED_ERR_INVALID_ARG;
   if (p->segments > INT32_MAX || br > INT64_MAX / p->segments) return ROWRED_ERR_UNSUPPORTED;
   p->grid = br * p->segments;
   if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
@@ -470,7 +538,8 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
     a.rows = n;
     // kernel operator = the public op: LayerNorm (any of r, gamma, beta) 0,
     // RMSNorm 1, softmax 2, row sum 3, row min/max 4
-    const int err = launch_split(c.op, p.chunks, n * p.segments, p.threads, a, stream);
+    const int err = (p.policy & kPolicyExchange) ? launch_exchange(c.op, p.chunks, n * p.segments, p.threads, a, stream)
+                                                 : launch_split(c.op, p.chunks, n * p.segments, p.threads, a, stream);
     if (err != 0) return ROWRED_ERR_HIP;
   }
   return ROWRED_OK;
@@ -491,23 +560,28 @@ int check_ws_call(int op, const float *x, const float *r, const float *gamma, co
   return op == ROWRED_OP_LAYERNORM_RESIDUAL ? attach_affine(c, gamma, beta) : ROWRED_OK;
 }
 
-// Rows beyond the register-resident window: with at least this many rows
-// the looped kernels (one workgroup per row, no workspace) fill the chip and
-// beat the split kernels (softmax 4096x65536: 0.88x the time, residual
-// LayerNorm 1024x65536: 0.94x); with fewer the split kernels win, by up to
-// 6x on 16 rows (measured on MI355X).
+// Rows beyond the register-resident window where the exchange kernels do
+// not apply (row sum and min/max, or rows too wide): with at least this many
+// rows the looped kernels (one workgroup per row, no workspace) fill the chip
+// and beat the three split kernels (softmax 4096x65536: 0.88x the time,
+// residual LayerNorm 1024x65536: 0.94x); with fewer the split kernels win,
+// by up to 6x on 16 rows (measured on MI355X).  The exchange kernels beat
+// both on matrix outputs (4096x65536 softmax: 0.79x the looped time).
 constexpr int64_t kLoopedMinRows = 2048;
 
 // A _ws call: the register-resident kernels when the row fits them, the
-// looped kernels for many wide rows, else (or with an explicit split plan)
-// the split kernels.
+// exchange kernels for wider rows of the matrix operators, the looped
+// kernels for many wide rows, else (or with an explicit split plan) the
+// three split kernels.
 int ws_entry(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y, float *y2,
              int64_t rows, int64_t width, float eps, const rowred_split_plan *plan, void *ws, size_t ws_bytes,
              hipStream_t stream) {
   Call c;
   int st = check_ws_call(op, x, r, gamma, beta, y, y2, rows, width, eps, &c);
   if (st != ROWRED_OK || rows == 0 || width == 0) return st;
-  if (!plan && (c.window <= kMaxWindow || c.rows >= kLoopedMinRows)) {
+  rowred_split_plan sp;
+  const bool exchange = !plan && c.window > kMaxWindow && choose_exchange(op, c.window, &sp);
+  if (!plan && !exchange && (c.window <= kMaxWindow || c.rows >= kLoopedMinRows)) {
     rowred_plan p;
     choose_plan(c, &p);
     if (p.chunks >= 0) {
@@ -519,6 +593,8 @@ int ws_entry(int op, const float *x, const float *r, const float *gamma, const f
   rowred_split_plan p;
   if (plan) {
     p = *plan;
+  } else if (exchange) {
+    p = sp;
   } else {
     choose_split(op, rows, width, &p);
   }
@@ -610,10 +686,19 @@ ROWRED_API int rowred_workspace_size(int op, int64_t rows, int64_t width, size_t
   *bytes = 0;
   if (rows == 0 || width == 0) return ROWRED_OK;
   if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  // enough for the three split kernels and for the exchange kernels at the
+  // worst 16-byte phase of x.  (An x whose own window admits the exchange
+  // kernels where the worst phase does not needs fewer, wider segments than
+  // the three-kernel plan counted here.)
   rowred_split_plan p;
   choose_split(op, rows, width, &p);
-  const int64_t G = (int64_t)p.threads * p.chunks;
-  const int64_t S = (worst_window(width) + G - 1) / G;
+  int64_t G = (int64_t)p.threads * p.chunks;
+  int64_t S = (worst_window(width) + G - 1) / G;
+  if (choose_exchange(op, worst_window(width), &p)) {
+    G = (int64_t)p.threads * p.chunks;
+    const int64_t Sx = (worst_window(width) + G - 1) / G;
+    S = Sx > S ? Sx : S;
+  }
   if (rows > INT64_MAX / 16 / (S + 1)) return ROWRED_ERR_UNSUPPORTED;
   *bytes = (size_t)(rows * (S + 1) * 16);
   return ROWRED_OK;
@@ -668,7 +753,7 @@ ROWRED_API int rowred_split_plan_query(int op, const float *x, int64_t rows, int
   c.width = width;
   c.r_vec = c.y_vec = false;
   c.window = max_window(x, rows, width);
-  if (plan->threads == 0) choose_split(op, rows, width, plan);
+  if (plan->threads == 0) choose_ws_split(op, rows, width, c.window, plan);
   return finish_split(c, plan);
 }
 

@@ -119,11 +119,29 @@ struct SegArgs {
 constexpr int kSplitChunkSet[] = {1, 2, 4};
 constexpr int kNumSplitChunks = 3;
 constexpr int kPolicyReverse = ROWRED_POLICY_REVERSE;
-constexpr int kSplitPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyReverse;
+constexpr int kPolicyExchange = ROWRED_POLICY_EXCHANGE;
+constexpr int kSplitPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyReverse | kPolicyExchange;
+// The segments of a row wait for each other in the exchange kernel: at most
+// this many (no more than the smallest workgroup's threads, since lane k
+// reads segment k's slot).
+constexpr int kMaxExchangeSegments = 64;
+// Exchange kernels: 1, 2, 4 or 8 slots per lane; 8 slots in workgroups of at
+// most 512 threads (their registers), and not for LayerNorm, whose x, r and
+// x + r pair at 8 slots outgrow the register file.
+constexpr int kNumExchangeChunks = 4;
+constexpr int exchange_max_threads(int chunks) { return chunks >= 8 ? 512 : 1024; }
+constexpr bool exchange_kernel_exists(int op, int chunks) { return chunks != 8 || op != 0; }
 
 // Enqueue the statistics kernel (op: LayerNorm 0, RMSNorm 1, softmax 2, row
 // sum 3, row min/max 4) and then the apply (ops 0-2) or merge (ops 3-4)
 // kernel.  grid = rows * segments.  Returns the first launch's hipError_t.
 int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream);
+
+// One-kernel split rows (ROWRED_POLICY_EXCHANGE, ops 0-2): a clear kernel
+// zeroes exchange_words() 64-bit words of the workspace, then one workgroup
+// per (row, segment) keeps its segment in registers and swaps statistics
+// with its row's other segments through those words.
+int64_t exchange_words(int op, int64_t rows, int64_t segments);
+int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream);
 
 }  // namespace rowred

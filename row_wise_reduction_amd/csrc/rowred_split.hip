@@ -306,21 +306,11 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Apply the row record to one segment and store it.
+// Apply a row record to one segment held in registers and store it.
 // ---------------------------------------------------------------------------
 template <int OP, int C>
-__global__ void __launch_bounds__(1024) seg_apply_kernel(SegArgs a) {
-  const int T = blockDim.x;
-  int64_t row;
-  int seg;
-  segment_of(a, (a.policy & kPolicyReverse) != 0, row, seg);
-  const SegView v = make_view(a, row, seg, T, C);
-  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
-  f32x4 xv[C], rv[C];
-  if (a.policy & kPolicyNtLoads) load_segment<true, C>(a, v, has_r, xv, rv);
-  else load_segment<false, C>(a, v, has_r, xv, rv);
-  const Rec rr = row_records(a)[row];
-
+__device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, int64_t row, const f32x4 (&xv)[C],
+                                            const f32x4 (&rv)[C], Rec rr) {
   float s[4 * C];
   if constexpr (OP == kOpRms) {
     const float scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v0, a.inv_width, a.eps));
@@ -389,6 +379,220 @@ __global__ void __launch_bounds__(1024) seg_apply_kernel(SegArgs a) {
   else store(std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// Apply the row record to one segment and store it.
+// ---------------------------------------------------------------------------
+template <int OP, int C>
+__global__ void __launch_bounds__(1024) seg_apply_kernel(SegArgs a) {
+  const int T = blockDim.x;
+  int64_t row;
+  int seg;
+  segment_of(a, (a.policy & kPolicyReverse) != 0, row, seg);
+  const SegView v = make_view(a, row, seg, T, C);
+  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  f32x4 xv[C], rv[C];
+  if (a.policy & kPolicyNtLoads) load_segment<true, C>(a, v, has_r, xv, rv);
+  else load_segment<false, C>(a, v, has_r, xv, rv);
+  apply_store<OP, C>(a, v, row, xv, rv, row_records(a)[row]);
+}
+
+// ---------------------------------------------------------------------------
+// One-kernel split rows (ROWRED_POLICY_EXCHANGE).  Each workgroup keeps its
+// segment in registers; the S workgroups of a row swap their statistics
+// through the workspace, and each folds all S of them in the same fixed
+// order, so every segment applies bitwise the same row record and x (and r)
+// are read once.
+//
+// Workspace, 64-bit words: word 0 is a status word (nonzero after a wait
+// gave up), then one slot per (round, row, segment).  A slot holds 0 until
+// its owner publishes.  A published slot holds the complement of the value's
+// bits, NaN made canonical first, which is never 0; value and flag are one
+// word, so relaxed agent-scope atomics order them.  A clear kernel zeroes the
+// words before every launch.
+//
+// One exchange per kernel: RMSNorm publishes the segment's sum of squares;
+// softmax its pair (max m_k, sum of exp(x - m_k)) as two floats in one word;
+// LayerNorm two words, its sum of x + r and its sum of squares about its own
+// mean (slots of rounds 0 and 1), each waited for on its own.  The pairs and
+// the LayerNorm records merge as in the split kernels (Chan, Golub and
+// LeVeque for LayerNorm).
+//
+// Waiting on other workgroups needs them to run.  Workgroups reach each XCD
+// in index order and a row's segments have consecutive indices, so a
+// segment that is not yet resident waits only for workgroups of its own row
+// or of earlier rows, and earlier rows can all finish: the oldest waiting
+// row always completes.  S is capped (kMaxExchangeSegments) far below the
+// workgroups the chip holds at once.  Every wait is bounded all the same:
+// after kSpinLimit polls a lane gives up, sets the status word and the row
+// comes out NaN.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ uint64_t encode(double v) {
+  if (v != v) v = __builtin_nan("");
+  return ~__builtin_bit_cast(uint64_t, v);
+}
+__device__ __forceinline__ double decode(uint64_t w) { return __builtin_bit_cast(double, ~w); }
+__device__ __forceinline__ uint64_t encode_pair(float m, float s) {
+  if (m != m) m = __builtin_nanf("");
+  if (s != s) s = __builtin_nanf("");
+  return ~(((uint64_t)__builtin_bit_cast(uint32_t, s) << 32) | __builtin_bit_cast(uint32_t, m));
+}
+
+__device__ __forceinline__ uint64_t *exchange_slots(const SegArgs &a, int round, int64_t row) {
+  return reinterpret_cast<uint64_t *>(a.ws) + 1 + ((int64_t)round * a.rows + row) * a.segments;
+}
+
+__device__ __forceinline__ void publish(uint64_t *slot, uint64_t w) {
+  if (threadIdx.x == 0) __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane k < S of the workgroup waits for slot k and returns its word; other
+// lanes return 0 without touching memory.  A lane that gives up returns 0
+// (decoded: NaN) and raises the status word.
+__device__ __forceinline__ uint64_t await_slot(const SegArgs &a, const uint64_t *slots) {
+  const int k = threadIdx.x;
+  if (k >= a.segments) return 0;
+  uint64_t w = __hip_atomic_load(slots + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma nounroll
+  for (uint32_t it = 0; w == 0; ++it) {
+    if (it == kSpinLimit) {
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(a.ws), (uint64_t)1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    w = __hip_atomic_load(slots + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return w;
+}
+
+// Row sum of one published double per segment: every workgroup of the row
+// gets the same bits (same lanes, same reduction tree).
+__device__ __forceinline__ double exchange_sum(const SegArgs &a, const uint64_t *slots, double *partials) {
+  const bool mine = (int)threadIdx.x < a.segments;
+  const uint64_t w = await_slot(a, slots);
+  return row_allreduce<SumOp>(mine ? decode(w) : 0.0, a.lanes_log2, partials);
+}
+
+template <int OP, int C>
+__global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegArgs a) {
+  __shared__ float partials[4][16];
+  __shared__ double partials_d[2][16];
+  const int T = blockDim.x;
+  const int lanes_log2 = a.lanes_log2;
+  int64_t row;
+  int seg;
+  segment_of(a, false, row, seg);
+  const SegView v = make_view(a, row, seg, T, C);
+  const bool has_r = OP == kOpLayerNorm && a.r != nullptr;
+  f32x4 xv[C], rv[C];
+  if (a.policy & kPolicyNtLoads) load_segment<true, C>(a, v, has_r, xv, rv);
+  else load_segment<false, C>(a, v, has_r, xv, rv);
+
+  Rec rr;
+  if constexpr (OP == kOpRms) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = v.valid(c, j) ? xv[c][j] : 0.0f;
+        acc[j] = fmaf(x, x, acc[j]);
+      }
+    const float sq = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
+    uint64_t *slots = exchange_slots(a, 0, row);
+    publish(slots + seg, encode((double)sq));
+    rr = Rec{exchange_sum(a, slots, partials_d[0]), 0.0};
+  } else if constexpr (OP == kOpSoftmax) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, v.valid(c, j) ? xv[c][j] : -__builtin_inff());
+    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    // -inf entries weigh 0 even in a segment whose max is -inf; NaN and
+    // +inf entries give NaN, as in one pass.
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = xv[c][j];
+        const bool zero = !v.valid(c, j) || x == -__builtin_inff();
+        acc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
+      }
+    const float s = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[1]);
+    uint64_t *slots = exchange_slots(a, 0, row);
+    publish(slots + seg, encode_pair(m, s));
+    const bool mine = (int)threadIdx.x < a.segments;
+    const uint64_t w = ~await_slot(a, slots);
+    const float mk = mine ? __builtin_bit_cast(float, (uint32_t)w) : -__builtin_inff();
+    const float sk = mine ? __builtin_bit_cast(float, (uint32_t)(w >> 32)) : 0.0f;
+    const float mrow = row_allreduce<MaxOp>(mk, lanes_log2, partials[2]);
+    // An all -inf row has mrow = -inf and s_k = 0: 0 * exp(NaN) is NaN, and
+    // so is the row, as in one pass.
+    const float t = mine ? sk * __builtin_amdgcn_exp2f((mk - mrow) * kLog2e) : 0.0f;
+    rr = Rec{(double)mrow, (double)row_allreduce<SumOp>(t, lanes_log2, partials[3])};
+  } else {  // LayerNorm: (sum, squares about the segment mean), merged as the split kernels merge them
+    float hi[4 * C], lo[4 * C];
+    two_sum<C>(v, xv, rv, hi, lo);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * C; ++i) {
+      acc[i & 3] += (double)hi[i];
+      acc_lo += lo[i];
+    }
+    const double sum =
+        row_allreduce<SumOp>(((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo, lanes_log2, partials_d[0]);
+    const int64_t G = (int64_t)T * C;
+    const int64_t n = segment_count(seg, G, v.off, a.width);
+    const double seg_mean = n > 0 ? sum / (double)n : 0.0;
+    const float s_hi = (float)seg_mean;
+    const float s_lo = (float)(seg_mean - (double)s_hi);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        const float d = v.valid(c, j) ? (hi[i] - s_hi) + (lo[i] - s_lo) : 0.0f;
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+    const float m2 = row_allreduce<SumOp>((sq[0] + sq[1]) + (sq[2] + sq[3]), lanes_log2, partials[0]);
+    uint64_t *slots0 = exchange_slots(a, 0, row);
+    uint64_t *slots1 = exchange_slots(a, 1, row);
+    publish(slots0 + seg, encode(sum));
+    publish(slots1 + seg, encode((double)m2));
+    // Both words of segment k, each written once: wait for each.
+    const int k = threadIdx.x;
+    const bool mine = k < a.segments;
+    const double sum_k = decode(await_slot(a, slots0));
+    const double m2_k = decode(await_slot(a, slots1));
+    const double mean = row_allreduce<SumOp>(mine ? sum_k : 0.0, lanes_log2, partials_d[1]) / (double)a.width;
+    const int64_t n_k = mine ? segment_count(k, G, v.off, a.width) : 0;
+    double t = 0.0;
+    if (n_k > 0) {
+      const double dm = sum_k / (double)n_k - mean;
+      t = m2_k + (double)n_k * dm * dm;
+    } else if (mine) {
+      t = m2_k + sum_k;  // 0 + 0, but a wait that gave up still turns the row NaN
+    }
+    // partials_d[0] again: every wave read it before the barrier that
+    // partials_d[1]'s reduction passed.
+    rr = Rec{mean, row_allreduce<SumOp>(t, lanes_log2, partials_d[0])};
+  }
+  apply_store<OP, C>(a, v, row, xv, rv, rr);
+}
+
+// Zero the status word and the slots (n64 words, 16-byte aligned, n64 even).
+__global__ void __launch_bounds__(256) exchange_clear_kernel(uint64_t *w, int64_t n128) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  if (i < n128) reinterpret_cast<u64x2 *>(w)[i] = u64x2{0, 0};
+}
+
 using SegFn = void (*)(SegArgs);
 
 #define ROWRED_SPLIT_ROW(K, OP) {K<OP, 1>, K<OP, 2>, K<OP, 4>}
@@ -403,14 +607,46 @@ const SegFn kApply[3][kNumSplitChunks] = {
     ROWRED_SPLIT_ROW(seg_apply_kernel, kOpSoftmax),
 };
 #undef ROWRED_SPLIT_ROW
+#define ROWRED_EXCHANGE_ROW(OP) \
+  {seg_exchange_kernel<OP, 1>, seg_exchange_kernel<OP, 2>, seg_exchange_kernel<OP, 4>, seg_exchange_kernel<OP, 8>}
+const SegFn kExchange[3][kNumExchangeChunks] = {
+    {seg_exchange_kernel<kOpLayerNorm, 1>, seg_exchange_kernel<kOpLayerNorm, 2>, seg_exchange_kernel<kOpLayerNorm, 4>,
+     nullptr},
+    ROWRED_EXCHANGE_ROW(kOpRms),
+    ROWRED_EXCHANGE_ROW(kOpSoftmax),
+};
+#undef ROWRED_EXCHANGE_ROW
 const SegFn kMerge[5] = {seg_merge_kernel<kOpLayerNorm>, seg_merge_kernel<kOpRms>, seg_merge_kernel<kOpSoftmax>,
                          seg_merge_kernel<kOpRowSum>, seg_merge_kernel<kOpRowMinMax>};
 static_assert(kNumSplitChunks == 3 && kSplitChunkSet[0] == 1 && kSplitChunkSet[1] == 2 && kSplitChunkSet[2] == 4,
               "split kernel tables follow kSplitChunkSet");
 
 constexpr int kMergeThreads = 256;  // four rows (wavefronts) per workgroup
+constexpr int kClearThreads = 256;
 
 }  // namespace
+
+int64_t exchange_words(int op, int64_t rows, int64_t segments) {
+  return 1 + (op == kOpLayerNorm ? 2 : 1) * rows * segments;
+}
+
+int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {
+  const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : chunks == 8 ? 3 : -1;
+  if (op < 0 || op > 2 || ci < 0 || !exchange_kernel_exists(op, chunks) || threads > exchange_max_threads(chunks) ||
+      args.segments > threads || args.segments > kMaxExchangeSegments)
+    return (int)hipErrorInvalidValue;
+  uint64_t *w = reinterpret_cast<uint64_t *>(args.ws);
+  int64_t n128 = (exchange_words(op, args.rows, args.segments) + 1) / 2;
+  void *clear_params[] = {&w, &n128};
+  int err = (int)hipLaunchKernel(reinterpret_cast<const void *>(exchange_clear_kernel),
+                                 dim3((uint32_t)((n128 + kClearThreads - 1) / kClearThreads)), dim3(kClearThreads),
+                                 clear_params, 0, stream);
+  if (err) return err;
+  SegArgs a = args;
+  void *params[] = {&a};
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(kExchange[op][ci]), dim3((uint32_t)grid),
+                              dim3(threads), params, 0, stream);
+}
 
 int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {
   const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : -1;

@@ -79,7 +79,8 @@ CORE_WORKLOADS = {
 # the row sum / paired min-max reductions at a wide and a short ragged shape,
 # rows beyond one workgroup's registers (1M, 128K, 256K and 4M columns) plus
 # the pages' few-row shape 7x1537 through the workspace entry points, and
-# many wide rows (64K and 128K columns) through the plain entry points.
+# many wide rows (64K and 128K columns) through the plain entry points and,
+# at the same shapes, through the workspace entry points.
 NEXT_WORKLOADS = {
     6: [Case(6, "layernorm", 1024, 4096, "uniform"), Case(6, "layernorm", 16384, 8192, "uniform")],
     7: [Case(7, "layernorm_affine", 1024, 4096, "uniform"), Case(7, "layernorm_affine", 16384, 8192, "uniform")],
@@ -90,6 +91,8 @@ NEXT_WORKLOADS = {
         Case(9, "softmax", 7, 1537, "normal")],
     10: [Case(10, "softmax", 4096, 1 << 16, "normal"), Case(10, "rmsnorm", 2048, 1 << 17, "uniform"),
          Case(10, "layernorm_residual", 1024, 1 << 16, "uniform"), Case(10, "row_sum", 2048, 1 << 17, "uniform")],
+    11: [Case(11, "softmax", 4096, 1 << 16, "normal"), Case(11, "rmsnorm", 2048, 1 << 17, "uniform"),
+         Case(11, "layernorm_residual", 1024, 1 << 16, "uniform"), Case(11, "row_sum", 2048, 1 << 17, "uniform")],
 }
 
 

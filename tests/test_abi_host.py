@@ -355,7 +355,15 @@ def test_workspace_size_covers_every_alignment(op, rows, width):
         assert p.window == window(X + 4 * mis, rows, width)
         assert p.segments == -(-p.window // G) and p.grid == rows * p.segments
         assert p.workspace_bytes == (p.grid + rows) * 16 <= need
-        assert p.threads in (64, 128, 256, 512, 1024) and p.chunks in (1, 2, 4)
+        assert p.threads in (64, 128, 256, 512, 1024)
+        if p.policy & R.ROWRED_POLICY_EXCHANGE:
+            # LayerNorm, RMSNorm and softmax rows of at most 64 segments
+            assert op in ("layernorm_residual", "rmsnorm", "softmax") and p.segments <= 64
+            assert p.chunks in ((1, 2, 4) if op == "layernorm_residual" else (1, 2, 4, 8))
+        else:
+            assert p.chunks in (1, 2, 4)
+            if op in ("layernorm_residual", "rmsnorm", "softmax"):
+                assert p.window > 64 * 4096  # no exchange geometry fits
         # the chooser never cuts a row into segments wider than the row, unless
         # the smallest one already is
         assert G <= max(p.window + 3, 64)
@@ -381,6 +389,57 @@ def test_split_plan_rejects(kw):
     assert e.value.status == R.ROWRED_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("op,width,kw", [
+    ("row_sum", 100000, {}), ("row_minmax", 100000, {}),                    # matrix operators only
+    ("softmax", 100000, dict(policy=R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_REVERSE)),
+    ("softmax", 4 * 1024 * 4 * 64 + 4, dict(threads=1024, chunks=4)),        # S = 65 > 64
+    ("rmsnorm", 4 * 64 * 2 * 70, dict(threads=64, chunks=2)),                # S = 70
+    ("softmax", 100000, dict(threads=1024, chunks=8)),                       # 8 slots: <= 512 threads
+    ("layernorm_residual", 100000, dict(threads=256, chunks=8)),             # LayerNorm: <= 4 slots
+])
+def test_exchange_plan_rejects(op, width, kw):
+    base = dict(threads=256, chunks=2, policy=R.ROWRED_POLICY_EXCHANGE)
+    base.update(kw)
+    base["policy"] |= R.ROWRED_POLICY_EXCHANGE
+    with pytest.raises(R.RowRedError) as e:
+        R.rowred_split_plan_query(op, X, 8, width, plan=R.SplitPlan(**base))
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("op", ["layernorm_residual", "rmsnorm", "softmax"])
+@pytest.mark.parametrize("T,C", [(64, 1), (256, 2), (1024, 4), (512, 8)])
+def test_exchange_plan_limits(op, T, C):
+    """The largest row an exchange plan takes: 64 segments."""
+    if C == 8 and op == "layernorm_residual":
+        return
+    S = 64
+    width = 4 * T * C * S - 3  # worst phase: window = S * T * C granules
+    plan = R.rowred_split_plan_query(op, X, 8, width, plan=R.SplitPlan(threads=T, chunks=C,
+                                                                         policy=R.ROWRED_POLICY_EXCHANGE))
+    assert plan.segments == S
+    # the exchange words fit the workspace the three-kernel path needs
+    assert (1 + 2 * 8 * S) * 8 <= plan.workspace_bytes
+
+
+@pytest.mark.parametrize("op,rows,width,want", [
+    ("softmax", 4096, 1 << 16, (256, 8, 8)), ("rmsnorm", 2048, 1 << 17, (256, 8, 16)),
+    ("layernorm_residual", 1024, 1 << 16, (256, 4, 16)), ("layernorm_residual", 256, 1 << 18, (256, 4, 64)),
+    ("rmsnorm", 1024, 1 << 18, (256, 8, 32)), ("rmsnorm", 64, 1 << 19, (256, 8, 64)), ("rmsnorm", 64, 600000, (512, 8, 37)), ("softmax", 64, 1 << 20, (512, 8, 64)),
+    ("layernorm_residual", 16, 1 << 20, (1024, 4, 64)), ("softmax", 7, 1537, (64, 2, 4)),
+    ("softmax", 16, 32768, (256, 8, 4)),
+])
+def test_ws_split_plan_choice(op, rows, width, want):
+    """The _ws entry points' split plans: exchange geometries from the sweep;
+    one phase off 16 bytes, a row of 2^20 floats spans 262145 granules, one
+    more than 64 segments of 4096 hold, and falls back to the three kernels."""
+    p = R.rowred_split_plan_query(op, X, rows, width)
+    assert (p.threads, p.chunks, p.segments) == want
+    assert p.policy == R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES
+    if width == 1 << 20 and op != "layernorm_residual":
+        q = R.rowred_split_plan_query(op, X + 4, rows, width)
+        assert not q.policy & R.ROWRED_POLICY_EXCHANGE and q.segments > 64
+
+
 def test_ws_entry_argument_checks():
     lib = R.lib()
     W = 0x7F6000000000  # a workspace address far from the operands
@@ -391,7 +450,9 @@ def test_ws_entry_argument_checks():
     # no, misaligned or short workspace
     assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), None, 0, None) == R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), W + 8, need, None) == R.ROWRED_ERR_INVALID_ARG
-    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), W, need - 16, None) == R.ROWRED_ERR_INVALID_ARG
+    chosen = R.rowred_split_plan_query("rmsnorm", X, rows, width).workspace_bytes
+    assert chosen <= need
+    assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), W, chosen - 16, None) == R.ROWRED_ERR_INVALID_ARG
     # workspace inside x, inside y
     assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), X + 4096, need, None) == R.ROWRED_ERR_ALIAS
     assert lib.rowred_rmsnorm_ws(X, Y, rows, width, f(1e-6), Y, need, None) == R.ROWRED_ERR_ALIAS

@@ -131,29 +131,49 @@ def test_full_size_wide_rows(case):
     t.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("op", ["rmsnorm", "softmax", "row_minmax"])
+@pytest.mark.parametrize("op", ["row_sum", "row_minmax"])
 def test_ws_entry_loops_many_wide_rows(op):
     """2048 rows beyond the register-resident window: the _ws entry points
-    run the looped kernels and never touch the workspace (None is fine)."""
+    of the row reductions run the looped kernels and never touch the
+    workspace (None is fine)."""
     t = torch()
     rows, width = 2048, 33001
     x = synthetic.random_matrix(77, rows, width, "normal")
     xd = shifted_input(x, 1)
+    lo = t.empty(rows, device="cuda")
+    hi = t.empty(rows, device="cuda")
     if op == "row_minmax":
-        lo = t.empty(rows, device="cuda")
-        hi = t.empty(rows, device="cuda")
         R.rowred_row_minmax_ws(xd, lo, hi, None)
         t.cuda.synchronize()
         got = (lo.cpu().numpy(), hi.cpu().numpy())
-        ref = reference(op, x, None, None, None)
-        check(op, got, ref, "ws looped minmax")
-        return
-    y = t.empty(rows, width, device="cuda")
-    if op == "rmsnorm":
-        R.rowred_rmsnorm_ws(xd, y, None, eps=1e-6)
     else:
-        R.rowred_softmax_ws(xd, y, None)
+        R.rowred_row_sum_ws(xd, lo, None)
+        t.cuda.synchronize()
+        got = lo.cpu().numpy()
+    check(op, got, reference(op, x, None, None, None), f"ws looped {op}")
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_ws_entry_needs_workspace_for_matrix_outputs(op):
+    """Same shape, matrix operators: the _ws entry points run the exchange
+    kernels, which need the workspace (None is an invalid argument)."""
+    t = torch()
+    rows, width = 2048, 33001
+    x = synthetic.random_matrix(78, rows, width, "normal")
+    xd = shifted_input(x, 1)
+    y = t.empty(rows, width, device="cuda")
+    with pytest.raises(R.RowRedError) as e:
+        if op == "rmsnorm":
+            R.rowred_rmsnorm_ws(xd, y, None, eps=1e-6)
+        else:
+            R.rowred_softmax_ws(xd, y, None)
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+    ws = R.new_workspace(op, rows, width)
+    if op == "rmsnorm":
+        R.rowred_rmsnorm_ws(xd, y, ws, eps=1e-6)
+    else:
+        R.rowred_softmax_ws(xd, y, ws)
     t.cuda.synchronize()
     yh = y.cpu().numpy()
     for i in (0, 1, 1024, 2047):
-        check(op, yh[i:i + 1], reference(op, x[i:i + 1], None, None, None), f"ws looped {op} row {i}")
+        check(op, yh[i:i + 1], reference(op, x[i:i + 1], None, None, None), f"ws exchange {op} row {i}")

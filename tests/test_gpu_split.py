@@ -184,10 +184,12 @@ def test_deterministic_and_workspace_reuse(op):
     assert np.array_equal(np.asarray(first).view(np.uint32), np.asarray(again).view(np.uint32))
 
 
-@pytest.mark.parametrize("case", synthetic.NEXT_WORKLOADS.get(9, []), ids=lambda c: c.name)
+@pytest.mark.parametrize("case", synthetic.NEXT_WORKLOADS.get(9, []) + synthetic.NEXT_WORKLOADS.get(11, []),
+                         ids=lambda c: c.name)
 def test_wide_workloads_full_size(case):
-    """The wide-row and few-row workload shapes at full size through the _ws
-    entry point; sampled rows against the oracle."""
+    """The wide-row, few-row and many-wide-row workload shapes at full size
+    through the _ws entry point (exchange, three-kernel or looped path, as
+    the chooser picks); sampled rows against the oracle."""
     t = torch()
     print_case(case.name)
     x = synthetic.case_input(case, "x")

@@ -56,8 +56,10 @@ def test_every_kernel_is_spill_free(asm):
     # five operators, affine LayerNorm (no 16-chunk kernel), the reload
     # variant of the three matrix operators at 1-8 chunks, copy; split rows:
     # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
-    # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9
+    # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only),
+    # the exchange kernels (3 operators x 4 chunk counts, LayerNorm not at 8)
+    # and their clear kernel
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -213,3 +215,29 @@ def test_looped_kernels(asm):
         assert body.count("s_barrier") == {0: 2, 1: 1, 2: 2, 3: 1, 4: 1}[op], dn
     assert seen == 9
 
+
+
+def test_exchange_kernels(asm):
+    """Exchange kernels: a non-temporal and a cached copy of the segment
+    loads; the statistics leave and arrive through 8-byte agent-scope (sc1)
+    stores and loads, with a sleep in the wait; no cache write-back or
+    invalidate instruction (value and flag share one word, so relaxed atomics
+    suffice); one cross-wave fold per reduction."""
+    seen = 0
+    for name in kernel_meta(asm):
+        dn = demangle(name)
+        if "seg_exchange_kernel<" not in dn:
+            continue
+        seen += 1
+        body = kernel_body(asm, name)
+        op = int(dn.split("seg_exchange_kernel<")[1].split(",")[0])
+        nt, cached = x4_loads(body)
+        assert nt > 0 and cached >= nt, (dn, nt, cached)
+        lines = [ln.strip() for ln in body.splitlines()]
+        assert any(ln.startswith("global_store_dwordx2") and ln.endswith("sc1") for ln in lines), dn
+        assert any(ln.startswith("global_load_dwordx2") and ln.endswith("sc1") for ln in lines), dn
+        assert "s_sleep" in body and "buffer_wbl2" not in body and "buffer_inv" not in body, dn
+        # RMSNorm: segment sum + exchanged sum; softmax: max, sum, exchanged max
+        # and sum; LayerNorm: sum, squares, exchanged sum and squares
+        assert body.count("s_barrier") == {0: 4, 1: 2, 2: 4}[op], (dn, body.count("s_barrier"))
+    assert seen == 11
