@@ -221,7 +221,8 @@ enum rowred_policy {
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the
                                      workspace and waits for the row's other segments, so x (and
-                                     r) are read once.  Needs S <= 64; chunks may also be 8
+                                     r) are read once.  Needs S <= 128 and S <= threads;
+                                     chunks may also be 8
                                      (threads <= 512; not LayerNorm).
                                      NT_LOADS / NT_STORES apply to its loads and stores;
                                      REVERSE may not be set */

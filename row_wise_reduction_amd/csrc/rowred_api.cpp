@@ -431,6 +431,10 @@ void choose_split(int op, int64_t rows, int64_t width, rowred_split_plan *p) {
 // `window`: the row's 16-byte granules (the x at hand's, or the worst phase's
 // for sizing).  False when no geometry cuts the row into at most
 // kMaxExchangeSegments.
+// More, shorter segments per row measured slower: 256 x 8 at 128 segments
+// was 15% behind 512 x 8 at 64 on 64x1048576 softmax.  Keeping a row's
+// segments on one XCD was 25-60% slower everywhere.
+constexpr int64_t kExchangeChosenSegments = 64;
 constexpr int kExchangeWide[2][3][2] = {{{256, 4}, {512, 4}, {1024, 4}},   // LayerNorm
                                         {{256, 8}, {512, 8}, {0, 0}}};     // RMSNorm, softmax
 constexpr int kExchangeNarrow[][2] = {{256, 4}, {256, 2}, {128, 2}, {64, 2}, {64, 1}};
@@ -442,7 +446,8 @@ bool choose_exchange(int op, int64_t window, rowred_split_plan *p) {
   int T = 0, C = 0;
   if (w >= 2 * (int64_t)wide[0][0] * wide[0][1]) {
     for (const auto &g : wide) {
-      if (g[0] && (w + (int64_t)g[0] * g[1] - 1) / ((int64_t)g[0] * g[1]) <= kMaxExchangeSegments) {
+      const int64_t S = g[0] ? (w + (int64_t)g[0] * g[1] - 1) / ((int64_t)g[0] * g[1]) : 0;
+      if (g[0] && S <= kExchangeChosenSegments && S <= g[0]) {
         T = g[0];
         C = g[1];
         break;
@@ -490,8 +495,8 @@ int finish_split(const Call &c, rowred_split_plan *p) {
   p->block_rows = br;
   p->window = c.window;
   p->segments = (c.window + G - 1) / G;
-  static_assert(kMaxExchangeSegments <= 64, "lane k of the smallest workgroup reads segment k's slot");
-  if (exchange && p->segments > kMaxExchangeSegments) return ROWRED_ERR_INVALID_ARG;
+  // lane k of the workgroup reads segment k's slot
+  if (exchange && (p->segments > kMaxExchangeSegments || p->segments > T)) return ROWRED_ERR_INVALID_ARG;
   if (p->segments > INT32_MAX || br > INT64_MAX / p->segments) return ROWRED_ERR_UNSUPPORTED;
   p->grid = br * p->segments;
   if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;

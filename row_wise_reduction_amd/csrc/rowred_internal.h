@@ -121,10 +121,13 @@ constexpr int kNumSplitChunks = 3;
 constexpr int kPolicyReverse = ROWRED_POLICY_REVERSE;
 constexpr int kPolicyExchange = ROWRED_POLICY_EXCHANGE;
 constexpr int kSplitPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyReverse | kPolicyExchange;
-// The segments of a row wait for each other in the exchange kernel: at most
-// this many (no more than the smallest workgroup's threads, since lane k
-// reads segment k's slot).
-constexpr int kMaxExchangeSegments = 64;
+// The segments of a row wait for each other in the exchange kernel, so all
+// of a row's segments must fit on the chip at once.  Every CU holds at least
+// one workgroup of any allowed size (launch bounds keep 1024-thread kernels
+// within 128 VGPRs): 32 per XCD, 256 in all.  Dealt round robin over the 8
+// XCDs, a row of at most 128 segments needs 16 per XCD.  Lane k reads
+// segment k's slot, so S is also at most the workgroup's threads.
+constexpr int kMaxExchangeSegments = 128;
 // Exchange kernels: 1, 2, 4 or 8 slots per lane; 8 slots in workgroups of at
 // most 512 threads (their registers), and not for LayerNorm, whose x, r and
 // x + r pair at 8 slots outgrow the register file.

@@ -308,7 +308,8 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
 // ---------------------------------------------------------------------------
 // Apply a row record to one segment held in registers and store it.
 // ---------------------------------------------------------------------------
-template <int OP, int C>
+// PAIR (LayerNorm): xv and rv already hold the TwoSum pair (hi, lo) of x + r.
+template <int OP, int C, bool PAIR = false>
 __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, int64_t row, const f32x4 (&xv)[C],
                                             const f32x4 (&rv)[C], Rec rr) {
   float s[4 * C];
@@ -331,7 +332,17 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
     const float m_lo = (float)(mean - (double)m_hi);
     const float rstd = __builtin_amdgcn_rsqf(fmaf((float)rr.v1, a.inv_width, a.eps));
     float hi[4 * C], lo[4 * C];
-    two_sum<C>(v, xv, rv, hi, lo);
+    if constexpr (PAIR) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hi[4 * c + j] = xv[c][j];
+          lo[4 * c + j] = rv[c][j];
+        }
+    } else {
+      two_sum<C>(v, xv, rv, hi, lo);
+    }
     const bool affine = a.gamma != nullptr || a.beta != nullptr;
     const int emax = a.width - 1;
 #pragma unroll
@@ -537,6 +548,14 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
   } else {  // LayerNorm: (sum, squares about the segment mean), merged as the split kernels merge them
     float hi[4 * C], lo[4 * C];
     two_sum<C>(v, xv, rv, hi, lo);
+    // from here on the segment lives as the pair: x and r are dropped
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[c][j] = hi[4 * c + j];
+        rv[c][j] = lo[4 * c + j];
+      }
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     float acc_lo = 0.0f;
 #pragma unroll
@@ -583,7 +602,7 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
     // partials_d[1]'s reduction passed.
     rr = Rec{mean, row_allreduce<SumOp>(t, lanes_log2, partials_d[0])};
   }
-  apply_store<OP, C>(a, v, row, xv, rv, rr);
+  apply_store<OP, C, OP == kOpLayerNorm>(a, v, row, xv, rv, rr);
 }
 
 // Zero the status word and the slots (n64 words, 16-byte aligned, n64 even).

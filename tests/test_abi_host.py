@@ -392,13 +392,14 @@ def test_split_plan_rejects(kw):
 @pytest.mark.parametrize("op,width,kw", [
     ("row_sum", 100000, {}), ("row_minmax", 100000, {}),                    # matrix operators only
     ("softmax", 100000, dict(policy=R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_REVERSE)),
-    ("softmax", 4 * 1024 * 4 * 64 + 4, dict(threads=1024, chunks=4)),        # S = 65 > 64
-    ("rmsnorm", 4 * 64 * 2 * 70, dict(threads=64, chunks=2)),                # S = 70
+    ("softmax", 4 * 1024 * 4 * 128 + 4, dict(threads=1024, chunks=4)),       # S = 129 > 128
+    ("rmsnorm", 4 * 64 * 2 * 70, dict(threads=64, chunks=2)),                # S = 70 > 64 threads
+    ("rmsnorm", 100000, dict(policy=R.ROWRED_POLICY_XCD_REMAP)),              # no XCD remap
     ("softmax", 100000, dict(threads=1024, chunks=8)),                       # 8 slots: <= 512 threads
     ("layernorm_residual", 100000, dict(threads=256, chunks=8)),             # LayerNorm: <= 4 slots
 ])
 def test_exchange_plan_rejects(op, width, kw):
-    base = dict(threads=256, chunks=2, policy=R.ROWRED_POLICY_EXCHANGE)
+    base = dict(threads=256, chunks=2, policy=0)
     base.update(kw)
     base["policy"] |= R.ROWRED_POLICY_EXCHANGE
     with pytest.raises(R.RowRedError) as e:
@@ -409,10 +410,11 @@ def test_exchange_plan_rejects(op, width, kw):
 @pytest.mark.parametrize("op", ["layernorm_residual", "rmsnorm", "softmax"])
 @pytest.mark.parametrize("T,C", [(64, 1), (256, 2), (1024, 4), (512, 8)])
 def test_exchange_plan_limits(op, T, C):
-    """The largest row an exchange plan takes: 64 segments."""
+    """The largest row an exchange plan takes: 128 segments, at most one per
+    thread."""
     if C == 8 and op == "layernorm_residual":
         return
-    S = 64
+    S = min(128, T)
     width = 4 * T * C * S - 3  # worst phase: window = S * T * C granules
     plan = R.rowred_split_plan_query(op, X, 8, width, plan=R.SplitPlan(threads=T, chunks=C,
                                                                          policy=R.ROWRED_POLICY_EXCHANGE))

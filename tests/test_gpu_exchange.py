@@ -45,12 +45,13 @@ def run_exchange(op, x, r, g, b, plan, shift=0):
 @pytest.mark.parametrize("geom", GEOMETRIES, ids=lambda g: f"T{g[0]}C{g[1]}")
 @pytest.mark.parametrize("op", MATRIX_OPS)
 def test_every_exchange_geometry(op, geom):
-    """One, three and the most (64) segments per row; ragged, misaligned."""
+    """One, three, 32 and the most (min(128, T)) segments per row; ragged,
+    misaligned."""
     T, C = geom
     if C == 8 and op.startswith("layernorm"):
         pytest.skip("LayerNorm exchanges at up to 4 chunks")
     G = T * C
-    for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 64 - 9, 2)):
+    for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 32 - 5, 1), (4 * G * min(128, T) - 9, 2)):
         rows = max(2, min(6, (1 << 21) // width))
         x, r, g, b = make_inputs(op, rows, width, seed=11 * width + T + C)
         ref = reference(op, x, r, g, b)
