@@ -757,7 +757,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
-    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-10)")
+    ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-11)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
     ap.add_argument("--reload", action="store_true",
