@@ -589,6 +589,13 @@ def _logged_hash(log_path):
     return "unknown"
 
 
+def kernel_short_name(name):
+    """A library kernel's name without return type and namespaces."""
+    if name.startswith("void "):
+        name = name[5:]
+    return name.replace("rowred::(anonymous namespace)::", "")
+
+
 # Kernels of the library's reduction paths (the streaming copy aside).
 LIBRARY_KERNELS = ("rows_kernel", "seg_", "looped_kernel", "exchange_clear_kernel")
 
@@ -618,7 +625,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
                     i += 1
                     in_call = True
                 pending[-1][2] += float(row["Counter_Value"])
-                short = name.replace("void rowred::(anonymous namespace)::", "").split("(")[0]
+                short = kernel_short_name(name).split("(")[0]
                 pending[-1][3].append(short)
             elif "copy_kernel" in name:
                 copy_kib = float(row["Counter_Value"])
@@ -739,7 +746,7 @@ def trace_summary(stats_csv, bench_json, out_path):
              f"# kernel_source_hash: {b.get('kernel_source_hash', 'unknown')}",
              "# name | calls | total_ns | average_ns | min_ns | max_ns | percentage"]
     for r in rows:
-        nm = r["Name"].replace("void rowred::(anonymous namespace)::", "")
+        nm = kernel_short_name(r["Name"])
         lines.append(" | ".join([nm, r["Calls"], r["TotalDurationNs"], f"{float(r['AverageNs']):.0f}",
                                  r["MinNs"], r["MaxNs"], f"{float(r['Percentage']):.2f}"]))
     lines.append("# benchmark (same command without the profiler): HIP-event average per call")
