@@ -260,6 +260,14 @@ int rowred_row_reduce_run_plan(int op, const float *x, float *out0, float *out1,
                                int64_t rows, int64_t width,
                                const rowred_plan *plan, hipStream_t stream);
 
+/* Host-only: the plan rowred_layernorm would launch for these arguments
+ * (pointers are only inspected for alignment and overlap; r, gamma, beta may
+ * be NULL).  Affine LayerNorm (gamma or beta given) has geometry rules of its
+ * own, so rowred_plan_query does not cover it.  Same status as
+ * rowred_layernorm would return before launching. */
+int rowred_layernorm_plan_query(const float *x, const float *r, const float *gamma, const float *beta,
+                                const float *y, int64_t rows, int64_t width, rowred_plan *out);
+
 /* rowred_layernorm with an explicit plan (as rowred_run_plan). */
 int rowred_layernorm_run_plan(const float *x, const float *r, const float *gamma,
                               const float *beta, float *y, int64_t rows,

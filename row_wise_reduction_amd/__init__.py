@@ -126,6 +126,7 @@ def lib():
             "rowred_layernorm_run_plan": [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
             "rowred_softmax": [_P, _P, _I64, _I64, _P],
             "rowred_plan_query": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan)],
+            "rowred_layernorm_plan_query": [_P, _P, _P, _P, _P, _I64, _I64, ctypes.POINTER(_Plan)],
             "rowred_run_plan": [ctypes.c_int, _P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.POINTER(_Plan), _P],
             "rowred_copy": [_P, _P, _I64, _P],
             "rowred_row_sum": [_P, _P, _I64, _I64, _P],
@@ -254,6 +255,18 @@ def rowred_layernorm_run_plan(x, r, gamma, beta, y, plan: "Plan", rows=None, wid
                                          my[0], rows, width, float(eps), ctypes.byref(c),
                                          _stream(stream, x, r, gamma, beta, y))
     _check(st, "rowred_layernorm_run_plan")
+
+
+def rowred_layernorm_plan_query(x, r, gamma, beta, y, rows=None, width=None) -> "Plan":
+    """The plan rowred_layernorm would launch (host only; no device work)."""
+    mx, mr, my = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width), _matrix(y, "y", rows, width)
+    rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+    p = _Plan()
+    st = lib().rowred_layernorm_plan_query(mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width),
+                                           my[0], rows, width, ctypes.byref(p))
+    _check(st, "rowred_layernorm_plan_query")
+    return Plan(p.lanes_per_row, p.rows_per_group, p.chunks, p.threads, p.grid, p.vector_io, p.window, p.policy,
+                p.reserved)
 
 
 def _row_vector(v, name, rows):

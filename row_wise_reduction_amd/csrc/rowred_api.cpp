@@ -211,13 +211,25 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // at 1024x4096, 2048x2048, 4096x1024, 8192x512 and 512x8192 (measured on
   // 16-byte-aligned rows; below 8 MiB 8 slots were up to 17% slower).
   const bool two_inputs = c.r != nullptr && c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
-  if (small && !scalar_out && !stage_ok &&
+  const int kop = kernel_op(c);
+  const bool affine = kop == kKernelOpLayerNormAffine;
+  if (small && !scalar_out && !stage_ok && !affine &&
       ((two_inputs && in_bytes >= (int64_t(8) << 20)) || (w >= 1024 && in_bytes >= (int64_t(16) << 20))))
     max_chunks = 8;
+  // Affine LayerNorm reads gamma and beta for every row it maps (from cache).
+  // On aligned rows it runs best in 256-thread workgroups with 4 slots per
+  // lane, 8 for rows of 1024-2048 granules beyond 32 MiB: 8-19% faster than
+  // the rules above at 16384x8192, 32768x4096, 65536x2048, 131072x1024 and
+  // 1024x4096, within 2% at 262144x512 (sweep of every geometry on MI355X).
+  // Wider rows keep the rules above (16384 columns: 1024 x 4 best).
+  bool affine_256 = false;
+  if (affine && rows_aligned && w <= 2048) {
+    max_chunks = !small && w >= 1024 ? 8 : 4;
+    affine_256 = true;
+  }
   int64_t L = 1;
   while (L < 1024 && (w + L - 1) / L > max_chunks) L *= 2;
   int chunks = round_up_chunks((w + L - 1) / L);
-  const int kop = kernel_op(c);
   // A stripe too wide for a 1024-lane workgroup of this kernel: halve the
   // lanes (and so double the stripe) until the kernel exists and fits.
   while (L > 1 && (L > max_threads_for(kop, chunks) || !kernel_exists(kop, chunks))) {
@@ -231,7 +243,7 @@ void choose_plan(const Call &c, rowred_plan *p) {
   }
   p->lanes_per_row = (int32_t)L;
   p->chunks = chunks;
-  const int64_t t_min = small && !scalar_out ? 256 : 512;
+  const int64_t t_min = (small && !scalar_out) || affine_256 ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = 0;
@@ -667,6 +679,24 @@ ROWRED_API int rowred_plan_query(int op, const float *x, const float *r, const f
     *out = rowred_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};
     return ROWRED_OK;
   }
+  choose_plan(c, out);
+  if (out->chunks < 0) return ROWRED_ERR_UNSUPPORTED;
+  return finish_plan(c, out);
+}
+
+ROWRED_API int rowred_layernorm_plan_query(const float *x, const float *r, const float *gamma, const float *beta,
+                                           const float *y, int64_t rows, int64_t width, rowred_plan *out) {
+  if (!out) return ROWRED_ERR_INVALID_ARG;
+  Call c;
+  int st = check_call(ROWRED_OP_LAYERNORM_RESIDUAL, x, r, const_cast<float *>(y), rows, width, false, false, 0.0f,
+                      &c);
+  if (st != ROWRED_OK) return st;
+  if (rows == 0 || width == 0) {
+    *out = rowred_plan{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return ROWRED_OK;
+  }
+  st = attach_affine(&c, gamma, beta);
+  if (st != ROWRED_OK) return st;
   choose_plan(c, out);
   if (out->chunks < 0) return ROWRED_ERR_UNSUPPORTED;
   return finish_plan(c, out);

@@ -510,3 +510,33 @@ def test_looped_layernorm_needs_two_chunks():
     p = R.rowred_plan_query("layernorm_residual", X, RR, Y, rows=4, width=100000)
     assert p.chunks == 2 and p.policy & R.ROWRED_POLICY_LOOPED
 
+
+
+@pytest.mark.parametrize("rows,width,want", [
+    ((16384, 8192, (256, 8, 256))), ((32768, 4096, (128, 8, 256))), ((65536, 2048, (128, 4, 256))),
+    ((131072, 1024, (64, 4, 256))), ((1024, 4096, (256, 4, 256))), ((512, 8192, (512, 4, 512))),
+    ((8192, 16384, (1024, 4, 1024))),
+])
+def test_layernorm_plan_query_affine(rows, width, want):
+    """Affine LayerNorm's own geometry rule (256-thread workgroups, 4 slots,
+    8 for rows of 1024-2048 granules beyond 32 MiB) on aligned rows; plain
+    LayerNorm keeps the general rules; misaligned affine rows too."""
+    G, B = 0x7F4000000000, 0x7F5000000000
+    p = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows=rows, width=width)
+    assert (p.lanes_per_row, p.chunks, p.threads) == want
+    assert p.lanes_per_row * p.chunks >= p.window
+    q = R.rowred_layernorm_plan_query(X, None, None, None, Y, rows=rows, width=width)
+    assert q == R.rowred_plan_query("layernorm_residual", X, None, Y, rows=rows, width=width)
+    m = R.rowred_layernorm_plan_query(X + 4, None, G, B, Y + 4, rows=rows, width=width - 1)
+    assert m == R.rowred_layernorm_plan_query(X + 4, None, None, None, Y + 4, rows=rows, width=width - 1)
+
+
+def test_layernorm_plan_query_errors():
+    lib = R.lib()
+    p = R._Plan()
+    # gamma overlapping y; misaligned beta; no output
+    assert lib.rowred_layernorm_plan_query(X, None, Y + 64, None, Y, 4, 4096, ctypes.byref(p)) == R.ROWRED_ERR_ALIAS
+    assert lib.rowred_layernorm_plan_query(X, None, None, 0x7F5000000002, Y, 4, 4096, ctypes.byref(p)) == \
+        R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_layernorm_plan_query(X, None, None, None, Y, 4, 4096, None) == R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_layernorm_plan_query(X, None, None, None, Y, 0, 4096, ctypes.byref(p)) == R.ROWRED_OK

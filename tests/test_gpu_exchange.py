@@ -199,3 +199,30 @@ def test_ws_entry_chooses_exchange(op, width):
     got = run(op, x, r, g, b, shift=width % 4, ws=ws)
     assert status_ok(ws)
     check(op, got, reference(op, x, r, g, b), f"{op} {rows}x{width}")
+
+
+def test_two_streams_at_once():
+    """Exchange calls on two streams at the same time, each with its own
+    workspace: the two kernels share the chip, every wait still ends (status
+    words clear) and both match the oracle on sampled rows."""
+    t = torch()
+    rows, width = 512, 65536
+    xs = [synthetic.random_matrix(500 + i, rows, width, "normal") for i in range(2)]
+    xd = [t.from_numpy(x).cuda() for x in xs]
+    ys = [t.empty(rows, width, device="cuda") for _ in range(2)]
+    ws = [R.new_workspace(op, rows, width) for op in ("softmax", "rmsnorm")]
+    for w in ws:
+        w.fill_(0x77)
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    t.cuda.synchronize()
+    for rep in range(3):
+        with t.cuda.stream(streams[0]):
+            R.rowred_softmax_ws(xd[0], ys[0], ws[0])
+        with t.cuda.stream(streams[1]):
+            R.rowred_rmsnorm_ws(xd[1], ys[1], ws[1], eps=1e-6)
+    t.cuda.synchronize()
+    assert all(status_ok(w) for w in ws)
+    for i, op in enumerate(("softmax", "rmsnorm")):
+        yh = ys[i].cpu().numpy()
+        for rr in (0, 255, 511):
+            check(op, yh[rr:rr + 1], reference(op, xs[i][rr:rr + 1], None, None, None), f"{op} stream {i} row {rr}")
