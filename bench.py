@@ -105,7 +105,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     for p in ("row_wise_reduction_amd/csrc/rowred_kernels.hip", "row_wise_reduction_amd/csrc/rowred_api.cpp",
               "row_wise_reduction_amd/csrc/rowred_internal.h", "row_wise_reduction_amd/csrc/rowred_device.h",
-              "row_wise_reduction_amd/csrc/rowred_split.hip", "row_wise_reduction_amd/csrc/rowred_looped.hip"):
+              "row_wise_reduction_amd/csrc/rowred_split.hip", "row_wise_reduction_amd/csrc/rowred_looped.hip",
+              "row_wise_reduction_amd/csrc/rowred_wide.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 

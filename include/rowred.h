@@ -217,7 +217,7 @@ enum rowred_policy {
                                      once).  NT_LOADS / NT_STORES apply to the second walk; no
                                      other bit may be set.  The entry points choose it for rows
                                      wider than 8192 granules */
-  ROWRED_POLICY_EXCHANGE = 128    /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
+  ROWRED_POLICY_EXCHANGE = 128,   /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the
                                      workspace and waits for the row's other segments, so x (and
@@ -226,6 +226,13 @@ enum rowred_policy {
                                      (threads <= 512; not LayerNorm).
                                      NT_LOADS / NT_STORES apply to its loads and stores;
                                      REVERSE may not be set */
+  ROWRED_POLICY_LDS_STRIPE = 256  /* RMSNorm and softmax, lanes_per_row == threads == 1024,
+                                     chunks 5-8: slots 0-3 of each lane stay in registers and
+                                     the rest are loaded straight into LDS (16-byte loads that
+                                     write LDS), so two workgroups fit a CU.  Same arithmetic
+                                     in the same order as the register-resident kernel: same
+                                     bits.  NT_LOADS / NT_STORES / XCD_REMAP apply; no other
+                                     bit may be set */
 };
 
 /*

@@ -36,6 +36,7 @@ ROWRED_POLICY_RELOAD = 16
 ROWRED_POLICY_REVERSE = 32
 ROWRED_POLICY_LOOPED = 64
 ROWRED_POLICY_EXCHANGE = 128
+ROWRED_POLICY_LDS_STRIPE = 256
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0
 ROWRED_OP_RMSNORM = 1

@@ -33,8 +33,9 @@ constexpr int kPolicyXcdRemap = ROWRED_POLICY_XCD_REMAP;
 constexpr int kPolicyStageStores = ROWRED_POLICY_STAGE_STORES;
 constexpr int kPolicyReload = ROWRED_POLICY_RELOAD;
 constexpr int kPolicyLooped = ROWRED_POLICY_LOOPED;
-constexpr int kPolicyAll =
-    kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload | kPolicyLooped;
+constexpr int kPolicyLdsStripe = ROWRED_POLICY_LDS_STRIPE;
+constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload |
+                           kPolicyLooped | kPolicyLdsStripe;
 // The per-phase reload variant exists for the three matrix operators (kernel
 // ops 0-2) at up to 8 chunks.
 constexpr int kMaxReloadChunks = 8;
@@ -83,6 +84,12 @@ int launch_looped(int op, int chunks, int64_t rows, int threads, const RowArgs &
 constexpr bool looped_kernel_exists(int op, int chunks) {
   return chunks == 2 || (chunks == 4 && op != 0 && op != kKernelOpLayerNormAffine);
 }
+
+// Enqueue the LDS-stripe kernel (ROWRED_POLICY_LDS_STRIPE): RMSNorm (op 1)
+// or softmax (op 2), one 1024-lane workgroup per row, chunks 5-8 of which
+// the first kWideRegChunks stay in registers.  grid = rows.
+constexpr int kWideMaxLdsChunks = 4;
+int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream_t stream);
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);

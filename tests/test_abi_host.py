@@ -83,7 +83,11 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
         assert L * p.chunks >= p.window
         # stripe within the private budget: <= 64 floats per lane
         assert 4 * p.chunks <= 64
-        assert 0 <= p.policy < 16 and p.reserved == 0
+        lds = R.ROWRED_POLICY_LDS_STRIPE
+        assert 0 <= p.policy & ~lds < 16 and p.reserved == 0
+        if p.policy & lds:  # RMSNorm / softmax, 1024 lanes, 5-8 slots, up to 2048 x 8192 granules
+            assert op in ("rmsnorm", "softmax") and L == T == 1024 and 5 <= p.chunks <= 8
+            assert rows * p.window <= 2048 * 8192 and not p.policy & R.ROWRED_POLICY_STAGE_STORES
 
 
 def test_plan_for_workload_shapes():
@@ -94,7 +98,8 @@ def test_plan_for_workload_shapes():
     cases = {(131072, 127): (16, 3, ns | st), (131072, 257): (32, 3, ns | st),
              (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
-             (17, 257): (32, 3, ns | st)}
+             (17, 257): (32, 3, ns | st), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
+             (2048, 32768): (1024, 8, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE)}
     for (rows, width), (L, C, pol) in cases.items():
         p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
@@ -230,6 +235,30 @@ def test_reload_policy_preconditions():
     # unknown policy bits stay rejected
     c32 = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=32)._c()
     assert lib.rowred_run_plan(1, X, None, Y, 8, 127, f(1e-6), ctypes.byref(c32), None) == R.ROWRED_ERR_INVALID_ARG
+
+
+def test_lds_stripe_preconditions():
+    """ROWRED_POLICY_LDS_STRIPE: RMSNorm and softmax, 1024 lanes and threads,
+    5-8 chunks, without staging or reloading."""
+    m = R.ROWRED_POLICY_LDS_STRIPE
+    lib = R.lib()
+    ok = bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=m)._c()
+    for op in (1, 2):  # zero rows: checked, nothing launched
+        assert lib.rowred_run_plan(op, X, None, Y, 0, 32768, f(1e-6), ctypes.byref(ok), None) == R.ROWRED_OK
+    for kw in (dict(chunks=4, policy=m), dict(lanes_per_row=512, chunks=16, threads=512, policy=m),
+               dict(lanes_per_row=512, threads=1024, chunks=16, policy=m),
+               dict(policy=m | R.ROWRED_POLICY_RELOAD), dict(policy=m | R.ROWRED_POLICY_LOOPED)):
+        base = dict(lanes_per_row=1024, chunks=8, threads=1024)
+        base.update(kw)
+        c = bad_plan(**base)._c()
+        assert lib.rowred_run_plan(2, X, None, Y, 8, 32768, f(0), ctypes.byref(c), None) == R.ROWRED_ERR_INVALID_ARG, kw
+    # LayerNorm (residual, plain, affine) and the row reductions have no LDS-stripe kernel
+    assert lib.rowred_run_plan(0, X, X + (1 << 30), Y, 8, 32768, f(1e-5), ctypes.byref(ok), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_layernorm_run_plan(X, None, None, None, Y, 8, 32768, f(1e-5), ctypes.byref(ok), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+    assert lib.rowred_row_reduce_run_plan(3, X, 0x7F4000000000, None, 8, 32768, ctypes.byref(ok), None) == \
+        R.ROWRED_ERR_INVALID_ARG
 
 
 def test_stage_policy_preconditions():

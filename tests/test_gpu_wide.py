@@ -1,0 +1,88 @@
+"""LDS-stripe kernels (ROWRED_POLICY_LDS_STRIPE): RMSNorm and softmax rows of
+4097-8192 granules, slots 0-3 of each lane in registers and the rest loaded
+straight into LDS.  Same arithmetic in the same order as the register-resident
+kernel with the same stripe: the results must be bitwise equal to it, and so
+within the oracle's bar (|y - ref| <= 1e-5 + 1e-5 |ref|)."""
+import numpy as np
+import pytest
+
+import row_wise_reduction_amd as R
+import synthetic
+from tests.gpu_util import Guarded, assert_close, print_case, shifted_input, torch
+from tests.test_gpu_parity import oracle_of
+
+pytestmark = pytest.mark.gpu
+
+LDS = R.ROWRED_POLICY_LDS_STRIPE
+
+
+def run(op, xd, plan, rows, width, shift, y_shift=None):
+    out = Guarded(rows, width, shift if y_shift is None else y_shift)
+    R.rowred_run_plan(op, xd, None, out.y, plan, eps=synthetic.EPS.get(op, 0.0))
+    torch().cuda.synchronize()
+    assert out.guards_intact(), f"{op} {rows}x{width} wrote outside y"
+    return out.host()
+
+
+@pytest.mark.parametrize("width", [16385, 20000, 24576, 28673, 32765, 32768])
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_matches_register_stripe_bitwise(op, width):
+    """Every stripe length 5-8, ragged and misaligned rows (y at x's phase and
+    at another), both memory policies, XCD remap."""
+    rows = 37
+    x = synthetic.random_matrix(width + 11, rows, width, "normal")
+    ref = oracle_of(op, x)
+    for shift, y_shift in ((0, 0), (1, 1), (3, 2)):
+        xd = shifted_input(x, shift)
+        C = -(-((width + shift + 3) // 4) // 1024)
+        if C > 8:
+            continue  # a window of 8193 granules: beyond the register-resident kernels
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+            base = R.Plan(1024, 0, C, 1024, 0, policy=pol)
+            wide = R.Plan(1024, 0, C, 1024, 0, policy=pol | LDS)
+            print_case("lds stripe", op, width, shift, y_shift, wide)
+            y0 = run(op, xd, base, rows, width, shift, y_shift)
+            y1 = run(op, xd, wide, rows, width, shift, y_shift)
+            assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32)), f"{op} {width} {shift} {wide}"
+            assert_close(y1, ref, f"{op} {width} {wide}")
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_special_values(op):
+    rows, width = 8, 32768
+    x = synthetic.random_matrix(95, rows, width, "normal")
+    x[0, :] = -np.inf
+    x[1, :20000] = -np.inf             # the max sits in the LDS slots
+    x[2, 30000] = np.nan
+    x[3, 17] = np.inf
+    x[4, :] = np.nan
+    x[5, :] = 3.0
+    x[6, 31000:] = 60.0                # large values in the LDS slots only
+    x[7, ::2] = 1e15
+    x[7, 1::2] = -1e15
+    xd = shifted_input(x, 0)
+    base = run(op, xd, R.Plan(1024, 0, 8, 1024, 0, policy=0), rows, width, 0)
+    wide = run(op, xd, R.Plan(1024, 0, 8, 1024, 0, policy=LDS), rows, width, 0)
+    assert np.array_equal(base.view(np.uint32), wide.view(np.uint32))
+    assert_close(wide, oracle_of(op, x), f"{op} special")
+
+
+@pytest.mark.parametrize("case", synthetic.CORE_WORKLOADS[5], ids=lambda c: c.name)
+def test_full_size_stress(case):
+    """The softmax stress workload at full size through the LDS stripe:
+    bitwise the register-resident result."""
+    t = torch()
+    print_case(case.name)
+    x = synthetic.case_input(case, "x")
+    xd = t.from_numpy(x).cuda()
+    y0 = t.empty_like(xd)
+    y1 = t.empty_like(xd)
+    pol = R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP
+    R.rowred_run_plan(case.op, xd, None, y0, R.Plan(1024, 0, 8, 1024, 0, policy=pol))
+    R.rowred_run_plan(case.op, xd, None, y1, R.Plan(1024, 0, 8, 1024, 0, policy=pol | LDS))
+    t.cuda.synchronize()
+    assert t.equal(y0.view(t.int32), y1.view(t.int32))
+    for i in (0, case.rows // 2, case.rows - 1):
+        assert_close(y1[i:i + 1].cpu().numpy(), oracle_of(case.op, x[i:i + 1]), f"{case.name} row {i}")
+    del y0, y1, xd
+    t.cuda.empty_cache()
