@@ -398,14 +398,19 @@ def copy_ceiling(nbytes, reps=20):
             for i in range(reps):
                 R.rowred_copy(src[i % pairs], dst[i % pairs])
     torch.cuda.current_stream().wait_stream(stream)
-    g.replay()
+    for _ in range(2):
+        g.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
+    # the best of three timed replays: one slow replay (seen once, 10x) would
+    # otherwise stand for the ceiling
+    us = 1e30
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = min(us, a.elapsed_time(b) * 1e3 / reps)
     return {"bytes_per_call": 8 * n, "us_per_call": round(us, 3), "GB_s": round(8 * n / (us * 1e-6) / 1e9, 1)}
 
 
