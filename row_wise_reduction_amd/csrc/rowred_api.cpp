@@ -458,25 +458,33 @@ void choose_split(int op, int64_t rows, int64_t width, rowred_split_plan *p) {
 // call on buffers rotated through >= 2 GiB.  A workgroup pays a fixed
 // latency (its loads, then the wait for its row's other segments) that only
 // more bytes per workgroup amortise:
-//   * 256 threads x 8 slots (RMSNorm, softmax) and 256 x 4 (LayerNorm, whose
-//     x and r need the registers) are best or within 4% at every wide shape;
-//     2 slots per lane were 1.5-2x slower;
-//   * rows too wide for 64 of those segments take 512 threads (LayerNorm
-//     512, then 1024);
-//   * rows narrower than two such segments take the first of 256 x 4,
-//     256 x 2, 128 x 2, 64 x 2 whose segment is at most half the row (else
-//     64 x 1): few-row shapes are latency bound and gain from more, shorter
-//     segments;
+//   * RMSNorm and softmax: 256 threads x 8 register slots, best or within 4%
+//     at every wide shape (2 slots per lane were 1.5-2x slower).  Rows that
+//     would take more than 64 such segments: 8 register + 8 LDS slots
+//     (LDS_STRIPE; 64x1048576 softmax 108 us against 120 for 512 x 8), then
+//     512 x 8.  The LDS stripe is 2-23% slower where 256 x 8 fits.
+//   * LayerNorm, whose x and r both take slots: 4 register + 4 LDS slots
+//     (LDS_STRIPE), 10% faster than 256 x 4 registers at 1024x65536 and 25%
+//     at 256x262144; rows beyond 64 of those segments: 1024 x 4.
+//   * rows narrower than two segments of the first geometry take the first
+//     of 256 x 4, 256 x 2, 128 x 2, 64 x 2 whose segment is at most half the
+//     row (else 64 x 1): few-row shapes are latency bound and gain from more,
+//     shorter segments;
 //   * streaming loads and stores, as everywhere on rows read once.
 // `window`: the row's 16-byte granules (the x at hand's, or the worst phase's
 // for sizing).  False when no geometry cuts the row into at most
-// kMaxExchangeSegments.
-// More, shorter segments per row measured slower: 256 x 8 at 128 segments
-// was 15% behind 512 x 8 at 64 on 64x1048576 softmax.  Keeping a row's
-// segments on one XCD was 25-60% slower everywhere.
+// kExchangeChosenSegments.  More, shorter segments per row measured slower:
+// 256 x 8 at 128 segments was 15% behind 512 x 8 at 64 on 64x1048576
+// softmax.  Keeping a row's segments on one XCD was 25-60% slower everywhere.
 constexpr int64_t kExchangeChosenSegments = 64;
-constexpr int kExchangeWide[2][3][2] = {{{256, 4}, {512, 4}, {1024, 4}},   // LayerNorm
-                                        {{256, 8}, {512, 8}, {0, 0}}};     // RMSNorm, softmax
+struct ExchangeGeometry {
+  int threads, chunks;
+  bool lds;
+};
+constexpr ExchangeGeometry kExchangeWide[2][3] = {
+    {{256, 8, true}, {1024, 4, false}, {0, 0, false}},  // LayerNorm
+    {{256, 8, false}, {256, 16, true}, {512, 8, false}},  // RMSNorm, softmax
+};
 constexpr int kExchangeNarrow[][2] = {{256, 4}, {256, 2}, {128, 2}, {64, 2}, {64, 1}};
 
 bool choose_exchange(int op, int64_t window, rowred_split_plan *p) {
@@ -484,12 +492,16 @@ bool choose_exchange(int op, int64_t window, rowred_split_plan *p) {
   const int64_t w = window;
   const auto &wide = kExchangeWide[op == ROWRED_OP_LAYERNORM_RESIDUAL ? 0 : 1];
   int T = 0, C = 0;
-  if (w >= 2 * (int64_t)wide[0][0] * wide[0][1]) {
+  bool lds = false;
+  if (w >= 2 * (int64_t)wide[0].threads * wide[0].chunks) {
     for (const auto &g : wide) {
-      const int64_t S = g[0] ? (w + (int64_t)g[0] * g[1] - 1) / ((int64_t)g[0] * g[1]) : 0;
-      if (g[0] && S <= kExchangeChosenSegments && S <= g[0]) {
-        T = g[0];
-        C = g[1];
+      if (!g.threads) break;
+      const int64_t G = (int64_t)g.threads * g.chunks;
+      const int64_t S = (w + G - 1) / G;
+      if (S <= kExchangeChosenSegments && S <= g.threads) {
+        T = g.threads;
+        C = g.chunks;
+        lds = g.lds;
         break;
       }
     }
@@ -508,7 +520,7 @@ bool choose_exchange(int op, int64_t window, rowred_split_plan *p) {
   *p = rowred_split_plan{};
   p->threads = T;
   p->chunks = C;
-  p->policy = kPolicyExchange | kPolicyNtLoads | kPolicyNtStores;
+  p->policy = kPolicyExchange | kPolicyNtLoads | kPolicyNtStores | (lds ? kPolicyLdsStripe : 0);
   return true;
 }
 
@@ -524,10 +536,16 @@ int finish_split(const Call &c, rowred_split_plan *p) {
   if (!is_pow2(T) || T < 64 || T > 1024) return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~kSplitPolicyAll) return ROWRED_ERR_INVALID_ARG;
   const bool exchange = (p->policy & kPolicyExchange) != 0;
-  if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4 && !(exchange && p->chunks == 8))
-    return ROWRED_ERR_INVALID_ARG;
-  if (exchange && (T > exchange_max_threads(p->chunks) || !exchange_kernel_exists(c.op, p->chunks)))
-    return ROWRED_ERR_INVALID_ARG;
+  const bool lds = (p->policy & kPolicyLdsStripe) != 0;
+  if (lds) {  // exchange kernels with part of the segment in LDS
+    if (!exchange || c.op > ROWRED_OP_SOFTMAX || T != kXldsThreads || xlds_stripe_index(c.op, p->chunks) < 0)
+      return ROWRED_ERR_INVALID_ARG;
+  } else {
+    if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4 && !(exchange && p->chunks == 8))
+      return ROWRED_ERR_INVALID_ARG;
+    if (exchange && (T > exchange_max_threads(p->chunks) || !exchange_kernel_exists(c.op, p->chunks)))
+      return ROWRED_ERR_INVALID_ARG;
+  }
   if (exchange && ((p->policy & kPolicyReverse) || c.op > ROWRED_OP_SOFTMAX)) return ROWRED_ERR_INVALID_ARG;
   if (p->block_rows < 0) return ROWRED_ERR_INVALID_ARG;
   const int64_t G = T * p->chunks;

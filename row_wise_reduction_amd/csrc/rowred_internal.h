@@ -127,7 +127,8 @@ constexpr int kSplitChunkSet[] = {1, 2, 4};
 constexpr int kNumSplitChunks = 3;
 constexpr int kPolicyReverse = ROWRED_POLICY_REVERSE;
 constexpr int kPolicyExchange = ROWRED_POLICY_EXCHANGE;
-constexpr int kSplitPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyReverse | kPolicyExchange;
+constexpr int kSplitPolicyAll =
+    kPolicyNtLoads | kPolicyNtStores | kPolicyReverse | kPolicyExchange | ROWRED_POLICY_LDS_STRIPE;
 // The segments of a row wait for each other in the exchange kernel, so all
 // of a row's segments must fit on the chip at once.  Every CU holds at least
 // one workgroup of any allowed size (launch bounds keep 1024-thread kernels
@@ -141,6 +142,14 @@ constexpr int kMaxExchangeSegments = 128;
 constexpr int kNumExchangeChunks = 4;
 constexpr int exchange_max_threads(int chunks) { return chunks >= 8 ? 512 : 1024; }
 constexpr bool exchange_kernel_exists(int op, int chunks) { return chunks != 8 || op != 0; }
+// Exchange kernels with part of the segment in LDS (ROWRED_POLICY_LDS_STRIPE
+// on a split plan): 256 threads; chunks 8 (4 in registers + 4 in LDS), 12
+// (8 + 4) or 16 (8 + 8); LayerNorm at 8 only.  -1: no such kernel.
+constexpr int kXldsThreads = 256;
+constexpr int kNumXldsStripes = 3;
+constexpr int xlds_stripe_index(int op, int chunks) {
+  return chunks == 8 ? 0 : (op != 0 && chunks == 12) ? 1 : (op != 0 && chunks == 16) ? 2 : -1;
+}
 
 // Enqueue the statistics kernel (op: LayerNorm 0, RMSNorm 1, softmax 2, row
 // sum 3, row min/max 4) and then the apply (ops 0-2) or merge (ops 3-4)

@@ -486,6 +486,44 @@ __device__ __forceinline__ double exchange_sum(const SegArgs &a, const uint64_t 
   return row_allreduce<SumOp>(mine ? decode(w) : 0.0, a.lanes_log2, partials);
 }
 
+// The row's softmax record from the S published pairs: m = max m_k,
+// s = sum s_k exp(m_k - m), the same bits in every segment.
+__device__ __forceinline__ Rec softmax_row_record(const SegArgs &a, const uint64_t *slots, int lanes_log2,
+                                                  float *pm, float *ps) {
+  const bool mine = (int)threadIdx.x < a.segments;
+  const uint64_t w = ~await_slot(a, slots);
+  const float mk = mine ? __builtin_bit_cast(float, (uint32_t)w) : -__builtin_inff();
+  const float sk = mine ? __builtin_bit_cast(float, (uint32_t)(w >> 32)) : 0.0f;
+  const float mrow = row_allreduce<MaxOp>(mk, lanes_log2, pm);
+  // An all -inf row has mrow = -inf and s_k = 0: 0 * exp(NaN) is NaN, and
+  // so is the row, as in one pass.
+  const float t = mine ? sk * __builtin_amdgcn_exp2f((mk - mrow) * kLog2e) : 0.0f;
+  return Rec{(double)mrow, (double)row_allreduce<SumOp>(t, lanes_log2, ps)};
+}
+
+// The row's LayerNorm record (mean, M2) from the S published (sum, M2)
+// words, segments of G granules of a row at phase `off`: Chan, Golub and
+// LeVeque's merge, the same bits in every segment.  p1 and p0 are the LDS
+// partials of its two reductions.
+__device__ __forceinline__ Rec layernorm_row_record(const SegArgs &a, const uint64_t *slots0, const uint64_t *slots1,
+                                                    int64_t G, int off, int lanes_log2, double *p1, double *p0) {
+  // Both words of segment k, each written once: wait for each.
+  const int k = threadIdx.x;
+  const bool mine = k < a.segments;
+  const double sum_k = decode(await_slot(a, slots0));
+  const double m2_k = decode(await_slot(a, slots1));
+  const double mean = row_allreduce<SumOp>(mine ? sum_k : 0.0, lanes_log2, p1) / (double)a.width;
+  const int64_t n_k = mine ? segment_count(k, G, off, a.width) : 0;
+  double t = 0.0;
+  if (n_k > 0) {
+    const double dm = sum_k / (double)n_k - mean;
+    t = m2_k + (double)n_k * dm * dm;
+  } else if (mine) {
+    t = m2_k + sum_k;  // 0 + 0, but a wait that gave up still turns the row NaN
+  }
+  return Rec{mean, row_allreduce<SumOp>(t, lanes_log2, p0)};
+}
+
 template <int OP, int C>
 __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegArgs a) {
   __shared__ float partials[4][16];
@@ -536,15 +574,7 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
     const float s = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[1]);
     uint64_t *slots = exchange_slots(a, 0, row);
     publish(slots + seg, encode_pair(m, s));
-    const bool mine = (int)threadIdx.x < a.segments;
-    const uint64_t w = ~await_slot(a, slots);
-    const float mk = mine ? __builtin_bit_cast(float, (uint32_t)w) : -__builtin_inff();
-    const float sk = mine ? __builtin_bit_cast(float, (uint32_t)(w >> 32)) : 0.0f;
-    const float mrow = row_allreduce<MaxOp>(mk, lanes_log2, partials[2]);
-    // An all -inf row has mrow = -inf and s_k = 0: 0 * exp(NaN) is NaN, and
-    // so is the row, as in one pass.
-    const float t = mine ? sk * __builtin_amdgcn_exp2f((mk - mrow) * kLog2e) : 0.0f;
-    rr = Rec{(double)mrow, (double)row_allreduce<SumOp>(t, lanes_log2, partials[3])};
+    rr = softmax_row_record(a, slots, lanes_log2, partials[2], partials[3]);
   } else {  // LayerNorm: (sum, squares about the segment mean), merged as the split kernels merge them
     float hi[4 * C], lo[4 * C];
     two_sum<C>(v, xv, rv, hi, lo);
@@ -584,25 +614,299 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
     uint64_t *slots1 = exchange_slots(a, 1, row);
     publish(slots0 + seg, encode(sum));
     publish(slots1 + seg, encode((double)m2));
-    // Both words of segment k, each written once: wait for each.
-    const int k = threadIdx.x;
-    const bool mine = k < a.segments;
-    const double sum_k = decode(await_slot(a, slots0));
-    const double m2_k = decode(await_slot(a, slots1));
-    const double mean = row_allreduce<SumOp>(mine ? sum_k : 0.0, lanes_log2, partials_d[1]) / (double)a.width;
-    const int64_t n_k = mine ? segment_count(k, G, v.off, a.width) : 0;
-    double t = 0.0;
-    if (n_k > 0) {
-      const double dm = sum_k / (double)n_k - mean;
-      t = m2_k + (double)n_k * dm * dm;
-    } else if (mine) {
-      t = m2_k + sum_k;  // 0 + 0, but a wait that gave up still turns the row NaN
-    }
     // partials_d[0] again: every wave read it before the barrier that
     // partials_d[1]'s reduction passed.
-    rr = Rec{mean, row_allreduce<SumOp>(t, lanes_log2, partials_d[0])};
+    rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
   }
   apply_store<OP, C, OP == kOpLayerNorm>(a, v, row, xv, rv, rr);
+}
+
+// ---------------------------------------------------------------------------
+// Exchange kernels with part of the segment in LDS (ROWRED_POLICY_EXCHANGE |
+// ROWRED_POLICY_LDS_STRIPE), 256 threads: a lane's slots 0..CR-1 stay in
+// registers and slots CR..CR+CL-1 go straight from HBM into LDS (x, and r
+// for LayerNorm) with 16-byte LDS-writing loads; each lane reads back only
+// its own LDS slots, so that needs no barrier.  A segment carries (CR + CL)
+// slots per lane for the registers of CR: fewer segments per row and more
+// bytes in flight per CU.  Statistics, their exchange and the merges are
+// those of seg_exchange_kernel.
+// ---------------------------------------------------------------------------
+template <int OP, int CR, int CL>
+__global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
+  constexpr int T = kXldsThreads;
+  constexpr int C = CR + CL;
+  constexpr bool kLN = OP == kOpLayerNorm;
+  constexpr int lanes_log2 = 8;
+  __shared__ f32x4 held_x[CL * T];
+  __shared__ f32x4 held_r[kLN ? CL * T : 1];
+  __shared__ float partials[4][16];
+  __shared__ double partials_d[2][16];
+  typedef __attribute__((address_space(3))) void lds_void;
+  int64_t row;
+  int seg;
+  segment_of(a, false, row, seg);
+  const SegView v = make_view(a, row, seg, T, C);
+  const int li = threadIdx.x;
+  const bool has_r = kLN && a.r != nullptr;
+  f32x4 *wave_x = held_x + (li & ~63);  // lane l of the wave lands at entry l
+  f32x4 *wave_r = held_r + (li & ~63);
+
+  f32x4 xv[CR], rv[CR];
+  auto load_all = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    if constexpr (NT) asm volatile("" ::: "memory");
+    const f32x4 *xw = reinterpret_cast<const f32x4 *>(v.xrow - v.off);
+#pragma unroll
+    for (int c = 0; c < CL; ++c)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xw + min(v.granule(CR + c), v.kmax)),
+                                       (lds_void *)(wave_x + c * T), 16, 0, NT ? 2 : 0);
+    if constexpr (kLN) {
+      if (has_r && a.r_vec) {
+        const f32x4 *rw = reinterpret_cast<const f32x4 *>(v.rrow - v.off);
+#pragma unroll
+        for (int c = 0; c < CL; ++c)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(rw + min(v.granule(CR + c), v.kmax)),
+                                           (lds_void *)(wave_r + c * T), 16, 0, NT ? 2 : 0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CR; ++c) xv[c] = load_g<NT>(xw + min(v.granule(c), v.kmax));
+    if (has_r) {
+      if (a.r_vec) {
+        const f32x4 *rw = reinterpret_cast<const f32x4 *>(v.rrow - v.off);
+#pragma unroll
+        for (int c = 0; c < CR; ++c) rv[c] = load_g<NT>(rw + min(v.granule(c), v.kmax));
+      } else {
+        const int emax = v.width - 1;
+#pragma unroll
+        for (int c = 0; c < CR; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rv[c][j] = load_g<NT>(v.rrow + max(0, min(v.elem(c, j), emax)));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CR; ++c) rv[c] = f32x4(0.0f);
+    }
+    if constexpr (NT) asm volatile("" ::: "memory");
+  };
+  if (a.policy & kPolicyNtLoads) load_all(std::true_type{});
+  else load_all(std::false_type{});
+  // The LDS writes of those loads are done once the loads have completed.
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (kLN) {
+    if (has_r && !a.r_vec) {
+      // r at another 16-byte phase than x: 4-byte loads into the lane's own
+      // LDS slots
+      const int emax = v.width - 1;
+#pragma unroll
+      for (int c = 0; c < CL; ++c) {
+        f32x4 t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = v.rrow[max(0, min(v.elem(CR + c, j), emax))];
+        held_r[c * T + li] = t;
+      }
+    }
+  }
+  // Elements outside the row take the reduction's identity here, once (x and
+  // r 0; softmax x -inf), so that the phases below need no per-element masks
+  // (LayerNorm's squares and the stores excepted).
+  constexpr float kIdent = OP == kOpSoftmax ? -__builtin_inff() : 0.0f;
+#pragma unroll
+  for (int c = 0; c < CR; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = v.valid(c, j);
+      xv[c][j] = in ? xv[c][j] : kIdent;
+      if constexpr (kLN) rv[c][j] = in ? rv[c][j] : 0.0f;
+    }
+#pragma unroll
+  for (int c = 0; c < CL; ++c) {
+    f32x4 t = held_x[c * T + li];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = v.valid(CR + c, j) ? t[j] : kIdent;
+    held_x[c * T + li] = t;
+    if constexpr (kLN) {
+      if (has_r) {
+        f32x4 u = held_r[c * T + li];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = v.valid(CR + c, j) ? u[j] : 0.0f;
+        held_r[c * T + li] = u;
+      }
+    }
+  }
+  // Slot c of the lane, from registers or LDS (c is a constant once unrolled).
+  auto x_at = [&](int c) -> f32x4 { return c < CR ? xv[c < CR ? c : 0] : held_x[(c - CR) * T + li]; };
+  auto r_at = [&](int c) -> f32x4 {
+    if constexpr (!kLN) {
+      return f32x4(0.0f);
+    } else {
+      if (!has_r) return f32x4(0.0f);
+      return c < CR ? rv[c < CR ? c : 0] : held_r[(c - CR) * T + li];
+    }
+  };
+  // x + r as the exact pair (h, l) (TwoSum); 0 outside the row.
+  auto pair = [&](const f32x4 &xx, const f32x4 &rr_, int j, float &h, float &l) {
+    const float x = xx[j];
+    const float r = rr_[j];
+    h = x + r;
+    const float bb = h - x;
+    l = (x - (h - bb)) + (r - bb);
+  };
+  // After each LDS slot: keep the compiler from reading every LDS slot up
+  // front, which would hold them all in registers at once.
+  auto slot_done = [&](int c) {
+    if (c >= CR) __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Rec rr;
+  float m = 0.0f;
+  if constexpr (OP == kOpRms) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = x_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(xx[j], xx[j], acc[j]);
+      slot_done(c);
+    }
+    const float sq = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
+    uint64_t *slots = exchange_slots(a, 0, row);
+    publish(slots + seg, encode((double)sq));
+    rr = Rec{exchange_sum(a, slots, partials_d[0]), 0.0};
+  } else if constexpr (OP == kOpSoftmax) {
+    m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = x_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, xx[j]);
+      slot_done(c);
+    }
+    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = x_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool zero = xx[j] == -__builtin_inff();  // outside the row too
+        acc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((xx[j] - m) * kLog2e);
+      }
+      slot_done(c);
+    }
+    const float s = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[1]);
+    uint64_t *slots = exchange_slots(a, 0, row);
+    publish(slots + seg, encode_pair(m, s));
+    rr = softmax_row_record(a, slots, lanes_log2, partials[2], partials[3]);
+  } else {  // LayerNorm
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = x_at(c), r4 = r_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h, l;
+        pair(xx, r4, j, h, l);
+        acc[j] += (double)h;
+        acc_lo += l;
+      }
+      slot_done(c);
+    }
+    const double sum =
+        row_allreduce<SumOp>(((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo, lanes_log2, partials_d[0]);
+    const int64_t G = (int64_t)T * C;
+    const int64_t n = segment_count(seg, G, v.off, a.width);
+    const double seg_mean = n > 0 ? sum / (double)n : 0.0;
+    const float s_hi = (float)seg_mean;
+    const float s_lo = (float)(seg_mean - (double)s_hi);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = x_at(c), r4 = r_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h, l;
+        pair(xx, r4, j, h, l);
+        const float d = v.valid(c, j) ? (h - s_hi) + (l - s_lo) : 0.0f;
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+      slot_done(c);
+    }
+    const float m2 = row_allreduce<SumOp>((sq[0] + sq[1]) + (sq[2] + sq[3]), lanes_log2, partials[0]);
+    uint64_t *slots0 = exchange_slots(a, 0, row);
+    uint64_t *slots1 = exchange_slots(a, 1, row);
+    publish(slots0 + seg, encode(sum));
+    publish(slots1 + seg, encode((double)m2));
+    rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
+  }
+
+  // ---- map and store, slot by slot.
+  float scale = 0.0f, m_hi = 0.0f, m_lo = 0.0f;
+  if constexpr (OP == kOpRms) {
+    scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v0, a.inv_width, a.eps));
+  } else if constexpr (OP == kOpSoftmax) {
+    m = (float)rr.v0;
+    scale = __builtin_amdgcn_rcpf((float)rr.v1);
+  } else {
+    m_hi = (float)rr.v0;
+    m_lo = (float)(rr.v0 - (double)m_hi);
+    scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v1, a.inv_width, a.eps));
+  }
+  const bool affine = kLN && (a.gamma != nullptr || a.beta != nullptr);
+  const int emax = a.width - 1;
+  auto map_slot = [&](int c, float (&o)[4]) {
+    const f32x4 xx = x_at(c);
+    if constexpr (OP == kOpRms) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = xx[j] * scale;
+    } else if constexpr (OP == kOpSoftmax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f((xx[j] - m) * kLog2e) * scale;
+    } else {
+      const f32x4 r4 = r_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h, l;
+        pair(xx, r4, j, h, l);
+        float y = ((h - m_hi) + (l - m_lo)) * scale;
+        if (affine) {
+          const int e = max(0, min(v.elem(c, j), emax));
+          const float g = a.gamma ? a.gamma[e] : 1.0f;
+          const float b = a.beta ? a.beta[e] : 0.0f;
+          y = fmaf(y, g, b);
+        }
+        o[j] = y;
+      }
+    }
+  };
+  auto store_all = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    float *yrow = a.y + row * (int64_t)a.width;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float o[4];
+      map_slot(c, o);
+      const int k = v.granule(c);
+      const int e0 = 4 * k - v.off;
+      if (a.y_vec) {
+        if (e0 >= 0 && e0 + 4 <= a.width) {
+          store_g<NT>(reinterpret_cast<f32x4 *>(yrow - v.off) + k, f32x4{o[0], o[1], o[2], o[3]});
+        } else if (k <= v.kmax) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((unsigned)(e0 + j) < (unsigned)a.width) store_g<NT>(yrow + e0 + j, o[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v.valid(c, j)) store_g<NT>(yrow + v.elem(c, j), o[j]);
+      }
+      slot_done(c);
+    }
+  };
+  if (a.policy & kPolicyNtStores) store_all(std::true_type{});
+  else store_all(std::false_type{});
 }
 
 // Zero the status word and the slots (n64 words, 16-byte aligned, n64 even).
@@ -635,6 +939,13 @@ const SegFn kExchange[3][kNumExchangeChunks] = {
     ROWRED_EXCHANGE_ROW(kOpSoftmax),
 };
 #undef ROWRED_EXCHANGE_ROW
+// [op][stripe: 0 = 4 + 4 slots, 1 = 8 + 4, 2 = 8 + 8] (registers + LDS);
+// LayerNorm at 4 + 4 only (its x and r both take the slots).
+const SegFn kXlds[3][kNumXldsStripes] = {
+    {seg_xlds_kernel<kOpLayerNorm, 4, 4>, nullptr, nullptr},
+    {seg_xlds_kernel<kOpRms, 4, 4>, seg_xlds_kernel<kOpRms, 8, 4>, seg_xlds_kernel<kOpRms, 8, 8>},
+    {seg_xlds_kernel<kOpSoftmax, 4, 4>, seg_xlds_kernel<kOpSoftmax, 8, 4>, seg_xlds_kernel<kOpSoftmax, 8, 8>},
+};
 const SegFn kMerge[5] = {seg_merge_kernel<kOpLayerNorm>, seg_merge_kernel<kOpRms>, seg_merge_kernel<kOpSoftmax>,
                          seg_merge_kernel<kOpRowSum>, seg_merge_kernel<kOpRowMinMax>};
 static_assert(kNumSplitChunks == 3 && kSplitChunkSet[0] == 1 && kSplitChunkSet[1] == 2 && kSplitChunkSet[2] == 4,
@@ -650,10 +961,18 @@ int64_t exchange_words(int op, int64_t rows, int64_t segments) {
 }
 
 int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {
-  const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : chunks == 8 ? 3 : -1;
-  if (op < 0 || op > 2 || ci < 0 || !exchange_kernel_exists(op, chunks) || threads > exchange_max_threads(chunks) ||
-      args.segments > threads || args.segments > kMaxExchangeSegments)
-    return (int)hipErrorInvalidValue;
+  SegFn fn = nullptr;
+  if (args.policy & kPolicyLdsStripe) {
+    const int si = xlds_stripe_index(op, chunks);
+    if (op < 0 || op > 2 || si < 0 || threads != kXldsThreads) return (int)hipErrorInvalidValue;
+    fn = kXlds[op][si];
+  } else {
+    const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : chunks == 8 ? 3 : -1;
+    if (op < 0 || op > 2 || ci < 0 || !exchange_kernel_exists(op, chunks) || threads > exchange_max_threads(chunks))
+      return (int)hipErrorInvalidValue;
+    fn = kExchange[op][ci];
+  }
+  if (!fn || args.segments > threads || args.segments > kMaxExchangeSegments) return (int)hipErrorInvalidValue;
   uint64_t *w = reinterpret_cast<uint64_t *>(args.ws);
   int64_t n128 = (exchange_words(op, args.rows, args.segments) + 1) / 2;
   void *clear_params[] = {&w, &n128};
@@ -663,8 +982,8 @@ int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs
   if (err) return err;
   SegArgs a = args;
   void *params[] = {&a};
-  return (int)hipLaunchKernel(reinterpret_cast<const void *>(kExchange[op][ci]), dim3((uint32_t)grid),
-                              dim3(threads), params, 0, stream);
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)grid), dim3(threads), params, 0,
+                              stream);
 }
 
 int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {

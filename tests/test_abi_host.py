@@ -388,7 +388,10 @@ def test_workspace_size_covers_every_alignment(op, rows, width):
         if p.policy & R.ROWRED_POLICY_EXCHANGE:
             # LayerNorm, RMSNorm and softmax rows of at most 64 segments
             assert op in ("layernorm_residual", "rmsnorm", "softmax") and p.segments <= 64
-            assert p.chunks in ((1, 2, 4) if op == "layernorm_residual" else (1, 2, 4, 8))
+            if p.policy & R.ROWRED_POLICY_LDS_STRIPE:
+                assert p.threads == 256 and p.chunks in ((8,) if op == "layernorm_residual" else (8, 12, 16))
+            else:
+                assert p.chunks in ((1, 2, 4) if op == "layernorm_residual" else (1, 2, 4, 8))
         else:
             assert p.chunks in (1, 2, 4)
             if op in ("layernorm_residual", "rmsnorm", "softmax"):
@@ -436,6 +439,24 @@ def test_exchange_plan_rejects(op, width, kw):
     assert e.value.status == R.ROWRED_ERR_INVALID_ARG
 
 
+def test_lds_stripe_split_plans():
+    """LDS-stripe exchange plans: 256 threads, 8 slots (4 + 4) for every
+    matrix operator, 12 and 16 (8 + 4, 8 + 8) for RMSNorm and softmax; only
+    with EXCHANGE."""
+    E, L = R.ROWRED_POLICY_EXCHANGE, R.ROWRED_POLICY_LDS_STRIPE
+    for op, chunks in (("layernorm_residual", 8), ("rmsnorm", 8), ("rmsnorm", 12), ("softmax", 16)):
+        p = R.rowred_split_plan_query(op, X, 8, 100000, plan=R.SplitPlan(threads=256, chunks=chunks, policy=E | L))
+        assert p.segments == -(-p.window // (256 * chunks))
+    for op, kw in (("softmax", dict(threads=256, chunks=8, policy=L)),          # without EXCHANGE
+                   ("softmax", dict(threads=512, chunks=8, policy=E | L)),      # 256 threads only
+                   ("softmax", dict(threads=256, chunks=4, policy=E | L)),
+                   ("layernorm_residual", dict(threads=256, chunks=12, policy=E | L)),
+                   ("row_sum", dict(threads=256, chunks=8, policy=E | L))):
+        with pytest.raises(R.RowRedError) as e:
+            R.rowred_split_plan_query(op, X, 8, 100000, plan=R.SplitPlan(**kw))
+        assert e.value.status == R.ROWRED_ERR_INVALID_ARG, (op, kw)
+
+
 @pytest.mark.parametrize("op", ["layernorm_residual", "rmsnorm", "softmax"])
 @pytest.mark.parametrize("T,C", [(64, 1), (256, 2), (1024, 4), (512, 8)])
 def test_exchange_plan_limits(op, T, C):
@@ -453,19 +474,23 @@ def test_exchange_plan_limits(op, T, C):
 
 
 @pytest.mark.parametrize("op,rows,width,want", [
-    ("softmax", 4096, 1 << 16, (256, 8, 8)), ("rmsnorm", 2048, 1 << 17, (256, 8, 16)),
-    ("layernorm_residual", 1024, 1 << 16, (256, 4, 16)), ("layernorm_residual", 256, 1 << 18, (256, 4, 64)),
-    ("rmsnorm", 1024, 1 << 18, (256, 8, 32)), ("rmsnorm", 64, 1 << 19, (256, 8, 64)), ("rmsnorm", 64, 600000, (512, 8, 37)), ("softmax", 64, 1 << 20, (512, 8, 64)),
-    ("layernorm_residual", 16, 1 << 20, (1024, 4, 64)), ("softmax", 7, 1537, (64, 2, 4)),
-    ("softmax", 16, 32768, (256, 8, 4)),
+    ("softmax", 4096, 1 << 16, (256, 8, 8, 0)), ("rmsnorm", 2048, 1 << 17, (256, 8, 16, 0)),
+    ("layernorm_residual", 1024, 1 << 16, (256, 8, 8, 1)), ("layernorm_residual", 256, 1 << 18, (256, 8, 32, 1)),
+    ("rmsnorm", 1024, 1 << 18, (256, 8, 32, 0)), ("rmsnorm", 64, 1 << 19, (256, 8, 64, 0)),
+    ("rmsnorm", 64, 600000, (256, 16, 37, 1)), ("softmax", 64, 1 << 20, (256, 16, 64, 1)),
+    ("layernorm_residual", 16, 1 << 20, (1024, 4, 64, 0)), ("softmax", 7, 1537, (64, 2, 4, 0)),
+    ("softmax", 16, 32768, (256, 8, 4, 0)),
 ])
 def test_ws_split_plan_choice(op, rows, width, want):
-    """The _ws entry points' split plans: exchange geometries from the sweep;
-    one phase off 16 bytes, a row of 2^20 floats spans 262145 granules, one
-    more than 64 segments of 4096 hold, and falls back to the three kernels."""
+    """The _ws entry points' split plans: exchange geometries from the sweep
+    (the last field: part of each segment in LDS); one phase off 16 bytes, a
+    row of 2^20 floats spans 262145 granules, one more than 64 segments of
+    4096 hold, and falls back to the three kernels."""
     p = R.rowred_split_plan_query(op, X, rows, width)
-    assert (p.threads, p.chunks, p.segments) == want
-    assert p.policy == R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES
+    T, C, S, lds = want
+    assert (p.threads, p.chunks, p.segments) == (T, C, S)
+    assert p.policy == R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | \
+        (R.ROWRED_POLICY_LDS_STRIPE if lds else 0)
     if width == 1 << 20 and op != "layernorm_residual":
         q = R.rowred_split_plan_query(op, X + 4, rows, width)
         assert not q.policy & R.ROWRED_POLICY_EXCHANGE and q.segments > 64

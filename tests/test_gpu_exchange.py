@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 MATRIX_OPS = ("layernorm_residual", "layernorm", "layernorm_affine", "rmsnorm", "softmax")
 EXCHANGE = R.ROWRED_POLICY_EXCHANGE
 STREAM = R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES
+LDS = R.ROWRED_POLICY_LDS_STRIPE
 GEOMETRIES = [(64, 1), (64, 2), (128, 4), (256, 1), (256, 2), (512, 2), (1024, 1), (1024, 2), (1024, 4), (64, 8),
               (256, 8), (512, 8)]
 
@@ -61,6 +62,45 @@ def test_every_exchange_geometry(op, geom):
             check(op, run_exchange(op, x, r, g, b, plan, shift=shift), ref, f"{op} {width} {plan}")
 
 
+LDS_STRIPES = [8, 12, 16]  # 4 + 4, 8 + 4 and 8 + 8 slots per lane (registers + LDS), 256 threads
+
+
+@pytest.mark.parametrize("chunks", LDS_STRIPES, ids=lambda c: f"C{c}")
+@pytest.mark.parametrize("op", MATRIX_OPS)
+def test_lds_stripe_exchange(op, chunks):
+    """Exchange kernels with part of each segment in LDS: one, three and 128
+    segments per row, ragged, misaligned (r and y at another 16-byte phase
+    than x too), both memory policies."""
+    if op.startswith("layernorm") and chunks != 8:
+        pytest.skip("LayerNorm keeps 4 + 4 slots")
+    G = 256 * chunks
+    for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 128 - 9, 2)):
+        rows = max(2, min(6, (1 << 21) // width))
+        x, r, g, b = make_inputs(op, rows, width, seed=13 * width + chunks)
+        ref = reference(op, x, r, g, b)
+        for policy in (EXCHANGE | LDS, EXCHANGE | LDS | STREAM):
+            plan = R.SplitPlan(threads=256, chunks=chunks, policy=policy)
+            print_case("exchange lds", op, rows, width, shift, plan)
+            check(op, run_exchange(op, x, r, g, b, plan, shift=shift), ref, f"{op} {width} {plan}")
+
+
+def test_lds_stripe_misaligned_residual():
+    """LayerNorm with r at another 16-byte phase than x: the LDS slots of r are
+    filled by 4-byte loads."""
+    t = torch()
+    rows, width = 5, 40003
+    x, r, g, b = make_inputs("layernorm_residual", rows, width, seed=77)
+    ref = reference("layernorm_residual", x, r, None, None)
+    xd, rd = shifted_input(x, 1), shifted_input(r, 3)
+    out = t.empty(rows, width, device="cuda")
+    plan = R.SplitPlan(threads=256, chunks=8, policy=EXCHANGE | LDS | STREAM)
+    ws = workspace("layernorm_residual", rows, width, plan, xd)
+    R.rowred_split_run_plan("layernorm_residual", xd, rd, None, None, out, None, plan, ws, eps=1e-5)
+    t.cuda.synchronize()
+    assert status_ok(ws)
+    check("layernorm_residual", out.cpu().numpy(), ref, "misaligned r")
+
+
 @pytest.mark.parametrize("op", ["softmax", "rmsnorm", "layernorm"])
 def test_special_values(op):
     rows, width = 8, 5000
@@ -74,10 +114,12 @@ def test_special_values(op):
     x[6, ::2] = 1e15
     x[6, 1::2] = -1e15
     x[7, 4990:] = 50.0                  # the max sits in the last segment
-    plan = R.SplitPlan(threads=64, chunks=2, policy=EXCHANGE)  # 128-granule segments: 10 per row
     ref = reference(op, x, None, None, None)
-    got = run_exchange(op, x, None, None, None, plan)
-    check(op, got, ref, f"{op} special")
+    # 128-granule segments (10 per row), and 8 + 8 LDS-stripe ones (2 per row)
+    for plan in (R.SplitPlan(threads=64, chunks=2, policy=EXCHANGE),
+                 R.SplitPlan(threads=256, chunks=8 if op == "layernorm" else 16, policy=EXCHANGE | LDS)):
+        got = run_exchange(op, x, None, None, None, plan)
+        check(op, got, ref, f"{op} special {plan}")
     if op == "softmax":
         assert np.isnan(got[0]).all() and not np.isnan(got[1]).any()
         assert np.abs(got[1].astype(np.float64).sum() - 1.0) < 1e-5

@@ -58,8 +58,9 @@ def test_every_kernel_is_spill_free(asm):
     # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
     # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only),
     # the exchange kernels (3 operators x 4 chunk counts, LayerNorm not at 8)
-    # and their clear kernel, the LDS-stripe kernels (2 operators x 4 stripes)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 8
+    # and their clear kernel, the LDS-stripe kernels (2 operators x 4 stripes),
+    # the LDS-stripe exchange kernels (LayerNorm 1, RMSNorm and softmax 3 each)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 8 + 7
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -267,3 +268,26 @@ def test_lds_stripe_kernels(asm):
         assert any(ln.startswith("s_waitcnt vmcnt(0)") for ln in lines[:first_read]), dn
         assert m["lds"] >= cl * 1024 * 16 and m["vgpr"] <= 64, (dn, m)
     assert seen == 8
+
+
+def test_lds_stripe_exchange_kernels(asm):
+    """LDS-stripe exchange kernels: CL slots of x (and of r for LayerNorm)
+    loaded straight into LDS, non-temporal and cached copies; the exchange's
+    agent-scope words; a full wait before the first LDS read."""
+    seen = 0
+    for name, m in kernel_meta(asm).items():
+        dn = demangle(name)
+        if "seg_xlds_kernel<" not in dn:
+            continue
+        seen += 1
+        op, cr, cl = (int(t) for t in dn.split("seg_xlds_kernel<")[1].split(">")[0].split(","))
+        body = kernel_body(asm, name)
+        lines = [ln.strip() for ln in body.splitlines()]
+        lds_loads = [ln for ln in lines if ln.startswith("global_load_lds_dwordx4")]
+        per_copy = cl * (2 if op == 0 else 1)
+        assert len(lds_loads) == 2 * per_copy and sum(ln.endswith(" nt") for ln in lds_loads) == per_copy, dn
+        assert any(ln.startswith("global_store_dwordx2") and ln.endswith("sc1") for ln in lines), dn
+        first_read = next(i for i, ln in enumerate(lines) if ln.startswith("ds_read_b128"))
+        assert any(ln.startswith("s_waitcnt vmcnt(0)") for ln in lines[:first_read]), dn
+        assert m["lds"] >= cl * 256 * 16 * (2 if op == 0 else 1), (dn, m)
+    assert seen == 7
