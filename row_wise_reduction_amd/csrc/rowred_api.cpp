@@ -115,8 +115,27 @@ int finish_looped_plan(const Call &c, rowred_plan *p) {
   return ROWRED_OK;
 }
 
+// An LDS-stripe plan (ROWRED_POLICY_LDS_STRIPE): RMSNorm or softmax, one
+// 1024-lane workgroup per row, 5-16 chunks.
+int finish_lds_plan(const Call &c, rowred_plan *p) {
+  const int kop = kernel_op(c);
+  if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || p->lanes_per_row != 1024 || p->threads != 1024 ||
+      p->chunks < kWideMinChunks || p->chunks > kWideMaxChunks)
+    return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
+  p->window = c.window;
+  p->vector_io = c.y_vec ? 1 : 0;
+  if ((int64_t)1024 * p->chunks < p->window) return ROWRED_ERR_INVALID_ARG;
+  p->rows_per_group = 1;
+  p->grid = c.rows;
+  if (p->grid > INT32_MAX || p->grid * 1024 > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
 int finish_plan(const Call &c, rowred_plan *p) {
   if (p->policy & kPolicyLooped) return finish_looped_plan(c, p);
+  if (p->policy & kPolicyLdsStripe) return finish_lds_plan(c, p);
   const int64_t L = p->lanes_per_row, T = p->threads;
   if (!is_pow2(L) || L > 1024) return ROWRED_ERR_INVALID_ARG;
   if (T < 64 || T > 1024 || T % 64 != 0 || T % L != 0) return ROWRED_ERR_INVALID_ARG;
@@ -128,10 +147,6 @@ int finish_plan(const Call &c, rowred_plan *p) {
       (!reload_kernel_exists(kop, p->chunks) || T > reload_max_threads_for(kop, p->chunks)))
     return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
-  if ((p->policy & kPolicyLdsStripe) &&
-      ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || L != 1024 || T != 1024 || p->chunks < 5 ||
-       p->chunks > 8 || (p->policy & (kPolicyStageStores | kPolicyReload))))
-    return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
   if (L * p->chunks < p->window) return ROWRED_ERR_INVALID_ARG;
@@ -198,6 +213,20 @@ void choose_looped(const Call &c, rowred_plan *p) {
 constexpr int64_t kLdsStripeMaxGranules = int64_t(2048) * 8192;
 
 void choose_plan(const Call &c, rowred_plan *p) {
+  // RMSNorm and softmax rows of 8193-16384 granules: 8 register and up to 8
+  // LDS slots per lane hold the whole row, read once (the looped kernels
+  // read it twice).
+  if (c.window > kMaxWindow && c.window <= kWideMaxWindow &&
+      (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX)) {
+    const bool aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+    p->lanes_per_row = 1024;
+    p->threads = 1024;
+    p->chunks = (int32_t)((c.window + 1023) / 1024);
+    p->policy = kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores |
+                (aligned && c.rows * c.width * 4 > (int64_t(64) << 20) ? kPolicyXcdRemap : 0);
+    p->reserved = 0;
+    return;
+  }
   if (c.window > kMaxWindow) {
     choose_looped(c, p);
     return;

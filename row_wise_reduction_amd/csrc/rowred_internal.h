@@ -86,9 +86,11 @@ constexpr bool looped_kernel_exists(int op, int chunks) {
 }
 
 // Enqueue the LDS-stripe kernel (ROWRED_POLICY_LDS_STRIPE): RMSNorm (op 1)
-// or softmax (op 2), one 1024-lane workgroup per row, chunks 5-8 of which
-// the first kWideRegChunks stay in registers.  grid = rows.
-constexpr int kWideMaxLdsChunks = 4;
+// or softmax (op 2), one 1024-lane workgroup per row, chunks 5-16 (the first
+// 4, from 9 chunks on 8, stay in registers).  grid = rows.
+constexpr int kWideMinChunks = 5;
+constexpr int kWideMaxChunks = 16;
+constexpr int kWideMaxWindow = 1024 * kWideMaxChunks;
 int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream_t stream);
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).

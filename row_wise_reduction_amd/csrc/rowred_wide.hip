@@ -1,18 +1,21 @@
-// rowred_wide.hip -- RMSNorm and softmax rows of 4097-8192 granules held
-// half in registers, half in LDS (ROWRED_POLICY_LDS_STRIPE).
+// rowred_wide.hip -- RMSNorm and softmax rows of 4097-16384 granules held
+// partly in registers, partly in LDS (ROWRED_POLICY_LDS_STRIPE).
 //
 // A 1024-lane workgroup owns one row, and lane li owns the row's granules
-// c*1024 + li (c < 4 + CL), as in the register-resident kernels.  Held
-// entirely in registers a stripe of 5-8 granules leaves room for one such
-// workgroup per CU; here slots 0-3 live in registers and slots 4..3+CL go
-// straight from HBM into LDS (16-byte loads that write LDS, no registers in
-// between), CL * 16 KB per workgroup, so two workgroups share a CU and one's
-// loads overlap the other's collectives and stores.  Every element is still
-// read from HBM once; the LDS slots are read back by the lane that loaded
-// them (no barrier needed for that) in each phase.
-//
-// Arithmetic and its order are those of the register-resident kernel with
-// the same stripe (chunks 4 + CL, 1024 lanes): results are bitwise equal.
+// c*1024 + li (c < CR + CL), as in the register-resident kernels.  Slots
+// 0..CR-1 live in registers and slots CR..CR+CL-1 go straight from HBM into
+// LDS (16-byte loads that write LDS, no registers in between), CL * 16 KB per
+// workgroup.  Every element is read from HBM once; the LDS slots are read
+// back by the lane that loaded them (no barrier needed for that) in each
+// phase.
+//   * 5-8 slots (CR = 4): held entirely in registers such a stripe leaves
+//     room for one workgroup per CU; with half of it in LDS two share a CU,
+//     and one's loads overlap the other's collectives and stores.  The
+//     arithmetic and its order are those of the register-resident kernel
+//     with the same stripe, so results are bitwise equal.
+//   * 9-16 slots (CR = 8, up to 128 KB of LDS): rows of up to 65536 aligned
+//     floats, which no register stripe holds, are read once instead of twice
+//     (the looped kernels' two walks).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,11 +28,9 @@ namespace rowred {
 namespace {
 
 constexpr int kWideLanes = 1024;
-constexpr int kWideRegChunks = 4;
 
-template <int OP, int CL>
+template <int OP, int CR, int CL>
 __global__ void __launch_bounds__(kWideLanes) wide_kernel(RowArgs a) {
-  constexpr int CR = kWideRegChunks;
   constexpr int C = CR + CL;
   constexpr int L = kWideLanes;
   __shared__ f32x4 held[CL * L];
@@ -169,22 +170,25 @@ __global__ void __launch_bounds__(kWideLanes) wide_kernel(RowArgs a) {
 }
 
 using WideFn = void (*)(RowArgs);
-// [RMSNorm, softmax][CL - 1]
-const WideFn kWide[2][kWideMaxLdsChunks] = {
-    {wide_kernel<kOpRms, 1>, wide_kernel<kOpRms, 2>, wide_kernel<kOpRms, 3>, wide_kernel<kOpRms, 4>},
-    {wide_kernel<kOpSoftmax, 1>, wide_kernel<kOpSoftmax, 2>, wide_kernel<kOpSoftmax, 3>,
-     wide_kernel<kOpSoftmax, 4>},
-};
-static_assert(kWideMaxLdsChunks == 4 && kWideRegChunks + kWideMaxLdsChunks == 8, "wide kernel table");
+#define ROWRED_WIDE_ROW(OP)                                                                                  \
+  {wide_kernel<OP, 4, 1>, wide_kernel<OP, 4, 2>, wide_kernel<OP, 4, 3>, wide_kernel<OP, 4, 4>,              \
+   wide_kernel<OP, 8, 1>, wide_kernel<OP, 8, 2>, wide_kernel<OP, 8, 3>, wide_kernel<OP, 8, 4>,              \
+   wide_kernel<OP, 8, 5>, wide_kernel<OP, 8, 6>, wide_kernel<OP, 8, 7>, wide_kernel<OP, 8, 8>}
+// [RMSNorm, softmax][chunks - kWideMinChunks]: 4 register slots up to 8
+// chunks, 8 from 9 on.
+const WideFn kWide[2][kWideMaxChunks - kWideMinChunks + 1] = {ROWRED_WIDE_ROW(kOpRms), ROWRED_WIDE_ROW(kOpSoftmax)};
+#undef ROWRED_WIDE_ROW
+static_assert(kWideMinChunks == 5 && kWideMaxChunks == 16, "wide kernel table");
 
 }  // namespace
 
 int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream_t stream) {
-  const int cl = chunks - kWideRegChunks;
-  if ((op != kOpRms && op != kOpSoftmax) || cl < 1 || cl > kWideMaxLdsChunks) return (int)hipErrorInvalidValue;
+  if ((op != kOpRms && op != kOpSoftmax) || chunks < kWideMinChunks || chunks > kWideMaxChunks)
+    return (int)hipErrorInvalidValue;
   RowArgs a = args;
   void *params[] = {&a};
-  return (int)hipLaunchKernel(reinterpret_cast<const void *>(kWide[op == kOpSoftmax][cl - 1]), dim3((uint32_t)rows),
+  return (int)hipLaunchKernel(reinterpret_cast<const void *>(kWide[op == kOpSoftmax][chunks - kWideMinChunks]),
+                              dim3((uint32_t)rows),
                               dim3(kWideLanes), params, 0, stream);
 }
 

@@ -85,9 +85,10 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
         assert 4 * p.chunks <= 64
         lds = R.ROWRED_POLICY_LDS_STRIPE
         assert 0 <= p.policy & ~lds < 16 and p.reserved == 0
-        if p.policy & lds:  # RMSNorm / softmax, 1024 lanes, 5-8 slots, up to 2048 x 8192 granules
-            assert op in ("rmsnorm", "softmax") and L == T == 1024 and 5 <= p.chunks <= 8
-            assert rows * p.window <= 2048 * 8192 and not p.policy & R.ROWRED_POLICY_STAGE_STORES
+        if p.policy & lds:  # RMSNorm / softmax, 1024 lanes, 5-8 slots up to 2048 x 8192 granules, 9-16 slots
+            assert op in ("rmsnorm", "softmax") and L == T == 1024 and 5 <= p.chunks <= 16
+            assert p.chunks > 8 or rows * p.window <= 2048 * 8192
+            assert not p.policy & R.ROWRED_POLICY_STAGE_STORES
 
 
 def test_plan_for_workload_shapes():
@@ -99,7 +100,9 @@ def test_plan_for_workload_shapes():
              (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
              (17, 257): (32, 3, ns | st), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
-             (2048, 32768): (1024, 8, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE)}
+             (2048, 32768): (1024, 8, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE),
+             (1024, 50257): (1024, 13, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
+             (4096, 65536): (1024, 16, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE)}
     for (rows, width), (L, C, pol) in cases.items():
         p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
@@ -157,11 +160,16 @@ def test_size_errors():
     assert raw("rowred_rmsnorm", None, None, 0, 4, f(1e-6), None) == R.ROWRED_OK
     assert raw("rowred_softmax", None, None, 7, 0, None) == R.ROWRED_OK
     assert raw("rowred_layernorm_residual", None, None, None, 0, 0, f(1e-5), None) == R.ROWRED_OK
-    # rows wider than one register-resident pass loop over the row instead
-    lp = R.ROWRED_POLICY_LOOPED
-    for xx, yy, w in ((X, Y, 32769), (X + 4, Y + 4, 32768), (X, Y, 1 << 20)):
-        p = R.rowred_plan_query("softmax", xx, None, yy, rows=4, width=w)
-        assert p.policy & lp and p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
+    # rows wider than one register-resident pass: softmax and RMSNorm hold up
+    # to 16384 granules in registers and LDS, wider rows (and LayerNorm) loop
+    lp, lds = R.ROWRED_POLICY_LOOPED, R.ROWRED_POLICY_LDS_STRIPE
+    for op, xx, yy, w, want in (("softmax", X, Y, 32769, lds), ("softmax", X + 4, Y + 4, 32768, lds),
+                                ("rmsnorm", X, Y, 65536, lds), ("softmax", X + 4, Y + 4, 65536, lp),
+                                ("softmax", X, Y, 1 << 20, lp)):
+        p = R.rowred_plan_query(op, xx, None, yy, rows=4, width=w)
+        assert p.policy & want and p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
+    p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=4, width=32769)
+    assert p.policy & lp
     # widths beyond 32-bit element indices within a row
     assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
 
@@ -245,9 +253,12 @@ def test_lds_stripe_preconditions():
     ok = bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=m)._c()
     for op in (1, 2):  # zero rows: checked, nothing launched
         assert lib.rowred_run_plan(op, X, None, Y, 0, 32768, f(1e-6), ctypes.byref(ok), None) == R.ROWRED_OK
-    for kw in (dict(chunks=4, policy=m), dict(lanes_per_row=512, chunks=16, threads=512, policy=m),
+    wide = bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=m)._c()  # 8 register + 8 LDS slots
+    assert lib.rowred_run_plan(2, X, None, Y, 0, 65536, f(0), ctypes.byref(wide), None) == R.ROWRED_OK
+    for kw in (dict(chunks=4, policy=m), dict(chunks=17, policy=m), dict(lanes_per_row=512, chunks=16, threads=512, policy=m),
                dict(lanes_per_row=512, threads=1024, chunks=16, policy=m),
-               dict(policy=m | R.ROWRED_POLICY_RELOAD), dict(policy=m | R.ROWRED_POLICY_LOOPED)):
+               dict(policy=m | R.ROWRED_POLICY_RELOAD), dict(policy=m | R.ROWRED_POLICY_LOOPED),
+               dict(policy=m | R.ROWRED_POLICY_STAGE_STORES)):
         base = dict(lanes_per_row=1024, chunks=8, threads=1024)
         base.update(kw)
         c = bad_plan(**base)._c()

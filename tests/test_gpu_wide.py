@@ -86,3 +86,54 @@ def test_full_size_stress(case):
         assert_close(y1[i:i + 1].cpu().numpy(), oracle_of(case.op, x[i:i + 1]), f"{case.name} row {i}")
     del y0, y1, xd
     t.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("width", [32769, 40000, 50257, 61440, 65533, 65536])
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_rows_held_in_registers_and_lds(op, width):
+    """Rows of 8193-16384 granules (9-16 slots per lane: 8 in registers, the
+    rest in LDS), through the plain entry point and as explicit plans with
+    both memory policies, ragged and misaligned: the oracle's bar, and within
+    it of the looped kernels, which read the row twice."""
+    t = torch()
+    rows = 9
+    x = synthetic.random_matrix(width + 21, rows, width, "normal")
+    ref = oracle_of(op, x)
+    for shift, y_shift in ((0, 0), (2, 2), (1, 3)):
+        if (width + shift + 3) // 4 > 16384:
+            continue
+        xd = shifted_input(x, shift)
+        C = -(-((width + shift + 3) // 4) // 1024)
+        plan = R.rowred_plan_query(op, xd, None, Guarded(rows, width, y_shift).y)
+        assert plan.policy & LDS and plan.chunks == C, plan
+        out = Guarded(rows, width, y_shift)
+        if op == "rmsnorm":
+            R.rowred_rmsnorm(xd, out.y, eps=synthetic.EPS["rmsnorm"])
+        else:
+            R.rowred_softmax(xd, out.y)
+        t.cuda.synchronize()
+        assert out.guards_intact()
+        assert_close(out.host(), ref, f"{op} {width} entry point")
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+            wide = R.Plan(1024, 0, C, 1024, 0, policy=pol | LDS)
+            print_case("lds stripe 9-16", op, width, shift, y_shift, wide)
+            y1 = run(op, xd, wide, rows, width, shift, y_shift)
+            assert_close(y1, ref, f"{op} {width} {wide}")
+        looped = run(op, xd, R.Plan(1024, 0, 4, 1024, 0, policy=R.ROWRED_POLICY_LOOPED), rows, width, shift, y_shift)
+        assert_close(y1, looped.astype(np.float64), f"{op} {width} vs looped")
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_wide_special_values(op):
+    rows, width = 6, 65536
+    x = synthetic.random_matrix(96, rows, width, "normal")
+    x[0, :] = -np.inf
+    x[1, :60000] = -np.inf             # the max sits in the LDS slots
+    x[2, 50000] = np.nan
+    x[3, 5] = np.inf
+    x[4, 64000:] = 70.0
+    x[5, ::2] = 1e15
+    x[5, 1::2] = -1e15
+    xd = shifted_input(x, 0)
+    got = run(op, xd, R.Plan(1024, 0, 16, 1024, 0, policy=LDS), rows, width, 0)
+    assert_close(got, oracle_of(op, x), f"{op} special 16 slots")

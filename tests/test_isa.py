@@ -58,9 +58,9 @@ def test_every_kernel_is_spill_free(asm):
     # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
     # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only),
     # the exchange kernels (3 operators x 4 chunk counts, LayerNorm not at 8)
-    # and their clear kernel, the LDS-stripe kernels (2 operators x 4 stripes),
+    # and their clear kernel, the LDS-stripe kernels (2 operators x 12 stripes),
     # the LDS-stripe exchange kernels (LayerNorm 1, RMSNorm and softmax 3 each)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 8 + 7
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 7
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
@@ -245,11 +245,11 @@ def test_exchange_kernels(asm):
 
 
 def test_lds_stripe_kernels(asm):
-    """LDS-stripe kernels: 1..4 slots per lane loaded straight into LDS with
-    16-byte LDS-writing loads (a non-temporal and a cached copy), 4 register
-    slots (16-byte loads, both copies), a full wait before the first LDS read,
-    LDS sized for the slots, and registers for two 1024-thread workgroups per
-    CU (at most 64 VGPRs)."""
+    """LDS-stripe kernels: 1..8 slots per lane loaded straight into LDS with
+    16-byte LDS-writing loads (a non-temporal and a cached copy), 4 or 8
+    register slots (16-byte loads, both copies), a full wait before the first
+    LDS read, LDS sized for the slots, and registers for two 1024-thread
+    workgroups per CU (at most 64 VGPRs)."""
     meta = kernel_meta(asm)
     seen = 0
     for name, m in meta.items():
@@ -257,17 +257,17 @@ def test_lds_stripe_kernels(asm):
         if "wide_kernel<" not in dn:
             continue
         seen += 1
-        cl = int(dn.split("wide_kernel<")[1].split(",")[1].split(">")[0])
+        _, cr, cl = (int(t) for t in dn.split("wide_kernel<")[1].split(">")[0].split(","))
         body = kernel_body(asm, name)
         lines = [ln.strip() for ln in body.splitlines()]
         lds_loads = [ln for ln in lines if ln.startswith("global_load_lds_dwordx4")]
         assert len(lds_loads) == 2 * cl and sum(ln.endswith(" nt") for ln in lds_loads) == cl, (dn, lds_loads)
         nt, cached = x4_loads(body)
-        assert nt == 4 and cached == 4, (dn, nt, cached)
+        assert nt == cr and cached == cr, (dn, nt, cached)
         first_read = next(i for i, ln in enumerate(lines) if ln.startswith("ds_read_b128"))
         assert any(ln.startswith("s_waitcnt vmcnt(0)") for ln in lines[:first_read]), dn
         assert m["lds"] >= cl * 1024 * 16 and m["vgpr"] <= 64, (dn, m)
-    assert seen == 8
+    assert seen == 24
 
 
 def test_lds_stripe_exchange_kernels(asm):
