@@ -42,7 +42,9 @@
  * A NULL or misaligned pointer otherwise -> ROWRED_ERR_INVALID_ARG.  A row
  * whose 16-byte slot window (ceil((width + misalignment) / 4)) is at most
  * 8192 (width <= 32768 for 16-byte-aligned rows) is held in registers across
- * the phases and read once; a wider row is walked twice by one workgroup
+ * the phases and read once; RMSNorm and softmax rows of up to 16384 slots
+ * (width <= 65536) are held in registers and LDS (ROWRED_POLICY_LDS_STRIPE)
+ * and read once too; a wider row is walked twice by one workgroup
  * (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is read
  * twice.  That suits many rows; for few wide rows the _ws entry points at the
  * end split each row over many workgroups.  width > INT32_MAX ->
@@ -216,7 +218,7 @@ enum rowred_policy {
                                      with cached loads, then map and store (row sum and min/max:
                                      once).  NT_LOADS / NT_STORES apply to the second walk; no
                                      other bit may be set.  The entry points choose it for rows
-                                     wider than 8192 granules */
+                                     wider than 8192 granules (RMSNorm and softmax: 16384) */
   ROWRED_POLICY_EXCHANGE = 128,   /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the
@@ -226,13 +228,19 @@ enum rowred_policy {
                                      (threads <= 512; not LayerNorm).
                                      NT_LOADS / NT_STORES apply to its loads and stores;
                                      REVERSE may not be set */
-  ROWRED_POLICY_LDS_STRIPE = 256  /* RMSNorm and softmax, lanes_per_row == threads == 1024,
-                                     chunks 5-8: slots 0-3 of each lane stay in registers and
-                                     the rest are loaded straight into LDS (16-byte loads that
-                                     write LDS), so two workgroups fit a CU.  Same arithmetic
-                                     in the same order as the register-resident kernel: same
-                                     bits.  NT_LOADS / NT_STORES / XCD_REMAP apply; no other
-                                     bit may be set */
+  ROWRED_POLICY_LDS_STRIPE = 256  /* row plans: RMSNorm and softmax, lanes_per_row == threads
+                                     == 1024, chunks 5-16: slots 0-3 (from 9 chunks on 0-7)
+                                     of each lane stay in registers and the rest are loaded
+                                     straight into LDS (16-byte loads that write LDS).  At
+                                     5-8 chunks two workgroups then fit a CU, with the
+                                     register kernel's arithmetic in the same order (same
+                                     bits); at 9-16 chunks rows of up to 16384 granules are
+                                     read once.  NT_LOADS / NT_STORES / XCD_REMAP apply; no
+                                     other bit may be set.
+                                     split plans (with EXCHANGE only): 256 threads, chunks 8
+                                     (4 in registers + 4 in LDS), 12 (8 + 4) or 16 (8 + 8),
+                                     LayerNorm at 8 only; x (and r) of the LDS slots go
+                                     straight into LDS */
 };
 
 /*
