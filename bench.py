@@ -603,7 +603,7 @@ def kernel_short_name(name):
 
 
 # Kernels of the library's reduction paths (the streaming copy aside).
-LIBRARY_KERNELS = ("rows_kernel", "seg_", "looped_kernel", "exchange_clear_kernel")
+LIBRARY_KERNELS = ("rows_kernel", "seg_", "looped_kernel", "wide_kernel", "exchange_clear_kernel")
 
 
 def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=None):
