@@ -44,9 +44,11 @@
  * 8192 (width <= 32768 for 16-byte-aligned rows) is held in registers across
  * the phases and read once; RMSNorm and softmax rows of up to 16384 slots
  * (width <= 65536) are held in registers and LDS (ROWRED_POLICY_LDS_STRIPE)
- * and read once too; a wider row is walked twice by one workgroup
- * (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is read
- * twice.  That suits many rows; for few wide rows the _ws entry points at the
+ * and read once too, and of wider RMSNorm and softmax rows the first 16384
+ * slots are held that way and the rest walked twice (ROWRED_POLICY_LDS_STRIPE
+ * | ROWRED_POLICY_LOOPED); any other wider row is walked twice by one
+ * workgroup (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is
+ * read twice.  That suits many rows; for few wide rows the _ws entry points at the
  * end split each row over many workgroups.  width > INT32_MAX ->
  * ROWRED_ERR_UNSUPPORTED.
  *
@@ -218,7 +220,11 @@ enum rowred_policy {
                                      with cached loads, then map and store (row sum and min/max:
                                      once).  NT_LOADS / NT_STORES apply to the second walk; no
                                      other bit may be set.  The entry points choose it for rows
-                                     wider than 8192 granules (RMSNorm and softmax: 16384) */
+                                     wider than 8192 granules (RMSNorm and softmax: with
+                                     LDS_STRIPE, below).  With LDS_STRIPE (RMSNorm and softmax,
+                                     chunks 16, rows wider than 16384 granules): the first
+                                     16384 granules are held as LDS_STRIPE holds them and the
+                                     rest is walked twice in tiles */
   ROWRED_POLICY_EXCHANGE = 128,   /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the

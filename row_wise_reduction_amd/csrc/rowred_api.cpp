@@ -133,7 +133,28 @@ int finish_lds_plan(const Call &c, rowred_plan *p) {
   return ROWRED_OK;
 }
 
+// A plan with the head of the row in registers and LDS and the rest walked
+// twice (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED): RMSNorm or
+// softmax, one 1024-lane workgroup per row, chunks 16 (the head), rows wider
+// than the head.
+int finish_wide_tail_plan(const Call &c, rowred_plan *p) {
+  const int kop = kernel_op(c);
+  if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || p->lanes_per_row != 1024 || p->threads != 1024 ||
+      p->chunks != kWideMaxChunks)
+    return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap))
+    return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0 || c.window <= kWideMaxWindow) return ROWRED_ERR_INVALID_ARG;
+  p->window = c.window;
+  p->vector_io = c.y_vec ? 1 : 0;
+  p->rows_per_group = 1;
+  p->grid = c.rows;
+  if (p->grid > INT32_MAX || p->grid * 1024 > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
 int finish_plan(const Call &c, rowred_plan *p) {
+  if ((p->policy & kPolicyLooped) && (p->policy & kPolicyLdsStripe)) return finish_wide_tail_plan(c, p);
   if (p->policy & kPolicyLooped) return finish_looped_plan(c, p);
   if (p->policy & kPolicyLdsStripe) return finish_lds_plan(c, p);
   const int64_t L = p->lanes_per_row, T = p->threads;
@@ -224,6 +245,20 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->chunks = (int32_t)((c.window + 1023) / 1024);
     p->policy = kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores |
                 (aligned && c.rows * c.width * 4 > (int64_t(64) << 20) ? kPolicyXcdRemap : 0);
+    p->reserved = 0;
+    return;
+  }
+  // Wider RMSNorm and softmax rows: the first 16384 granules held the same
+  // way, the rest walked twice.  Faster than the looped kernels at every
+  // width measured (MI355X): 4096x65540 softmax 486 -> 417 us, 2048x128256
+  // 436 -> 381 us, 2048x131072 RMSNorm 493 -> 434 us, 1024x262144 softmax
+  // 491 -> 446 us, 512x524288 491 -> 473 us, 128x1048576 321 -> 297 us;
+  // remapping rows over the XCDs changed nothing.
+  if (c.window > kWideMaxWindow && (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX)) {
+    p->lanes_per_row = 1024;
+    p->threads = 1024;
+    p->chunks = kWideMaxChunks;
+    p->policy = kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores;
     p->reserved = 0;
     return;
   }
@@ -334,9 +369,11 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
                   ((uintptr_t)c.beta & 15) == 0)
                      ? 1
                      : 0;
-  const int err = (plan.policy & kPolicyLooped)      ? launch_looped(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
-                  : (plan.policy & kPolicyLdsStripe) ? launch_wide(kernel_op(c), plan.chunks, plan.grid, a, stream)
-                                                     : launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);
+  const bool looped = (plan.policy & kPolicyLooped) != 0, lds = (plan.policy & kPolicyLdsStripe) != 0;
+  const int err = looped && lds ? launch_wide_tail(kernel_op(c), plan.grid, a, stream)
+                  : looped      ? launch_looped(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
+                  : lds         ? launch_wide(kernel_op(c), plan.chunks, plan.grid, a, stream)
+                                : launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);
   return err == 0 ? ROWRED_OK : ROWRED_ERR_HIP;
 }
 

@@ -92,6 +92,10 @@ constexpr int kWideMinChunks = 5;
 constexpr int kWideMaxChunks = 16;
 constexpr int kWideMaxWindow = 1024 * kWideMaxChunks;
 int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream_t stream);
+// Rows wider than kWideMaxWindow (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED,
+// RMSNorm or softmax): the first kWideMaxWindow granules held as by the
+// 16-chunk LDS-stripe kernel, the rest walked twice in tiles.  grid = rows.
+int launch_wide_tail(int op, int64_t rows, const RowArgs &args, hipStream_t stream);
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);

@@ -169,6 +169,191 @@ __global__ void __launch_bounds__(kWideLanes) wide_kernel(RowArgs a) {
   else store_all(std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// Rows wider than the LDS stripe (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED):
+// the row's first 16384 granules are held as above (8 register + 8 LDS
+// slots per lane) and read once; the rest is walked in tiles of 4096
+// granules twice (statistics with cached loads, then map and store), as
+// the looped kernels walk a whole row.  Softmax keeps an online (max, sum)
+// per lane over the held part and then the tiles; RMSNorm sums squares.
+// ---------------------------------------------------------------------------
+constexpr int kTailChunks = 4;
+
+template <int OP>
+__global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
+  constexpr int CR = 8, CL = 8, C = CR + CL, L = kWideLanes, TC = kTailChunks;
+  constexpr int kHead = C * L;  // granules held
+  constexpr int kTile = TC * L;
+  __shared__ f32x4 held[CL * L];
+  __shared__ float partials[2][16];
+  constexpr int lanes_log2 = 10;
+  const int li = threadIdx.x;
+  const int width = a.width;
+  const int64_t row = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0);
+  const int64_t base = row * (int64_t)width;
+  const float *xrow = a.x + base;
+  const int off = (int)(((uintptr_t)xrow >> 2) & 3);
+  const int nwin = (width + off + 3) >> 2;
+  const int kmax = nwin - 1;
+  const int ntiles = (nwin - kHead + kTile - 1) / kTile;  // >= 1: the row is wider than the head
+  auto valid_k = [&](int k, int j) -> bool { return (unsigned)(4 * k + j - off) < (unsigned)width; };
+  const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
+  f32x4 *wave_held = held + (li & ~63);
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr float kIdent = OP == kOpSoftmax ? -__builtin_inff() : 0.0f;
+
+  // ---- the head: LDS slots, then register slots, then a full wait.
+  f32x4 xv[CR];
+  auto load_head = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    if constexpr (NT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < CL; ++c)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xw + min((CR + c) * L + li, kmax)),
+                                       (lds_void *)(wave_held + c * L), 16, 0, NT ? 2 : 0);
+#pragma unroll
+    for (int c = 0; c < CR; ++c) xv[c] = load_g<NT>(xw + min(c * L + li, kmax));
+    if constexpr (NT) asm volatile("" ::: "memory");
+  };
+  if (a.policy & kPolicyNtLoads) load_head(std::true_type{});
+  else load_head(std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0);
+  // head granule of slot c: c * L + li (all inside the row's window: the row
+  // is wider than the head)
+#pragma unroll
+  for (int c = 0; c < CR; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[c][j] = valid_k(c * L + li, j) ? xv[c][j] : kIdent;
+  auto head_at = [&](int c) -> f32x4 { return c < CR ? xv[c < CR ? c : 0] : held[(c - CR) * L + li]; };
+
+  // ---- the tail: tiles of TC slots, two deep.
+  auto tile_k = [&](int t, int c) -> int { return kHead + t * kTile + c * L + li; };
+  auto load_tile = [&](auto nt, int t, f32x4(&tv)[TC]) {
+    constexpr bool NT = decltype(nt)::value;
+    if constexpr (NT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < TC; ++c) tv[c] = load_g<NT>(xw + min(tile_k(t, c), kmax));
+    if constexpr (NT) asm volatile("" ::: "memory");
+  };
+  f32x4 ta[TC], tb[TC];
+  auto walk = [&](auto nt, auto f) {
+    load_tile(nt, 0, ta);
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load_tile(nt, t + 1, tb);
+      f(t, ta);
+      if (t + 2 < ntiles) load_tile(nt, t + 2, ta);
+      if (t + 1 < ntiles) f(t + 1, tb);
+    }
+  };
+
+  // ---- pass 1: statistics over the head, then the tail tiles.
+  float scale, m_row = 0.0f;
+  if constexpr (OP == kOpRms) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 v = head_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(v[j], v[j], acc[j]);
+    }
+    walk(std::false_type{}, [&](int t, const f32x4(&tv)[TC]) {
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = valid_k(tile_k(t, c), j) ? tv[c][j] : 0.0f;
+          acc[j] = fmaf(x, x, acc[j]);
+        }
+    });
+    const float ss = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
+    scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
+  } else {  // softmax: online (max m, sum s of exp(x - m)) per lane
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 v = head_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, v[j]);
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 v = head_at(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += v[j] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((v[j] - m) * kLog2e);
+    }
+    float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    walk(std::false_type{}, [&](int t, const f32x4(&tv)[TC]) {
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mt = fmaxf(mt, valid_k(tile_k(t, c), j) ? tv[c][j] : -__builtin_inff());
+      const float m_new = fmaxf(m, mt);
+      // rescale the running sum to the new max (no rescale while the max
+      // stays, which also covers a lane that has seen only -inf)
+      if (m_new != m) s *= __builtin_amdgcn_exp2f((m - m_new) * kLog2e);
+      m = m_new;
+      float tacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = tv[c][j];
+          const bool zero = !valid_k(tile_k(t, c), j) || x == -__builtin_inff();
+          tacc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
+        }
+      s += (tacc[0] + tacc[1]) + (tacc[2] + tacc[3]);
+    });
+    const float M = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    // an all -inf row: M = -inf, every s = 0, sum 0 and 1/sum = inf, and the
+    // map's exp(-inf - -inf) makes the row NaN, as in one pass
+    const float term = (m == M) ? s : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+    const float S = row_allreduce<SumOp>(term, lanes_log2, partials[1]);
+    m_row = M;
+    scale = __builtin_amdgcn_rcpf(S);
+  }
+
+  // ---- pass 2: map and store, the head from registers and LDS, the tail
+  // read again.
+  auto map = [&](float x) -> float {
+    if constexpr (OP == kOpRms) return x * scale;
+    else return __builtin_amdgcn_exp2f((x - m_row) * kLog2e) * scale;
+  };
+  float *yrow = a.y + base;
+  auto store_granule = [&](auto nt, int k, const float (&o)[4]) {
+    constexpr bool NT = decltype(nt)::value;
+    const int e0 = 4 * k - off;
+    if (a.y_vec && e0 >= 0 && e0 + 4 <= width) {
+      store_g<NT>(reinterpret_cast<f32x4 *>(yrow - off) + k, f32x4{o[0], o[1], o[2], o[3]});
+    } else if (k <= kmax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((unsigned)(e0 + j) < (unsigned)width) store_g<NT>(yrow + e0 + j, o[j]);
+    }
+  };
+  auto pass2 = [&](auto ntl, auto nts) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 v = head_at(c);
+      const float o[4] = {map(v[0]), map(v[1]), map(v[2]), map(v[3])};
+      store_granule(nts, c * L + li, o);
+    }
+    walk(ntl, [&](int t, const f32x4(&tv)[TC]) {
+#pragma unroll
+      for (int c = 0; c < TC; ++c) {
+        const float o[4] = {map(tv[c][0]), map(tv[c][1]), map(tv[c][2]), map(tv[c][3])};
+        store_granule(nts, tile_k(t, c), o);
+      }
+    });
+  };
+  const bool ntl = (a.policy & kPolicyNtLoads) != 0, nts = (a.policy & kPolicyNtStores) != 0;
+  if (ntl && nts) pass2(std::true_type{}, std::true_type{});
+  else if (ntl) pass2(std::true_type{}, std::false_type{});
+  else if (nts) pass2(std::false_type{}, std::true_type{});
+  else pass2(std::false_type{}, std::false_type{});
+}
+
 using WideFn = void (*)(RowArgs);
 #define ROWRED_WIDE_ROW(OP)                                                                                  \
   {wide_kernel<OP, 4, 1>, wide_kernel<OP, 4, 2>, wide_kernel<OP, 4, 3>, wide_kernel<OP, 4, 4>,              \
@@ -181,6 +366,15 @@ const WideFn kWide[2][kWideMaxChunks - kWideMinChunks + 1] = {ROWRED_WIDE_ROW(kO
 static_assert(kWideMinChunks == 5 && kWideMaxChunks == 16, "wide kernel table");
 
 }  // namespace
+
+int launch_wide_tail(int op, int64_t rows, const RowArgs &args, hipStream_t stream) {
+  if (op != kOpRms && op != kOpSoftmax) return (int)hipErrorInvalidValue;
+  RowArgs a = args;
+  void *params[] = {&a};
+  const void *fn = op == kOpRms ? reinterpret_cast<const void *>(wide_tail_kernel<kOpRms>)
+                                : reinterpret_cast<const void *>(wide_tail_kernel<kOpSoftmax>);
+  return (int)hipLaunchKernel(fn, dim3((uint32_t)rows), dim3(kWideLanes), params, 0, stream);
+}
 
 int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream_t stream) {
   if ((op != kOpRms && op != kOpSoftmax) || chunks < kWideMinChunks || chunks > kWideMaxChunks)

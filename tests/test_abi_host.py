@@ -164,12 +164,15 @@ def test_size_errors():
     # to 16384 granules in registers and LDS, wider rows (and LayerNorm) loop
     lp, lds = R.ROWRED_POLICY_LOOPED, R.ROWRED_POLICY_LDS_STRIPE
     for op, xx, yy, w, want in (("softmax", X, Y, 32769, lds), ("softmax", X + 4, Y + 4, 32768, lds),
-                                ("rmsnorm", X, Y, 65536, lds), ("softmax", X + 4, Y + 4, 65536, lp),
-                                ("softmax", X, Y, 1 << 20, lp)):
+                                ("rmsnorm", X, Y, 65536, lds), ("softmax", X + 4, Y + 4, 65536, lp | lds),
+                                ("softmax", X, Y, 1 << 20, lp | lds)):
         p = R.rowred_plan_query(op, xx, None, yy, rows=4, width=w)
-        assert p.policy & want and p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
-    p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=4, width=32769)
-    assert p.policy & lp
+        assert p.policy & (lp | lds) == want, (op, w, p)
+        assert p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
+    for op in ("layernorm_residual", "row_sum"):
+        p = R.rowred_plan_query(op, X, None, Y, rows=4, width=32769) if op != "row_sum" else \
+            R.rowred_plan_query(op, X, None, Y, rows=4, width=65537)
+        assert p.policy & lp and not p.policy & lds
     # widths beyond 32-bit element indices within a row
     assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
 
@@ -270,6 +273,26 @@ def test_lds_stripe_preconditions():
         R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_row_reduce_run_plan(3, X, 0x7F4000000000, None, 8, 32768, ctypes.byref(ok), None) == \
         R.ROWRED_ERR_INVALID_ARG
+
+
+def test_head_tail_plan_preconditions():
+    """ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED: RMSNorm and softmax,
+    1024 lanes and threads, 16 chunks (the held head), rows wider than 16384
+    granules."""
+    m = R.ROWRED_POLICY_LDS_STRIPE | R.ROWRED_POLICY_LOOPED
+    lib = R.lib()
+    ok = bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=m)._c()
+    assert lib.rowred_run_plan(2, X, None, Y, 0, 100000, f(0), ctypes.byref(ok), None) == R.ROWRED_OK
+    for op, width, kw in ((2, 65536, {}),                       # not wider than the head
+                          (2, 100000, dict(chunks=8)), (2, 100000, dict(lanes_per_row=512, threads=512)),
+                          (2, 100000, dict(policy=m | R.ROWRED_POLICY_STAGE_STORES)),
+                          (0, 100000, {})):                     # LayerNorm
+        base = dict(lanes_per_row=1024, chunks=16, threads=1024, policy=m)
+        base.update(kw)
+        c = bad_plan(**base)._c()
+        r = X + (1 << 32) if op == 0 else None
+        assert lib.rowred_run_plan(op, X, r, Y, 4, width, f(1e-5), ctypes.byref(c), None) == \
+            R.ROWRED_ERR_INVALID_ARG, (op, width, kw)
 
 
 def test_stage_policy_preconditions():

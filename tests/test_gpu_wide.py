@@ -137,3 +137,44 @@ def test_wide_special_values(op):
     xd = shifted_input(x, 0)
     got = run(op, xd, R.Plan(1024, 0, 16, 1024, 0, policy=LDS), rows, width, 0)
     assert_close(got, oracle_of(op, x), f"{op} special 16 slots")
+
+
+TAIL = R.ROWRED_POLICY_LDS_STRIPE | R.ROWRED_POLICY_LOOPED
+
+
+@pytest.mark.parametrize("width", [65537, 70001, 100003, 128256, 262147])
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_head_held_tail_walked(op, width):
+    """Rows wider than 16384 granules: the first 16384 held in registers and
+    LDS, the rest walked twice in tiles (one, two and many tiles, odd tile
+    counts, a partial last tile), ragged and misaligned, both memory
+    policies; the oracle's bar and within it of the looped kernels."""
+    rows = 5
+    x = synthetic.random_matrix(width + 31, rows, width, "normal")
+    ref = oracle_of(op, x)
+    for shift, y_shift in ((0, 0), (3, 3), (1, 2)):
+        xd = shifted_input(x, shift)
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+            plan = R.Plan(1024, 0, 16, 1024, 0, policy=pol | TAIL)
+            print_case("head + tail", op, width, shift, y_shift, plan)
+            got = run(op, xd, plan, rows, width, shift, y_shift)
+            assert_close(got, ref, f"{op} {width} {plan}")
+        looped = run(op, xd, R.Plan(1024, 0, 4, 1024, 0, policy=R.ROWRED_POLICY_LOOPED), rows, width, shift, y_shift)
+        assert_close(got, looped.astype(np.float64), f"{op} {width} vs looped")
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_head_tail_special_values(op):
+    rows, width = 7, 100000
+    x = synthetic.random_matrix(97, rows, width, "normal")
+    x[0, :] = -np.inf
+    x[1, :90000] = -np.inf             # the max only in the tail
+    x[2, 10] = np.nan                  # NaN in the head
+    x[3, 99000] = np.inf               # +inf in the tail
+    x[4, 99990:] = 80.0                # the max in the last tile: the running sum rescales
+    x[5, :65536] = -1e15               # the head far below the tail
+    x[6, ::2] = 1e15
+    x[6, 1::2] = -1e15
+    xd = shifted_input(x, 0)
+    got = run(op, xd, R.Plan(1024, 0, 16, 1024, 0, policy=TAIL), rows, width, 0)
+    assert_close(got, oracle_of(op, x), f"{op} special head + tail")

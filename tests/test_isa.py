@@ -58,9 +58,10 @@ def test_every_kernel_is_spill_free(asm):
     # statistics (5 operators x 3 chunk counts), apply (3 x 3), merge (5)
     # ... and the looped kernels (5 operators x 2 chunk counts, LayerNorm at 2 only),
     # the exchange kernels (3 operators x 4 chunk counts, LayerNorm not at 8)
-    # and their clear kernel, the LDS-stripe kernels (2 operators x 12 stripes),
-    # the LDS-stripe exchange kernels (LayerNorm 1, RMSNorm and softmax 3 each)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 7
+    # and their clear kernel, the LDS-stripe kernels (2 operators x 12 stripes,
+    # and 2 with a walked tail), the LDS-stripe exchange kernels (LayerNorm 1,
+    # RMSNorm and softmax 3 each)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 2 + 7
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
