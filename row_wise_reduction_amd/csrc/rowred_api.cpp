@@ -134,17 +134,18 @@ int finish_lds_plan(const Call &c, rowred_plan *p) {
 }
 
 // A plan with the head of the row in registers and LDS and the rest walked
-// twice (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED): RMSNorm or
-// softmax, one 1024-lane workgroup per row, chunks 16 (the head), rows wider
-// than the head.
+// twice (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED), one 1024-lane
+// workgroup per row: RMSNorm or softmax with chunks 16 (the head), LayerNorm
+// (any) with chunks 8 (x and r of 8192 granules); rows wider than the head.
 int finish_wide_tail_plan(const Call &c, rowred_plan *p) {
   const int kop = kernel_op(c);
-  if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || p->lanes_per_row != 1024 || p->threads != 1024 ||
-      p->chunks != kWideMaxChunks)
+  const bool ln = kop == ROWRED_OP_LAYERNORM_RESIDUAL || kop == kKernelOpLayerNormAffine;
+  if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX && !ln) || p->lanes_per_row != 1024 ||
+      p->threads != 1024 || p->chunks != (ln ? kLnTailHeadChunks : kWideMaxChunks))
     return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~(kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap))
     return ROWRED_ERR_INVALID_ARG;
-  if (p->reserved != 0 || c.window <= kWideMaxWindow) return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0 || c.window <= (int64_t)1024 * p->chunks) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec ? 1 : 0;
   p->rows_per_group = 1;
@@ -259,6 +260,23 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->threads = 1024;
     p->chunks = kWideMaxChunks;
     p->policy = kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores;
+    p->reserved = 0;
+    return;
+  }
+  // LayerNorm (residual, plain, affine) rows wider than 8192 granules: x and r
+  // of the first 8192 held in registers and LDS, the rest walked twice.
+  // Faster than the looped kernel at every shape measured (MI355X): residual
+  // 1024x65536 191 -> 164 us, 2048x40000 233 -> 171 us, 4096x32772 400 ->
+  // 298 us, 8192x36864 826 -> 635 us, 256x262144 211 -> 200 us; plain
+  // 1024x65536 128 -> 109 us.  Remapping rows over the XCDs pays beyond 256
+  // MiB per input (4-7%) and costs below (7%).
+  if (c.window > kMaxWindow && c.op == ROWRED_OP_LAYERNORM_RESIDUAL) {
+    const bool aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+    p->lanes_per_row = 1024;
+    p->threads = 1024;
+    p->chunks = kLnTailHeadChunks;
+    p->policy = kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores |
+                (aligned && c.rows * c.width * 4 > (int64_t(256) << 20) ? kPolicyXcdRemap : 0);
     p->reserved = 0;
     return;
   }

@@ -96,6 +96,9 @@ int launch_wide(int op, int chunks, int64_t rows, const RowArgs &args, hipStream
 // RMSNorm or softmax): the first kWideMaxWindow granules held as by the
 // 16-chunk LDS-stripe kernel, the rest walked twice in tiles.  grid = rows.
 int launch_wide_tail(int op, int64_t rows, const RowArgs &args, hipStream_t stream);
+// LayerNorm's head in that kernel: x and r of 8 granules per lane (4 in
+// registers, 4 in LDS).
+constexpr int kLnTailHeadChunks = 8;
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);

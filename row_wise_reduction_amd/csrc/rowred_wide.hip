@@ -354,6 +354,268 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
   else pass2(std::false_type{}, std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// LayerNorm (residual, plain, affine) rows wider than 8192 granules
+// (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED with chunks 8): x and r of
+// the row's first 8192 granules are held -- 4 slots of each per lane in
+// registers, 4 of each in LDS (128 KB) -- and read once; the rest is walked
+// in tiles of 2048 granules twice, as the looped LayerNorm kernel walks a
+// whole row.  Per lane, the head's (count, sum, sum of squares about its
+// mean) and then each tile's are folded into (n, mean, M2) by the pairwise
+// update of Chan, Golub and LeVeque; across lanes as in the looped kernel.
+// ---------------------------------------------------------------------------
+constexpr int kLnHeadReg = 4, kLnHeadLds = 4, kLnTailChunks = 2;
+static_assert(kLnHeadReg + kLnHeadLds == kLnTailHeadChunks, "LayerNorm head");
+
+// AFFINE: 0 none, 1 gamma/beta read 4 bytes at a time, 2 gamma/beta read
+// 16 bytes at a time (rows start on 16-byte boundaries and so do gamma and
+// beta: row granule k is gamma/beta granule k).
+template <int AFFINE>
+__global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
+  constexpr int CR = kLnHeadReg, CL = kLnHeadLds, C = CR + CL, L = kWideLanes, TC = kLnTailChunks;
+  constexpr int kHead = C * L;
+  constexpr int kTile = TC * L;
+  __shared__ f32x4 held_x[CL * L];
+  __shared__ f32x4 held_r[CL * L];
+  __shared__ double partials_d[2][16];
+  constexpr int lanes_log2 = 10;
+  const int li = threadIdx.x;
+  const int width = a.width;
+  const int64_t row = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0);
+  const int64_t base = row * (int64_t)width;
+  const float *xrow = a.x + base;
+  const bool has_r = a.r != nullptr;
+  const float *rrow = has_r ? a.r + base : nullptr;
+  const int off = (int)(((uintptr_t)xrow >> 2) & 3);
+  const int nwin = (width + off + 3) >> 2;
+  const int kmax = nwin - 1;
+  const int ntiles = (nwin - kHead + kTile - 1) / kTile;  // >= 1: the row is wider than the head
+  auto valid_k = [&](int k, int j) -> bool { return (unsigned)(4 * k + j - off) < (unsigned)width; };
+  const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
+  const f32x4 *rw = has_r ? reinterpret_cast<const f32x4 *>(rrow - off) : nullptr;
+  typedef __attribute__((address_space(3))) void lds_void;
+  f32x4 *wave_x = held_x + (li & ~63);
+  f32x4 *wave_r = held_r + (li & ~63);
+
+  // r of granule k: 16 bytes when r shares x's phase, else 4 bytes at a time
+  // at the same element positions (each index clamped into the row).
+  auto load_r = [&](auto nt, int k) -> f32x4 {
+    constexpr bool NT = decltype(nt)::value;
+    if (!has_r) return f32x4(0.0f);
+    if (a.r_vec) return load_g<NT>(rw + min(k, kmax));
+    f32x4 v;
+    const int emax = width - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load_g<NT>(rrow + max(0, min(4 * k + j - off, emax)));
+    return v;
+  };
+
+  // ---- the head.
+  f32x4 xv[CR], rv[CR];
+  auto load_head = [&](auto nt) {
+    constexpr bool NT = decltype(nt)::value;
+    if constexpr (NT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < CL; ++c)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xw + (CR + c) * L + li),
+                                       (lds_void *)(wave_x + c * L), 16, 0, NT ? 2 : 0);
+    if (has_r && a.r_vec) {
+#pragma unroll
+      for (int c = 0; c < CL; ++c)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(rw + (CR + c) * L + li),
+                                         (lds_void *)(wave_r + c * L), 16, 0, NT ? 2 : 0);
+    }
+#pragma unroll
+    for (int c = 0; c < CR; ++c) xv[c] = load_g<NT>(xw + c * L + li);
+#pragma unroll
+    for (int c = 0; c < CR; ++c) rv[c] = load_r(nt, c * L + li);
+    if constexpr (NT) asm volatile("" ::: "memory");
+  };
+  if (a.policy & kPolicyNtLoads) load_head(std::true_type{});
+  else load_head(std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0);
+  if (!(has_r && a.r_vec)) {
+    // r at another phase than x (4-byte loads), or no residual: the lane
+    // fills its own LDS slots of r
+#pragma unroll
+    for (int c = 0; c < CL; ++c) held_r[c * L + li] = load_r(std::false_type{}, (CR + c) * L + li);
+  }
+  // Head granules are all inside the row but the first, which may start
+  // before it: its elements outside the row become 0 (x and r).
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool in = valid_k(li, j);
+    xv[0][j] = in ? xv[0][j] : 0.0f;
+    rv[0][j] = in ? rv[0][j] : 0.0f;
+  }
+  auto head_x = [&](int c) -> f32x4 { return c < CR ? xv[c < CR ? c : 0] : held_x[(c - CR) * L + li]; };
+  auto head_r = [&](int c) -> f32x4 { return c < CR ? rv[c < CR ? c : 0] : held_r[(c - CR) * L + li]; };
+  // x + r as the exact pair (h, l) (TwoSum).
+  auto pair = [&](float x, float r, float &h, float &l) {
+    h = x + r;
+    const float bb = h - x;
+    l = (x - (h - bb)) + (r - bb);
+  };
+
+  // ---- the tail: tiles of TC slots of x and r, two deep.
+  auto tile_k = [&](int t, int c) -> int { return kHead + t * kTile + c * L + li; };
+  auto load_tile = [&](auto nt, int t, f32x4(&tx)[TC], f32x4(&tr)[TC]) {
+    constexpr bool NT = decltype(nt)::value;
+    if constexpr (NT) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < TC; ++c) tx[c] = load_g<NT>(xw + min(tile_k(t, c), kmax));
+#pragma unroll
+    for (int c = 0; c < TC; ++c) tr[c] = load_r(nt, tile_k(t, c));
+    if constexpr (NT) asm volatile("" ::: "memory");
+  };
+  f32x4 xa[TC], ra[TC], xb[TC], rb[TC];
+  auto walk = [&](auto nt, auto f) {
+    load_tile(nt, 0, xa, ra);
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load_tile(nt, t + 1, xb, rb);
+      f(t, xa, ra);
+      if (t + 2 < ntiles) load_tile(nt, t + 2, xa, ra);
+      if (t + 1 < ntiles) f(t + 1, xb, rb);
+    }
+  };
+
+  // ---- pass 1: per-lane (n, mean, M2), the head first.
+  double n_l, mean_l, m2_l;
+  {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = head_x(c), r4 = head_r(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h, l;
+        pair(xx[j], r4[j], h, l);
+        acc[j] += (double)h;
+        acc_lo += l;
+      }
+    }
+    const int n_h = 4 * C - (li == 0 ? off : 0);  // the first granule may start before the row
+    const double s_h = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo;
+    const double mu = s_h / (double)n_h;
+    const float th = (float)mu;
+    const float tl = (float)(mu - (double)th);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const f32x4 xx = head_x(c), r4 = head_r(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float h, l;
+        pair(xx[j], r4[j], h, l);
+        const float d = (c == 0 && !valid_k(li, j)) ? 0.0f : (h - th) + (l - tl);
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+    }
+    n_l = (double)n_h;
+    mean_l = mu;
+    m2_l = (double)((sq[0] + sq[1]) + (sq[2] + sq[3]));
+  }
+  walk(std::false_type{}, [&](int t, const f32x4(&tx)[TC], const f32x4(&tr)[TC]) {
+    float hi[4 * TC], lo[4 * TC];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    float acc_lo = 0.0f;
+    int n_t = 0;
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = valid_k(tile_k(t, c), j);
+        pair(in ? tx[c][j] : 0.0f, in ? tr[c][j] : 0.0f, hi[4 * c + j], lo[4 * c + j]);
+        acc[j] += (double)hi[4 * c + j];
+        acc_lo += lo[4 * c + j];
+        n_t += in ? 1 : 0;
+      }
+    if (n_t == 0) return;
+    const double mu_t = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo) / (double)n_t;
+    const float th = (float)mu_t;
+    const float tl = (float)(mu_t - (double)th);
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * c + j;
+        const float d = valid_k(tile_k(t, c), j) ? (hi[i] - th) + (lo[i] - tl) : 0.0f;
+        sq[j] = fmaf(d, d, sq[j]);
+      }
+    const double m2_t = (double)((sq[0] + sq[1]) + (sq[2] + sq[3]));
+    const double n = n_l + (double)n_t;
+    const double delta = mu_t - mean_l;
+    mean_l += delta * ((double)n_t / n);
+    m2_l += m2_t + delta * delta * (n_l * (double)n_t / n);
+    n_l = n;
+  });
+  const double mean = row_allreduce<SumOp>(n_l * mean_l, lanes_log2, partials_d[0]) / (double)width;
+  const double dm = mean_l - mean;
+  const double m2 = row_allreduce<SumOp>(m2_l + n_l * dm * dm, lanes_log2, partials_d[1]);
+  const float m_hi = (float)mean;
+  const float m_lo = (float)(mean - (double)m_hi);
+  const float rstd = __builtin_amdgcn_rsqf(fmaf((float)m2, a.inv_width, a.eps));
+
+  // ---- pass 2: map and store.
+  float *yrow = a.y + base;
+  constexpr bool affine = AFFINE != 0;
+  const int emax = width - 1;
+  auto map_granule = [&](int k, const f32x4 &xx, const f32x4 &r4, float (&o)[4]) {
+    f32x4 g4 = f32x4(1.0f), b4 = f32x4(0.0f);
+    if constexpr (AFFINE == 2) {
+      const int kk = min(k, kmax);
+      if (a.gamma) g4 = load_g<false>(reinterpret_cast<const f32x4 *>(a.gamma) + kk);
+      if (a.beta) b4 = load_g<false>(reinterpret_cast<const f32x4 *>(a.beta) + kk);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float h, l;
+      pair(xx[j], r4[j], h, l);
+      const float y = ((h - m_hi) + (l - m_lo)) * rstd;
+      if constexpr (AFFINE == 1) {
+        const int e = max(0, min(4 * k + j - off, emax));
+        o[j] = fmaf(y, a.gamma ? a.gamma[e] : 1.0f, a.beta ? a.beta[e] : 0.0f);
+      } else {
+        o[j] = affine ? fmaf(y, g4[j], b4[j]) : y;
+      }
+    }
+  };
+  auto store_granule = [&](auto nt, int k, const float (&o)[4]) {
+    constexpr bool NT = decltype(nt)::value;
+    const int e0 = 4 * k - off;
+    if (a.y_vec && e0 >= 0 && e0 + 4 <= width) {
+      store_g<NT>(reinterpret_cast<f32x4 *>(yrow - off) + k, f32x4{o[0], o[1], o[2], o[3]});
+    } else if (k <= kmax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((unsigned)(e0 + j) < (unsigned)width) store_g<NT>(yrow + e0 + j, o[j]);
+    }
+  };
+  auto pass2 = [&](auto ntl, auto nts) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float o[4];
+      map_granule(c * L + li, head_x(c), head_r(c), o);
+      store_granule(nts, c * L + li, o);
+    }
+    walk(ntl, [&](int t, const f32x4(&tx)[TC], const f32x4(&tr)[TC]) {
+#pragma unroll
+      for (int c = 0; c < TC; ++c) {
+        float o[4];
+        map_granule(tile_k(t, c), tx[c], tr[c], o);
+        store_granule(nts, tile_k(t, c), o);
+      }
+    });
+  };
+  const bool ntl = (a.policy & kPolicyNtLoads) != 0, nts = (a.policy & kPolicyNtStores) != 0;
+  if (ntl && nts) pass2(std::true_type{}, std::true_type{});
+  else if (ntl) pass2(std::true_type{}, std::false_type{});
+  else if (nts) pass2(std::false_type{}, std::true_type{});
+  else pass2(std::false_type{}, std::false_type{});
+}
+
 using WideFn = void (*)(RowArgs);
 #define ROWRED_WIDE_ROW(OP)                                                                                  \
   {wide_kernel<OP, 4, 1>, wide_kernel<OP, 4, 2>, wide_kernel<OP, 4, 3>, wide_kernel<OP, 4, 4>,              \
@@ -368,11 +630,15 @@ static_assert(kWideMinChunks == 5 && kWideMaxChunks == 16, "wide kernel table");
 }  // namespace
 
 int launch_wide_tail(int op, int64_t rows, const RowArgs &args, hipStream_t stream) {
-  if (op != kOpRms && op != kOpSoftmax) return (int)hipErrorInvalidValue;
+  if (op != kOpRms && op != kOpSoftmax && op != kOpLayerNorm && op != kOpLayerNormAffine)
+    return (int)hipErrorInvalidValue;
   RowArgs a = args;
   void *params[] = {&a};
-  const void *fn = op == kOpRms ? reinterpret_cast<const void *>(wide_tail_kernel<kOpRms>)
-                                : reinterpret_cast<const void *>(wide_tail_kernel<kOpSoftmax>);
+  const void *fn = op == kOpRms       ? reinterpret_cast<const void *>(wide_tail_kernel<kOpRms>)
+                   : op == kOpSoftmax ? reinterpret_cast<const void *>(wide_tail_kernel<kOpSoftmax>)
+                   : op == kOpLayerNorm ? reinterpret_cast<const void *>(ln_tail_kernel<0>)
+                   : a.affine_vec       ? reinterpret_cast<const void *>(ln_tail_kernel<2>)
+                                        : reinterpret_cast<const void *>(ln_tail_kernel<1>);
   return (int)hipLaunchKernel(fn, dim3((uint32_t)rows), dim3(kWideLanes), params, 0, stream);
 }
 

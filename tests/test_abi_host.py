@@ -169,10 +169,11 @@ def test_size_errors():
         p = R.rowred_plan_query(op, xx, None, yy, rows=4, width=w)
         assert p.policy & (lp | lds) == want, (op, w, p)
         assert p.lanes_per_row == p.threads == 1024 and p.grid == 4 and p.rows_per_group == 1
-    for op in ("layernorm_residual", "row_sum"):
-        p = R.rowred_plan_query(op, X, None, Y, rows=4, width=32769) if op != "row_sum" else \
-            R.rowred_plan_query(op, X, None, Y, rows=4, width=65537)
-        assert p.policy & lp and not p.policy & lds
+    # LayerNorm holds x and r of its first 8192 granules; row sum loops
+    p = R.rowred_plan_query("layernorm_residual", X, None, Y, rows=4, width=32769)
+    assert p.policy & (lp | lds) == lp | lds and p.chunks == 8
+    p = R.rowred_plan_query("row_sum", X, None, Y, rows=4, width=65537)
+    assert p.policy & lp and not p.policy & lds
     # widths beyond 32-bit element indices within a row
     assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
 
@@ -276,17 +277,20 @@ def test_lds_stripe_preconditions():
 
 
 def test_head_tail_plan_preconditions():
-    """ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED: RMSNorm and softmax,
-    1024 lanes and threads, 16 chunks (the held head), rows wider than 16384
-    granules."""
+    """ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED: 1024 lanes and threads;
+    RMSNorm and softmax with 16 chunks (the held head), rows wider than 16384
+    granules; LayerNorm with 8, rows wider than 8192."""
     m = R.ROWRED_POLICY_LDS_STRIPE | R.ROWRED_POLICY_LOOPED
     lib = R.lib()
     ok = bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=m)._c()
     assert lib.rowred_run_plan(2, X, None, Y, 0, 100000, f(0), ctypes.byref(ok), None) == R.ROWRED_OK
+    ln = bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=m)._c()  # LayerNorm: x and r of 8 slots
+    assert lib.rowred_run_plan(0, X, X + (1 << 32), Y, 0, 40000, f(1e-5), ctypes.byref(ln), None) == R.ROWRED_OK
     for op, width, kw in ((2, 65536, {}),                       # not wider than the head
                           (2, 100000, dict(chunks=8)), (2, 100000, dict(lanes_per_row=512, threads=512)),
                           (2, 100000, dict(policy=m | R.ROWRED_POLICY_STAGE_STORES)),
-                          (0, 100000, {})):                     # LayerNorm
+                          (0, 100000, {}),                      # LayerNorm takes 8 chunks
+                          (0, 32768, dict(chunks=8))):          # LayerNorm row not wider than its head
         base = dict(lanes_per_row=1024, chunks=16, threads=1024, policy=m)
         base.update(kw)
         c = bad_plan(**base)._c()
@@ -595,8 +599,12 @@ def test_looped_layernorm_needs_two_chunks():
                policy=R.ROWRED_POLICY_LOOPED)._c()
     assert R.lib().rowred_run_plan(0, X, RR, Y, 4, 100000, f(1e-5), ctypes.byref(c), None) == \
         R.ROWRED_ERR_INVALID_ARG
+    c2 = R.Plan(lanes_per_row=1024, rows_per_group=0, chunks=2, threads=1024, grid=0,
+                policy=R.ROWRED_POLICY_LOOPED)._c()
+    assert R.lib().rowred_run_plan(0, X, RR, Y, 0, 100000, f(1e-5), ctypes.byref(c2), None) == R.ROWRED_OK
+    # the entry point holds x and r of the first 8192 granules instead
     p = R.rowred_plan_query("layernorm_residual", X, RR, Y, rows=4, width=100000)
-    assert p.chunks == 2 and p.policy & R.ROWRED_POLICY_LOOPED
+    assert p.chunks == 8 and p.policy & R.ROWRED_POLICY_LOOPED and p.policy & R.ROWRED_POLICY_LDS_STRIPE
 
 
 

@@ -178,3 +178,87 @@ def test_head_tail_special_values(op):
     xd = shifted_input(x, 0)
     got = run(op, xd, R.Plan(1024, 0, 16, 1024, 0, policy=TAIL), rows, width, 0)
     assert_close(got, oracle_of(op, x), f"{op} special head + tail")
+
+
+def run_ln(x, r, g, b, plan, shift_x, shift_r, shift_y):
+    t = torch()
+    rows, width = x.shape
+    xd = shifted_input(x, shift_x)
+    rd = shifted_input(r, shift_r) if r is not None else None
+    gd = t.from_numpy(g).cuda() if g is not None else None
+    bd = t.from_numpy(b).cuda() if b is not None else None
+    out = Guarded(rows, width, shift_y)
+    if plan is None:
+        R.rowred_layernorm(xd, rd, gd, bd, out.y, eps=1e-5)
+    else:
+        R.rowred_layernorm_run_plan(xd, rd, gd, bd, out.y, plan, eps=1e-5)
+    t.cuda.synchronize()
+    assert out.guards_intact()
+    return out.host()
+
+
+@pytest.mark.parametrize("width", [32769, 40003, 65536, 100003])
+@pytest.mark.parametrize("variant", ["residual", "plain", "affine"])
+def test_layernorm_head_held_tail_walked(variant, width):
+    """LayerNorm rows wider than 8192 granules: x and r of the first 8192
+    held in registers and LDS, the rest walked twice; through the entry point
+    and as an explicit plan, r at x's phase and at another, both memory
+    policies; the oracle's bar and within it of the looped kernel."""
+    import oracle
+    rows = 5
+    x = synthetic.random_matrix(width + 41, rows, width, "uniform")
+    r = synthetic.random_matrix(width + 42, rows, width, "uniform", tensor="r") if variant == "residual" else None
+    g = b = None
+    if variant == "affine":
+        g = (1.0 + 0.1 * synthetic.random_matrix(width + 43, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
+        b = (0.1 * synthetic.random_matrix(width + 44, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
+    ref = oracle.layernorm(x, r, eps=1e-5, gamma=g, beta=b)
+    for sx, sr, sy in ((0, 0, 0), (1, 1, 1), (2, 3, 2)):
+        got = run_ln(x, r, g, b, None, sx, sr, sy)
+        assert_close(got, ref, f"{variant} {width} entry point")
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+            plan = R.Plan(1024, 0, 8, 1024, 0, policy=pol | TAIL)
+            print_case("layernorm head + tail", variant, width, sx, sr, sy, plan)
+            assert_close(run_ln(x, r, g, b, plan, sx, sr, sy), ref, f"{variant} {width} {plan}")
+        looped = run_ln(x, r, g, b, R.Plan(1024, 0, 2, 1024, 0, policy=R.ROWRED_POLICY_LOOPED), sx, sr, sy)
+        assert_close(got, looped.astype(np.float64), f"{variant} {width} vs looped")
+
+
+def test_layernorm_head_tail_offset_rows():
+    """Rows with a large common offset (spread << magnitude): the TwoSum pair
+    and the FP64 statistics keep the centred values exact."""
+    import oracle
+    rows, width = 4, 70001
+    x = (synthetic.random_matrix(301, rows, width, "uniform") + 1e4).astype(np.float32)
+    r = synthetic.random_matrix(302, rows, width, "uniform", tensor="r")
+    ref = oracle.layernorm(x, r, eps=1e-5)
+    assert_close(run_ln(x, r, None, None, R.Plan(1024, 0, 8, 1024, 0, policy=TAIL), 1, 1, 1), ref, "offset rows")
+
+
+@pytest.mark.parametrize("which", ["gamma", "beta", "both", "gamma_offset"])
+def test_layernorm_head_tail_affine_loads(which):
+    """gamma and/or beta over the head and the tail: read 16 bytes at a time
+    when rows, gamma and beta start on 16-byte boundaries, else 4 bytes at a
+    time (gamma_offset: gamma one element past an aligned start)."""
+    import oracle
+    t = torch()
+    rows, width = 3, 65536 + 4096
+    x = synthetic.random_matrix(311, rows, width, "uniform")
+    r = synthetic.random_matrix(312, rows, width, "uniform", tensor="r")
+    g = (1.0 + 0.1 * synthetic.random_matrix(313, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
+    b = (0.1 * synthetic.random_matrix(314, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
+    use_g = which != "beta"
+    use_b = which in ("beta", "both", "gamma_offset")
+    ref = oracle.layernorm(x, r, eps=1e-5, gamma=g if use_g else None, beta=b if use_b else None)
+    xd = shifted_input(x, 0)
+    rd = shifted_input(r, 0)
+    gd = shifted_input(g[None, :], 1 if which == "gamma_offset" else 0)[0] if use_g else None
+    bd = t.from_numpy(b).cuda() if use_b else None
+    out = Guarded(rows, width, 0)
+    plan = R.rowred_layernorm_plan_query(xd, rd, gd, bd, out.y)
+    assert plan.policy & TAIL == TAIL and plan.chunks == 8
+    print_case("layernorm head + tail affine", which, plan)
+    R.rowred_layernorm(xd, rd, gd, bd, out.y, eps=1e-5)
+    t.cuda.synchronize()
+    assert out.guards_intact()
+    assert_close(out.host(), ref, f"affine {which}")
