@@ -49,7 +49,7 @@
  * | ROWRED_POLICY_LOOPED); any other wider row is walked twice by one
  * workgroup (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is
  * read twice.  That suits many rows; for few wide rows the _ws entry points at the
- * end split each row over many workgroups.  width > INT32_MAX ->
+ * end split each row over many workgroups.  width > ROWRED_MAX_WIDTH ->
  * ROWRED_ERR_UNSUPPORTED.
  *
  * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
@@ -65,6 +65,12 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* Widest row any entry point takes: 2^31 - 2^20 - 1 floats.  The kernels
+ * index a row's elements, and the 16-byte granules past its end that their
+ * last tile or segment covers, in 32-bit integers; this keeps every such
+ * index below 2^31. */
+#define ROWRED_MAX_WIDTH 2146435071LL
 
 #ifdef __cplusplus
 extern "C" {

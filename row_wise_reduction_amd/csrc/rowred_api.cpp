@@ -83,7 +83,7 @@ int check_call(int op, const float *x, const float *r, const float *y, int64_t r
   out->r_vec = out->y_vec = false;
   out->window = 0;
   if (rows == 0 || width == 0) return ROWRED_OK;
-  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (width > ROWRED_MAX_WIDTH || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
   if (!x || !y || (need_r && !r)) return ROWRED_ERR_INVALID_ARG;
   if (((uintptr_t)x & 3) || ((uintptr_t)y & 3) || (r && ((uintptr_t)r & 3))) return ROWRED_ERR_INVALID_ARG;
   const int64_t bytes = rows * width * 4;
@@ -424,7 +424,7 @@ int check_reduce_call(int op, const float *x, float *out0, float *out1, int64_t 
   out->window = 0;
   if (rows == 0) return ROWRED_OK;
   if (width == 0) return ROWRED_ERR_INVALID_ARG;  // a row needs at least one element
-  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (width > ROWRED_MAX_WIDTH || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
   if (!x || !out0 || (op == ROWRED_OP_ROW_MINMAX && !out1)) return ROWRED_ERR_INVALID_ARG;
   if (((uintptr_t)x & 3) || ((uintptr_t)out0 & 3) || (out->y2 && ((uintptr_t)out1 & 3))) return ROWRED_ERR_INVALID_ARG;
   const uintptr_t px = (uintptr_t)x, nx = (uintptr_t)(rows * width * 4), no = (uintptr_t)rows * 4;
@@ -850,7 +850,7 @@ ROWRED_API int rowred_workspace_size(int op, int64_t rows, int64_t width, size_t
   if (op < 0 || op > ROWRED_OP_ROW_MINMAX || rows < 0 || width < 0) return ROWRED_ERR_INVALID_ARG;
   *bytes = 0;
   if (rows == 0 || width == 0) return ROWRED_OK;
-  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (width > ROWRED_MAX_WIDTH || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
   // enough for the three split kernels and for the exchange kernels at the
   // worst 16-byte phase of x.  (An x whose own window admits the exchange
   // kernels where the worst phase does not needs fewer, wider segments than
@@ -908,7 +908,7 @@ ROWRED_API int rowred_split_plan_query(int op, const float *x, int64_t rows, int
     return ROWRED_OK;
   }
   if (!x || ((uintptr_t)x & 3)) return ROWRED_ERR_INVALID_ARG;
-  if (width > INT32_MAX || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
+  if (width > ROWRED_MAX_WIDTH || rows > INT64_MAX / width || rows * width > INT64_MAX / 4) return ROWRED_ERR_UNSUPPORTED;
   Call c;
   c.op = op;
   c.x = x;
@@ -935,7 +935,7 @@ ROWRED_API const char *rowred_status_string(int status) {
     case ROWRED_OK: return "ok";
     case ROWRED_ERR_INVALID_ARG: return "invalid argument (size, pointer, eps or plan)";
     case ROWRED_ERR_ALIAS: return "output overlaps an input";
-    case ROWRED_ERR_UNSUPPORTED: return "size beyond the library's limits (width above INT32_MAX or launch grid too large)";
+    case ROWRED_ERR_UNSUPPORTED: return "size beyond the library's limits (width above ROWRED_MAX_WIDTH or launch grid too large)";
     case ROWRED_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

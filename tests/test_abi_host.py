@@ -178,6 +178,24 @@ def test_size_errors():
     assert raw("rowred_rmsnorm", X, Y, 1, 1 << 40, f(1e-6), None) == R.ROWRED_ERR_UNSUPPORTED
 
 
+def test_max_width():
+    """ROWRED_MAX_WIDTH leaves 2^20 elements of headroom below 2^31 for the
+    kernels' 32-bit element and granule indices (a last tile or segment runs
+    up to 16384 granules past the row); one more element is refused before
+    anything launches, by every family of entry points."""
+    M = R.ROWRED_MAX_WIDTH
+    assert M == 2**31 - 2**20 - 1
+    assert M + 3 + 4 * 16384 * 4 < 2**31
+    for w, want in ((M + 1, R.ROWRED_ERR_UNSUPPORTED), (2**31 - 1, R.ROWRED_ERR_UNSUPPORTED)):
+        assert raw("rowred_rmsnorm", X, Y, 1, w, f(1e-6), None) == want
+        assert raw("rowred_softmax_ws", X, Y, 1, w, RR + (1 << 36), 1 << 30, None) == want
+        assert raw("rowred_row_sum", X, Y, 1, w, None) == want
+        assert raw("rowred_layernorm_residual", X, RR, Y, 1, w, f(1e-5), None) == want
+    for op in ("softmax", "rmsnorm", "layernorm_residual", "row_sum"):
+        p = R.rowred_plan_query(op, X, None, Y, rows=1, width=M)
+        assert p.grid == 1 and p.policy & R.ROWRED_POLICY_LOOPED, (op, p)
+
+
 def test_pointer_errors():
     assert raw("rowred_rmsnorm", None, Y, 4, 4, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
     assert raw("rowred_rmsnorm", X, None, 4, 4, f(1e-6), None) == R.ROWRED_ERR_INVALID_ARG
