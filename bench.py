@@ -124,6 +124,12 @@ class CaseBuffers:
         x = synthetic.case_input(case, "x")
         r = synthetic.case_input(case, "r") if case.op == "layernorm_residual" else None
         self.host_x, self.host_r = x, r
+        # the run record: each input's seed entropy and the SHA-256 of its
+        # first and last MiB
+        self.inputs = {t: {"seed_entropy": [int(v) for v in
+                                            synthetic.seed_sequence(case.cfg, case.op, t, case.rows, case.width).entropy],
+                           "sha256_first_last_MiB": synthetic.fingerprint(a)}
+                       for t, a in (("x", x), ("r", r)) if a is not None}
         self.host_g = self.host_b = None
         self.g = self.b = None
         if case.op == "layernorm_affine":
@@ -245,6 +251,36 @@ def replay_timed(graphs):
     return [a.elapsed_time(b) for a, b in evs], evs[0][0].elapsed_time(evs[-1][1])
 
 
+def aa_control(b, steps, rounds=5):
+    """A/A control: two separately captured, identical graphs of `steps`
+    calls on the same rotating buffers, replayed alternately `rounds` times.
+    Their medians differ only by noise; the relative difference bounds what
+    any A/B comparison on this machine can resolve."""
+    import torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    b.call(i)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(stream)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    us = [[], []]
+    for _ in range(rounds):
+        ms, _ = replay_timed(graphs)
+        for k in range(2):
+            us[k].append(ms[k] * 1e3 / steps)
+    a, a2 = float(np.median(us[0])), float(np.median(us[1]))
+    return {"a_us": round(a, 3), "a_prime_us": round(a2, 3), "rounds": rounds,
+            "rel_diff": round(abs(a - a2) / min(a, a2), 4)}
+
+
 def single_and_warm(b, steps, reps=3):
     """(cold single call us, warm us per call): one eager call after a 1 GiB
     flush, median of `reps`; and a graph of `steps` calls all on buffer set
@@ -342,7 +378,8 @@ def bench(cfg, steps, warmup, cpu_seconds):
             "frac_of_copy": round(gbs / copy["GB_s"], 4),
             "rounds_us": {"n": len(r_us), "median": round(float(np.median(r_us)), 3),
                           "min": round(min(r_us), 3), "max": round(max(r_us), 3)},
-            "single_call_cold_us": round(cold, 3), "warm_us_per_call": round(warm, 3)}
+            "single_call_cold_us": round(cold, 3), "warm_us_per_call": round(warm, 3),
+            "inputs": b.inputs}
     dom = int(np.argmax(per_case_ms))
     dc = cases[dom]
     dom_us = per_case_ms[dom] * 1e3 / steps
@@ -351,6 +388,7 @@ def bench(cfg, steps, warmup, cpu_seconds):
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(cfg, dc),
             "kernel": f"{dc.op} {dc.rows}x{dc.width}", "bytes_per_launch": algo_bytes(dc),
             "avg_launch_us": round(dom_us, 3)}
+    aa = aa_control(bufs[dom], steps)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -368,6 +406,7 @@ def bench(cfg, steps, warmup, cpu_seconds):
     out["copy_ceiling"] = {"same_bytes_as_dominant": copy_ceiling(algo_bytes(dc)),
                            "1GiB": copy_ceiling(2 ** 30, reps=10)}
     out["launch_floor_us"] = launch_floor()
+    out["aa_control"] = dict(kernel=f"{dc.op} {dc.rows}x{dc.width}", **aa)
     if cfg == 2:
         out["context_m1max_us"] = M1MAX_CONTEXT_US
     if cpu_seconds > 0:
