@@ -44,13 +44,13 @@
  * 8192 (width <= 32768 for 16-byte-aligned rows) is held in registers across
  * the phases and read once; RMSNorm and softmax rows of up to 16384 slots
  * (width <= 65536) are held in registers and LDS (ROWRED_POLICY_LDS_STRIPE)
- * and read once too, and of wider RMSNorm and softmax rows the first 16384
- * slots are held that way and the rest walked twice (ROWRED_POLICY_LDS_STRIPE
- * | ROWRED_POLICY_LOOPED); any other wider row is walked twice by one
- * workgroup (ROWRED_POLICY_LOOPED: statistics, then map and store), so it is
- * read twice.  That suits many rows; for few wide rows the _ws entry points at the
- * end split each row over many workgroups.  width > ROWRED_MAX_WIDTH ->
- * ROWRED_ERR_UNSUPPORTED.
+ * and read once too.  Of wider RMSNorm and softmax rows the first 16384
+ * slots are held that way, of wider LayerNorm rows x and r of the first 8192,
+ * and the rest is walked twice (ROWRED_POLICY_LDS_STRIPE |
+ * ROWRED_POLICY_LOOPED).  Wider row sum and min/max rows are walked once by
+ * one workgroup (ROWRED_POLICY_LOOPED).  That suits many rows; for few
+ * wide rows the _ws entry points at the end split each row over many
+ * workgroups.  width > ROWRED_MAX_WIDTH -> ROWRED_ERR_UNSUPPORTED.
  *
  * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
  * accepted; a LayerNorm row with zero variance then gives NaN (0/0), as
@@ -216,21 +216,27 @@ enum rowred_policy {
                                      gamma/beta, RMSNorm, softmax), chunks <= 8, LayerNorm at
                                      7-8 chunks with threads <= 512; never chosen by the
                                      entry points */
-  ROWRED_POLICY_REVERSE = 32,     /* split plans only (rowred_split_plan): the apply kernel
-                                     walks the (row, segment) pairs in reverse order, so
-                                     that it first reads again what the statistics kernel
-                                     read last; measured no faster, never chosen */
+  ROWRED_POLICY_REVERSE = 32,     /* split plans (rowred_split_plan): the apply kernel walks
+                                     the (row, segment) pairs in reverse order, so that it
+                                     first reads again what the statistics kernel read last;
+                                     head+tail row plans (LOOPED | LDS_STRIPE, below): the
+                                     second walk takes the tail last tile first.  Measured
+                                     no faster, never chosen */
   ROWRED_POLICY_LOOPED = 64,      /* rows of any width: lanes_per_row == threads, one row per
                                      workgroup, which walks the row in tiles of threads * chunks
                                      granules (chunks 2 or 4; LayerNorm 2) twice -- statistics
                                      with cached loads, then map and store (row sum and min/max:
-                                     once).  NT_LOADS / NT_STORES apply to the second walk; no
-                                     other bit may be set.  The entry points choose it for rows
-                                     wider than 8192 granules (RMSNorm and softmax: with
-                                     LDS_STRIPE, below).  With LDS_STRIPE (RMSNorm and softmax,
-                                     chunks 16, rows wider than 16384 granules): the first
-                                     16384 granules are held as LDS_STRIPE holds them and the
-                                     rest is walked twice in tiles */
+                                     once).  NT_LOADS / NT_STORES apply to the second walk,
+                                     XCD_REMAP to the row order; no other bit may be set.  The
+                                     entry points choose it for row sum and min/max rows wider
+                                     than 8192 granules.  With LDS_STRIPE (rows wider than the
+                                     held head): RMSNorm and softmax with chunks 16 hold the
+                                     first 16384 granules as LDS_STRIPE holds them, LayerNorm
+                                     with chunks 8 holds x and r of the first 8192 (4 register
+                                     and 4 LDS slots of each), and the rest is walked twice in
+                                     tiles; REVERSE then walks the tail last tile first in the
+                                     second walk and maps the head after it (measured within
+                                     3% either way, not chosen) */
   ROWRED_POLICY_EXCHANGE = 128,   /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the

@@ -105,7 +105,7 @@ int finish_looped_plan(const Call &c, rowred_plan *p) {
   const int64_t L = p->lanes_per_row, T = p->threads;
   if (L != T || !is_pow2(T) || T < 64 || T > 1024) return ROWRED_ERR_INVALID_ARG;
   if (!looped_kernel_exists(kernel_op(c), p->chunks)) return ROWRED_ERR_INVALID_ARG;
-  if (p->policy & ~(kPolicyLooped | kPolicyNtLoads | kPolicyNtStores)) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
@@ -143,7 +143,8 @@ int finish_wide_tail_plan(const Call &c, rowred_plan *p) {
   if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX && !ln) || p->lanes_per_row != 1024 ||
       p->threads != 1024 || p->chunks != (ln ? kLnTailHeadChunks : kWideMaxChunks))
     return ROWRED_ERR_INVALID_ARG;
-  if (p->policy & ~(kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap))
+  if (p->policy & ~(kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap |
+                    kPolicyReverse))
     return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0 || c.window <= (int64_t)1024 * p->chunks) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
@@ -221,15 +222,23 @@ int finish_plan(const Call &c, rowred_plan *p) {
 // slots leaves half of each 257-column row's lanes idle).
 // Rows wider than the register-resident kernels hold (or affine LayerNorm
 // beyond its 6144-granule kernels) loop over the row: 1024 lanes, tiles of
+// One workgroup per wide row: XCD remap from 2048 rows that start on 16-byte
+// boundaries (measured for the looped and head+tail kernels below).
+bool remap_many_aligned_rows(const Call &c) {
+  return c.rows >= 2048 && c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+}
+
 // 4 slots per lane (2 for LayerNorm), streaming loads and stores in the
-// second walk.
+// second walk.  Rows over the XCDs in contiguous runs from 2048 aligned rows
+// (MI355X, row sum: 2048x131072 180 -> 172 us, row min/max 180 -> 174 us;
+// 8192x40000 unchanged; 512x524288 and misaligned 4096x65537 1-4% slower).
 void choose_looped(const Call &c, rowred_plan *p) {
   const int kop = kernel_op(c);
   *p = rowred_plan{};
   p->lanes_per_row = 1024;
   p->threads = 1024;
   p->chunks = looped_kernel_exists(kop, 4) ? 4 : 2;
-  p->policy = kPolicyLooped | kPolicyNtLoads | kPolicyNtStores;
+  p->policy = kPolicyLooped | kPolicyNtLoads | kPolicyNtStores | (remap_many_aligned_rows(c) ? kPolicyXcdRemap : 0);
 }
 
 constexpr int64_t kLdsStripeMaxGranules = int64_t(2048) * 8192;
@@ -253,13 +262,17 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // way, the rest walked twice.  Faster than the looped kernels at every
   // width measured (MI355X): 4096x65540 softmax 486 -> 417 us, 2048x128256
   // 436 -> 381 us, 2048x131072 RMSNorm 493 -> 434 us, 1024x262144 softmax
-  // 491 -> 446 us, 512x524288 491 -> 473 us, 128x1048576 321 -> 297 us;
-  // remapping rows over the XCDs changed nothing.
+  // 491 -> 446 us, 512x524288 491 -> 473 us, 128x1048576 321 -> 297 us.
+  // Remapping rows over the XCDs pays from 2048 aligned rows (RMSNorm
+  // 2048x131072 423 -> 382 us, softmax 2048x131072 429 -> 388 us, 4096x65540
+  // 424 -> 405 us, RMSNorm 8192x65544 797 -> 777 us) and costs 2-6% at 128-1024
+  // rows (softmax 512x524288 473 -> 499 us).
   if (c.window > kWideMaxWindow && (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX)) {
     p->lanes_per_row = 1024;
     p->threads = 1024;
     p->chunks = kWideMaxChunks;
-    p->policy = kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores;
+    p->policy = kPolicyLdsStripe | kPolicyLooped | kPolicyNtLoads | kPolicyNtStores |
+                (remap_many_aligned_rows(c) ? kPolicyXcdRemap : 0);
     p->reserved = 0;
     return;
   }

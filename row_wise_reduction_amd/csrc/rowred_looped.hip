@@ -46,7 +46,8 @@ __global__ void __launch_bounds__(1024) looped_kernel(RowArgs a) {
   const int T = blockDim.x;
   const int li = threadIdx.x;
   const int lanes_log2 = a.lanes_log2;
-  const int64_t row = blockIdx.x;  // one row per workgroup
+  // one row per workgroup; XCD_REMAP gives each XCD a contiguous run of rows
+  const int64_t row = row_block(blockIdx.x, gridDim.x, (a.policy & kPolicyXcdRemap) != 0);
   const int width = a.width;
   const int64_t base = row * (int64_t)width;
   const float *xrow = a.x + base;

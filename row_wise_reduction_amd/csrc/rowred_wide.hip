@@ -236,13 +236,16 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
     if constexpr (NT) asm volatile("" ::: "memory");
   };
   f32x4 ta[TC], tb[TC];
-  auto walk = [&](auto nt, auto f) {
-    load_tile(nt, 0, ta);
+  // rev: the tiles last to first (the second walk then starts on what the
+  // first walk read last, the likeliest to be still in cache)
+  auto walk = [&](auto nt, auto f, bool rev) {
+    auto at = [&](int t) { return rev ? ntiles - 1 - t : t; };
+    load_tile(nt, at(0), ta);
     for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) load_tile(nt, t + 1, tb);
-      f(t, ta);
-      if (t + 2 < ntiles) load_tile(nt, t + 2, ta);
-      if (t + 1 < ntiles) f(t + 1, tb);
+      if (t + 1 < ntiles) load_tile(nt, at(t + 1), tb);
+      f(at(t), ta);
+      if (t + 2 < ntiles) load_tile(nt, at(t + 2), ta);
+      if (t + 1 < ntiles) f(at(t + 1), tb);
     }
   };
 
@@ -264,7 +267,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
           const float x = valid_k(tile_k(t, c), j) ? tv[c][j] : 0.0f;
           acc[j] = fmaf(x, x, acc[j]);
         }
-    });
+    }, false);
     const float ss = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
     scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
   } else {  // softmax: online (max m, sum s of exp(x - m)) per lane
@@ -304,7 +307,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
           tacc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
         }
       s += (tacc[0] + tacc[1]) + (tacc[2] + tacc[3]);
-    });
+    }, false);
     const float M = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
     // an all -inf row: M = -inf, every s = 0, sum 0 and 1/sum = inf, and the
     // map's exp(-inf - -inf) makes the row NaN, as in one pass
@@ -332,20 +335,26 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
         if ((unsigned)(e0 + j) < (unsigned)width) store_g<NT>(yrow + e0 + j, o[j]);
     }
   };
+  // ROWRED_POLICY_REVERSE: the tail last tile first, then the head.
+  const bool rev = (a.policy & kPolicyReverse) != 0;
   auto pass2 = [&](auto ntl, auto nts) {
+    auto head = [&] {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const f32x4 v = head_at(c);
-      const float o[4] = {map(v[0]), map(v[1]), map(v[2]), map(v[3])};
-      store_granule(nts, c * L + li, o);
-    }
+      for (int c = 0; c < C; ++c) {
+        const f32x4 v = head_at(c);
+        const float o[4] = {map(v[0]), map(v[1]), map(v[2]), map(v[3])};
+        store_granule(nts, c * L + li, o);
+      }
+    };
+    if (!rev) head();
     walk(ntl, [&](int t, const f32x4(&tv)[TC]) {
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
         const float o[4] = {map(tv[c][0]), map(tv[c][1]), map(tv[c][2]), map(tv[c][3])};
         store_granule(nts, tile_k(t, c), o);
       }
-    });
+    }, rev);
+    if (rev) head();
   };
   const bool ntl = (a.policy & kPolicyNtLoads) != 0, nts = (a.policy & kPolicyNtStores) != 0;
   if (ntl && nts) pass2(std::true_type{}, std::true_type{});
@@ -469,13 +478,15 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
     if constexpr (NT) asm volatile("" ::: "memory");
   };
   f32x4 xa[TC], ra[TC], xb[TC], rb[TC];
-  auto walk = [&](auto nt, auto f) {
-    load_tile(nt, 0, xa, ra);
+  // rev: the tiles last to first (as in the RMSNorm/softmax kernel)
+  auto walk = [&](auto nt, auto f, bool rev) {
+    auto at = [&](int t) { return rev ? ntiles - 1 - t : t; };
+    load_tile(nt, at(0), xa, ra);
     for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) load_tile(nt, t + 1, xb, rb);
-      f(t, xa, ra);
-      if (t + 2 < ntiles) load_tile(nt, t + 2, xa, ra);
-      if (t + 1 < ntiles) f(t + 1, xb, rb);
+      if (t + 1 < ntiles) load_tile(nt, at(t + 1), xb, rb);
+      f(at(t), xa, ra);
+      if (t + 2 < ntiles) load_tile(nt, at(t + 2), xa, ra);
+      if (t + 1 < ntiles) f(at(t + 1), xb, rb);
     }
   };
 
@@ -550,7 +561,7 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
     mean_l += delta * ((double)n_t / n);
     m2_l += m2_t + delta * delta * (n_l * (double)n_t / n);
     n_l = n;
-  });
+  }, false);
   const double mean = row_allreduce<SumOp>(n_l * mean_l, lanes_log2, partials_d[0]) / (double)width;
   const double dm = mean_l - mean;
   const double m2 = row_allreduce<SumOp>(m2_l + n_l * dm * dm, lanes_log2, partials_d[1]);
@@ -593,13 +604,18 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
         if ((unsigned)(e0 + j) < (unsigned)width) store_g<NT>(yrow + e0 + j, o[j]);
     }
   };
+  // ROWRED_POLICY_REVERSE: the tail last tile first, then the head.
+  const bool rev = (a.policy & kPolicyReverse) != 0;
   auto pass2 = [&](auto ntl, auto nts) {
+    auto head = [&] {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      float o[4];
-      map_granule(c * L + li, head_x(c), head_r(c), o);
-      store_granule(nts, c * L + li, o);
-    }
+      for (int c = 0; c < C; ++c) {
+        float o[4];
+        map_granule(c * L + li, head_x(c), head_r(c), o);
+        store_granule(nts, c * L + li, o);
+      }
+    };
+    if (!rev) head();
     walk(ntl, [&](int t, const f32x4(&tx)[TC], const f32x4(&tr)[TC]) {
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
@@ -607,7 +623,8 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
         map_granule(tile_k(t, c), tx[c], tr[c], o);
         store_granule(nts, tile_k(t, c), o);
       }
-    });
+    }, rev);
+    if (rev) head();
   };
   const bool ntl = (a.policy & kPolicyNtLoads) != 0, nts = (a.policy & kPolicyNtStores) != 0;
   if (ntl && nts) pass2(std::true_type{}, std::true_type{});

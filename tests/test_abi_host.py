@@ -304,6 +304,9 @@ def test_head_tail_plan_preconditions():
     assert lib.rowred_run_plan(2, X, None, Y, 0, 100000, f(0), ctypes.byref(ok), None) == R.ROWRED_OK
     ln = bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=m)._c()  # LayerNorm: x and r of 8 slots
     assert lib.rowred_run_plan(0, X, X + (1 << 32), Y, 0, 40000, f(1e-5), ctypes.byref(ln), None) == R.ROWRED_OK
+    # REVERSE orders the second walk (last tail tile first, head last)
+    rev = bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=m | R.ROWRED_POLICY_REVERSE)._c()
+    assert lib.rowred_run_plan(1, X, None, Y, 0, 100000, f(1e-6), ctypes.byref(rev), None) == R.ROWRED_OK
     for op, width, kw in ((2, 65536, {}),                       # not wider than the head
                           (2, 100000, dict(chunks=8)), (2, 100000, dict(lanes_per_row=512, threads=512)),
                           (2, 100000, dict(policy=m | R.ROWRED_POLICY_STAGE_STORES)),
@@ -602,7 +605,7 @@ def test_ws_entry_argument_checks():
                                 dict(lanes_per_row=1024, threads=1024, chunks=2,
                                      policy=R.ROWRED_POLICY_LOOPED | R.ROWRED_POLICY_STAGE_STORES),
                                 dict(lanes_per_row=1024, threads=1024, chunks=2,
-                                     policy=R.ROWRED_POLICY_LOOPED | R.ROWRED_POLICY_XCD_REMAP)])
+                                     policy=R.ROWRED_POLICY_LOOPED | R.ROWRED_POLICY_REVERSE)])
 def test_looped_plan_rejects(kw):
     base = dict(lanes_per_row=1024, rows_per_group=0, chunks=4, threads=1024, grid=0,
                 policy=R.ROWRED_POLICY_LOOPED)
@@ -654,3 +657,22 @@ def test_layernorm_plan_query_errors():
         R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_layernorm_plan_query(X, None, None, None, Y, 4, 4096, None) == R.ROWRED_ERR_INVALID_ARG
     assert lib.rowred_layernorm_plan_query(X, None, None, None, Y, 0, 4096, ctypes.byref(p)) == R.ROWRED_OK
+
+
+def test_wide_row_remap_rule():
+    """One workgroup per wide row: rows go over the XCDs in contiguous runs
+    from 2048 rows that start on 16-byte boundaries (head+tail RMSNorm and
+    softmax, looped row sum and min/max); LayerNorm's head+tail from 256 MiB
+    per aligned input."""
+    rem = R.ROWRED_POLICY_XCD_REMAP
+    for op, rows, width, xx, want in (("rmsnorm", 2048, 131072, X, True), ("softmax", 4096, 65540, X, True),
+                                      ("softmax", 1024, 131072, X, False), ("softmax", 512, 524288, X, False),
+                                      ("rmsnorm", 2048, 131073, X, False), ("rmsnorm", 2048, 131072, X + 4, False),
+                                      ("row_sum", 2048, 131072, X, True), ("row_minmax", 8192, 40000, X, True),
+                                      ("row_sum", 512, 524288, X, False), ("row_sum", 4096, 65537, X, False),
+                                      ("layernorm_residual", 1024, 65536, X, False),
+                                      ("layernorm_residual", 2048, 40000, X, True)):
+        r = RR if op in ("layernorm_residual", "row_minmax") else None
+        p = R.rowred_plan_query(op, xx, r, Y, rows=rows, width=width)
+        assert p.policy & R.ROWRED_POLICY_LOOPED, (op, rows, width, p)
+        assert bool(p.policy & rem) == want, (op, rows, width, p)

@@ -81,7 +81,7 @@ def test_explicit_looped_plans(op, geom):
     for width, shift in ((4 * G * 3 - 7, 1), (4 * G * 4 + 5, 3), (4 * G, 0), (5, 2)):
         x, r, g, b = make_inputs(op, 4, width, seed=width * 7 + T)
         ref = reference(op, x, r, g, b)
-        for policy in (0, STREAM):
+        for policy in (0, STREAM, STREAM | R.ROWRED_POLICY_XCD_REMAP):
             plan = looped_plan(T, C, policy)
             print_case("looped", op, width, shift, plan)
             check(op, run(op, x, r, g, b, plan=plan, shift=shift), ref, f"{op} {width} {plan}")

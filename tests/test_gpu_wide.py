@@ -154,11 +154,16 @@ def test_head_held_tail_walked(op, width):
     ref = oracle_of(op, x)
     for shift, y_shift in ((0, 0), (3, 3), (1, 2)):
         xd = shifted_input(x, shift)
-        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+        outs = []
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP,
+                    R.ROWRED_POLICY_REVERSE, R.ROWRED_POLICY_REVERSE | R.ROWRED_POLICY_NT_LOADS):
             plan = R.Plan(1024, 0, 16, 1024, 0, policy=pol | TAIL)
             print_case("head + tail", op, width, shift, y_shift, plan)
             got = run(op, xd, plan, rows, width, shift, y_shift)
             assert_close(got, ref, f"{op} {width} {plan}")
+            outs.append(got)
+        # the second walk's order changes no arithmetic
+        assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
         looped = run(op, xd, R.Plan(1024, 0, 4, 1024, 0, policy=R.ROWRED_POLICY_LOOPED), rows, width, shift, y_shift)
         assert_close(got, looped.astype(np.float64), f"{op} {width} vs looped")
 
@@ -216,10 +221,15 @@ def test_layernorm_head_held_tail_walked(variant, width):
     for sx, sr, sy in ((0, 0, 0), (1, 1, 1), (2, 3, 2)):
         got = run_ln(x, r, g, b, None, sx, sr, sy)
         assert_close(got, ref, f"{variant} {width} entry point")
-        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP):
+        outs = []
+        for pol in (0, R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP,
+                    R.ROWRED_POLICY_REVERSE, R.ROWRED_POLICY_REVERSE | R.ROWRED_POLICY_NT_STORES):
             plan = R.Plan(1024, 0, 8, 1024, 0, policy=pol | TAIL)
             print_case("layernorm head + tail", variant, width, sx, sr, sy, plan)
-            assert_close(run_ln(x, r, g, b, plan, sx, sr, sy), ref, f"{variant} {width} {plan}")
+            outs.append(run_ln(x, r, g, b, plan, sx, sr, sy))
+            assert_close(outs[-1], ref, f"{variant} {width} {plan}")
+        # the second walk's order changes no arithmetic
+        assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
         looped = run_ln(x, r, g, b, R.Plan(1024, 0, 2, 1024, 0, policy=R.ROWRED_POLICY_LOOPED), sx, sr, sy)
         assert_close(got, looped.astype(np.float64), f"{variant} {width} vs looped")
 
