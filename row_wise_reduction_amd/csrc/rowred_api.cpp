@@ -302,18 +302,42 @@ void choose_plan(const Call &c, rowred_plan *p) {
   const bool small = in_bytes <= (int64_t(32) << 20);
   const bool rows_aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
   const bool scalar_out = c.op == ROWRED_OP_ROW_SUM || c.op == ROWRED_OP_ROW_MINMAX;
-  const bool stage_ok = !rows_aligned && c.y_vec;
+  const int kop = kernel_op(c);
+  const bool affine = kop == kKernelOpLayerNormAffine;
+  // Small calls (at most 2^19 elements, rows of at most 512 granules) are
+  // latency-bound: one round of short-lived workgroups.  Two slots per lane
+  // (L the smallest power of two >= half the window), one wavefront per
+  // workgroup up to 2^16 elements and 256 threads beyond, streaming loads,
+  // nothing staged: 0.4-1.3 us faster than the rules below at 1-4096 rows
+  // of 127, 257 and 1537 columns (softmax and residual LayerNorm, MI355X;
+  // 17x257 LayerNorm 3.38 -> 2.51 us, 1x127 3.20 -> 2.09 us, softmax
+  // 7x1537 3.60 -> 2.69 us).
+  if (!scalar_out && !affine && w <= 512 && c.rows * c.width <= (int64_t(1) << 19)) {
+    int64_t L = 8;
+    while (L < 1024 && 2 * L < w) L *= 2;
+    p->lanes_per_row = (int32_t)L;
+    p->chunks = round_up_chunks((w + L - 1) / L);
+    const int64_t t_min = c.rows * c.width <= (int64_t(1) << 16) ? 64 : 256;
+    p->threads = (int32_t)(L > t_min ? L : t_min);
+    p->policy = kPolicyNtLoads;
+    p->reserved = 0;
+    return;
+  }
+  // Outputs are staged only for rows of at most 256 granules, where a
+  // workgroup holds many rows whose boundary lines it shares: at 127-769
+  // columns staging is 1-40% faster at 65536-262144 rows; from 1537 columns
+  // it is 4% faster to 19% slower (65536x2049 softmax 266 -> 216 us
+  // unstaged), so longer rows store unstaged and streaming.
+  const bool stage_ok = !rows_aligned && c.y_vec && w <= 256;
   // Staged rows that fit one wavefront (<= 64 lanes x 4 slots) store through
   // LDS, so their lanes can hold more slots.
-  int64_t max_chunks = (small || scalar_out || (stage_ok && w <= 256)) ? 4 : 2;
+  int64_t max_chunks = (small || scalar_out || stage_ok) ? 4 : 2;
   // Single-round inputs of 8-32 MiB per input with two input streams
   // (residual LayerNorm), or of 16-32 MiB with rows of >= 1024 granules,
   // keep more loads in flight per lane with 8 slots: 5-10% and 0-6% faster
   // at 1024x4096, 2048x2048, 4096x1024, 8192x512 and 512x8192 (measured on
   // 16-byte-aligned rows; below 8 MiB 8 slots were up to 17% slower).
   const bool two_inputs = c.r != nullptr && c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
-  const int kop = kernel_op(c);
-  const bool affine = kop == kKernelOpLayerNormAffine;
   if (small && !scalar_out && !stage_ok && !affine &&
       ((two_inputs && in_bytes >= (int64_t(8) << 20)) || (w >= 1024 && in_bytes >= (int64_t(16) << 20))))
     max_chunks = 8;
@@ -363,8 +387,8 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // Row sum and min/max on rows of at most 40 granules read them cached (the
   // boundary granule two neighbouring rows share is read by both): 2-7%
   // faster at 63 and 127 columns.
-  if (!(can_stage && w <= 256) && !(scalar_out && w <= 40)) policy |= kPolicyNtLoads;
-  if (!scalar_out && (rows_aligned || can_stage || p->chunks <= 2)) policy |= kPolicyNtStores;
+  if (!can_stage && !(scalar_out && w <= 40)) policy |= kPolicyNtLoads;
+  if (!scalar_out && (rows_aligned || can_stage || p->chunks <= 2 || w > 256)) policy |= kPolicyNtStores;
   if (can_stage) policy |= kPolicyStageStores;
   if (rows_aligned && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
   // Rows of 5-8 slots per 1024-lane workgroup, up to 2048 rows of 8192

@@ -97,9 +97,9 @@ def test_plan_for_workload_shapes():
     st = R.ROWRED_POLICY_STAGE_STORES
     # short ragged rows (staged, <= 256 granules) keep cached loads
     cases = {(131072, 127): (16, 3, ns | st), (131072, 257): (32, 3, ns | st),
-             (131072, 1537): (256, 2, nl | ns | st), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
+             (131072, 1537): (256, 2, nl | ns), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
-             (17, 257): (32, 3, ns | st), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
+             (17, 257): (64, 2, nl), (7, 1537): (256, 2, nl), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
              (2048, 32768): (1024, 8, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE),
              (1024, 50257): (1024, 13, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
              (4096, 65536): (1024, 16, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE)}
@@ -113,14 +113,36 @@ def test_plan_memory_policy():
     st = R.ROWRED_POLICY_STAGE_STORES
     # small, every row on a 16-byte boundary: streaming, no remap, no staging
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=4096).policy == nl | ns
-    # rows share boundary lines: outputs staged in LDS, streaming stores;
-    # short rows keep cached loads (each boundary granule is read twice)
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=127).policy == ns | st
-    assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns | st
+    # short rows share boundary lines: outputs staged in LDS, streaming
+    # stores, cached loads (each boundary granule is read twice)
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=16384, width=127).policy == ns | st
+    # longer ragged rows (> 256 granules): unstaged, streaming
+    assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2049).policy == nl | ns
     # shared lines but y at another phase (no staging), > 2 slots per lane: cached stores
-    assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=64, width=127).policy == nl
+    assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=16384, width=127).policy == nl
     # large aligned matrix: streaming + remap
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=4096).policy == nl | ns | rm
+
+
+def test_plan_for_latency_bound_calls():
+    """At most 2^19 elements in rows of at most 512 granules: 2 slots per
+    lane, L the smallest power of two >= half the window, one wavefront per
+    workgroup up to 2^16 elements (256 threads beyond), streaming loads,
+    nothing staged.  Row reductions and affine LayerNorm keep their rules."""
+    nl = R.ROWRED_POLICY_NT_LOADS
+    for op, rows, width, want in (("softmax", 7, 1537, (256, 2, 256, nl)), ("softmax", 1, 127, (16, 2, 64, nl)),
+                                  ("rmsnorm", 4096, 127, (32, 2, 256, nl)), ("softmax", 256, 2048, (256, 2, 256, nl)),
+                                  ("layernorm_residual", 17, 257, (64, 2, 64, nl)),
+                                  ("layernorm_residual", 1, 5, (8, 1, 64, nl)),
+                                  ("rmsnorm", 1024, 512, (64, 2, 256, nl))):
+        r = RR if op == "layernorm_residual" else None
+        p = R.rowred_plan_query(op, X, r, Y, rows=rows, width=width)
+        assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == want, (op, rows, width, p)
+    # beyond either bound the general rules apply
+    assert R.rowred_plan_query("softmax", X, None, Y, rows=4097, width=128).policy != nl
+    assert R.rowred_plan_query("softmax", X, None, Y, rows=64, width=4096).lanes_per_row == 256
+    assert R.rowred_plan_query("row_sum", X, None, Y, rows=7, width=1537).policy & R.ROWRED_POLICY_NT_LOADS
 
 
 def test_plan_reports_4byte_io_on_mixed_alignment():
