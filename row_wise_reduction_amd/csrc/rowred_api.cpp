@@ -311,10 +311,15 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // nothing staged: 0.4-1.3 us faster than the rules below at 1-4096 rows
   // of 127, 257 and 1537 columns (softmax and residual LayerNorm, MI355X;
   // 17x257 LayerNorm 3.38 -> 2.51 us, 1x127 3.20 -> 2.09 us, softmax
-  // 7x1537 3.60 -> 2.69 us).
-  if (!scalar_out && !affine && w <= 512 && c.rows * c.width <= (int64_t(1) << 19)) {
+  // 7x1537 3.60 -> 2.69 us).  Affine LayerNorm, which also reads gamma and
+  // beta per element, runs best with one slot per lane up to 256 granules
+  // (1024x127 4.19 -> 2.91 us, 64x257 4.26 -> 2.90 us, 7x1537 4.47 -> 3.42 us
+  // against its general rule).
+  const bool tiny = c.rows * c.width <= (int64_t(1) << 19);
+  if (!scalar_out && w <= 512 && tiny) {
+    const int64_t slots = affine && w <= 256 ? 1 : 2;
     int64_t L = 8;
-    while (L < 1024 && 2 * L < w) L *= 2;
+    while (L < 1024 && slots * L < w) L *= 2;
     p->lanes_per_row = (int32_t)L;
     p->chunks = round_up_chunks((w + L - 1) / L);
     const int64_t t_min = c.rows * c.width <= (int64_t(1) << 16) ? 64 : 256;
@@ -380,7 +385,10 @@ void choose_plan(const Call &c, rowred_plan *p) {
   }
   p->lanes_per_row = (int32_t)L;
   p->chunks = chunks;
-  const int64_t t_min = (small && !scalar_out) || affine_256 ? 256 : 512;
+  // Row sum and min/max take 512 threads, except calls of at most 2^19
+  // elements, where 256 are 0.05-0.2 us faster (1x4096 2.41 -> 2.24 us,
+  // 256x1024 2.84 -> 2.68 us).
+  const int64_t t_min = (small && !scalar_out) || affine_256 || (scalar_out && tiny) ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = 0;

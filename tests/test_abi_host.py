@@ -139,6 +139,15 @@ def test_plan_for_latency_bound_calls():
         r = RR if op == "layernorm_residual" else None
         p = R.rowred_plan_query(op, X, r, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == want, (op, rows, width, p)
+    # affine LayerNorm: one slot per lane up to 256 granules, then two
+    G, B = RR + (1 << 30), RR + (1 << 31)
+    for rows, width, want in ((64, 257, (128, 1, 128)), (1024, 127, (64, 1, 256)), (7, 1537, (256, 2, 256))):
+        p = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows, width)
+        assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (*want, nl), (rows, width, p)
+    # row sum and min/max keep their geometry, in 256-thread workgroups
+    p = R.rowred_plan_query("row_sum", X, None, Y, rows=1, width=4096)
+    assert (p.lanes_per_row, p.chunks, p.threads) == (256, 4, 256)
+    assert R.rowred_plan_query("row_sum", X, None, Y, rows=16384, width=8192).threads == 512
     # beyond either bound the general rules apply
     assert R.rowred_plan_query("softmax", X, None, Y, rows=4097, width=128).policy != nl
     assert R.rowred_plan_query("softmax", X, None, Y, rows=64, width=4096).lanes_per_row == 256
