@@ -244,7 +244,9 @@ __global__ void __launch_bounds__(1024) seg_stats_kernel(SegArgs a) {
 // ---------------------------------------------------------------------------
 // Fold a row's records: one wavefront per row, lanes stride over the
 // records, then the wavefront butterfly.  Wavefronts past the last row
-// return at once (no barrier in this kernel).
+// return at once (no barrier in this kernel).  The loops over a row's
+// records are unrolled so that a lane's loads issue together (S = 1024
+// records take 16 per lane); the additions keep their order.
 // ---------------------------------------------------------------------------
 template <int OP>
 __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
@@ -255,11 +257,13 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
   const Rec *rec = records(a) + row * S;
   if constexpr (OP == kOpRowSum) {
     double s = 0.0;
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) s += rec[k].v0;
     s = group_allreduce<SumOp>(s, 6);
     if (lane == 0) a.y[row] = (float)s;
   } else if constexpr (OP == kOpRowMinMax) {
     float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) {
       mn = fminf(mn, (float)rec[k].v0);
       mx = fmaxf(mx, (float)rec[k].v1);
@@ -272,16 +276,19 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
     }
   } else if constexpr (OP == kOpRms) {
     double s = 0.0;
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) s += rec[k].v0;
     s = group_allreduce<SumOp>(s, 6);
     if (lane == 0) row_records(a)[row] = Rec{s, 0.0};
   } else if constexpr (OP == kOpSoftmax) {
     float m = -__builtin_inff();
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) m = fmaxf(m, (float)rec[k].v0);
     m = group_allreduce<MaxOp>(m, 6);
     // An all -inf row has m = -inf and s_k = 0 everywhere: 0 * exp(NaN)
     // makes s NaN, and the row NaN, as in one pass.
     float s = 0.0f;
+#pragma unroll 16
     for (int k = lane; k < S; k += 64)
       s += (float)rec[k].v1 * __builtin_amdgcn_exp2f(((float)rec[k].v0 - m) * kLog2e);
     s = group_allreduce<SumOp>(s, 6);
@@ -289,10 +296,12 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
   } else {  // LayerNorm
     const int off = (int)((((uintptr_t)a.x >> 2) + row * (int64_t)a.width) & 3);
     double s = 0.0;
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) s += rec[k].v0;
     s = group_allreduce<SumOp>(s, 6);
     const double mean = s / (double)a.width;
     double m2 = 0.0;
+#pragma unroll 16
     for (int k = lane; k < S; k += 64) {
       const int64_t n = segment_count(k, a.seg_granules, off, a.width);
       if (n > 0) {
