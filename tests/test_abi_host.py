@@ -569,7 +569,9 @@ def test_exchange_plan_limits(op, T, C):
     ("rmsnorm", 1024, 1 << 18, (256, 8, 32, 0)), ("rmsnorm", 64, 1 << 19, (256, 8, 64, 0)),
     ("rmsnorm", 64, 600000, (256, 16, 37, 1)), ("softmax", 64, 1 << 20, (256, 16, 64, 1)),
     ("layernorm_residual", 16, 1 << 20, (1024, 4, 64, 0)), ("softmax", 7, 1537, (64, 2, 4, 0)),
-    ("softmax", 16, 32768, (256, 8, 4, 0)),
+    # no more (row, segment) workgroups than CUs: the segment is halved
+    ("softmax", 16, 32768, (256, 4, 8, 0)), ("layernorm_residual", 8, 1 << 16, (256, 4, 16, 0)),
+    ("softmax", 32, 1 << 16, (256, 4, 16, 0)), ("softmax", 33, 1 << 16, (256, 8, 8, 0)),
 ])
 def test_ws_split_plan_choice(op, rows, width, want):
     """The _ws entry points' split plans: exchange geometries from the sweep
@@ -707,3 +709,16 @@ def test_wide_row_remap_rule():
         p = R.rowred_plan_query(op, xx, r, Y, rows=rows, width=width)
         assert p.policy & R.ROWRED_POLICY_LOOPED, (op, rows, width, p)
         assert bool(p.policy & rem) == want, (op, rows, width, p)
+
+
+@pytest.mark.parametrize("op", ["layernorm_residual", "rmsnorm", "softmax", "row_sum"])
+def test_workspace_size_covers_every_chosen_plan(op):
+    """rowred_workspace_size(op, rows, width) is enough for the plan a _ws
+    call of that shape chooses at any 16-byte phase of x, including row
+    counts on either side of the segment-halving rule."""
+    for width in (32769, 40000, 65536, 98304, 100003, 262144, 1 << 20):
+        for rows in (1, 7, 8, 16, 31, 32, 33, 63, 64, 65, 127, 255, 256):
+            need = R.rowred_workspace_size(op, rows, width)
+            for shift in (0, 4, 8, 12):
+                p = R.rowred_split_plan_query(op, X + shift, rows, width)
+                assert p.workspace_bytes <= need, (op, rows, width, shift, p, need)
