@@ -110,8 +110,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m row_wise_reduction_amd.build` "
-                              "(or __graft_entry__.build())")
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m row_wise_reduction_amd.build`")
         # torch ships its own copy of the HIP runtime under the same soname.
         # Loaded first, it is the one this library binds to; loaded after
         # this library, it would be a second runtime in the process, and
