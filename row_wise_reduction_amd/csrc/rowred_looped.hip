@@ -153,9 +153,12 @@ __global__ void __launch_bounds__(1024) looped_kernel(RowArgs a) {
   float scale = 0.0f;           // RMSNorm: 1 / sqrt(mean square + eps); LayerNorm: rstd; softmax: 1 / sum
   float m_row = 0.0f;           // softmax: row max
   float m_hi = 0.0f, m_lo = 0.0f;  // LayerNorm: row mean as an FP32 pair
+  // RMSNorm and softmax sum each tile's terms in FP32 and the lane's running
+  // total in FP64 (a lane of a 2^31-column row adds up 2^21 terms).
   if constexpr (OP == kOpRms) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    double total = 0.0;
     walk(std::false_type{}, [&](int t, const f32x4(&xv)[C], const f32x4(&)[C]) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < C; ++c)
 #pragma unroll
@@ -163,11 +166,13 @@ __global__ void __launch_bounds__(1024) looped_kernel(RowArgs a) {
           const float x = valid(t, c, j) ? xv[c][j] : 0.0f;
           acc[j] = fmaf(x, x, acc[j]);
         }
+      total += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
     });
-    const float ss = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
-    scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
+    const double ss = row_allreduce<SumOp>(total, lanes_log2, partials_d[0]);
+    scale = __builtin_amdgcn_rsqf(fmaf((float)ss, a.inv_width, a.eps));
   } else if constexpr (OP == kOpSoftmax) {
-    float m = -__builtin_inff(), s = 0.0f;
+    float m = -__builtin_inff();
+    double s = 0.0;
     walk(std::false_type{}, [&](int t, const f32x4(&xv)[C], const f32x4(&)[C]) {
       float mt = -__builtin_inff();
 #pragma unroll
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(1024) looped_kernel(RowArgs a) {
       const float m_new = fmaxf(m, mt);
       // rescale the running sum to the new max (no rescale while the max
       // stays, which also covers a lane that has seen only -inf)
-      if (m_new != m) s *= __builtin_amdgcn_exp2f((m - m_new) * kLog2e);
+      if (m_new != m) s *= (double)__builtin_amdgcn_exp2f((m - m_new) * kLog2e);
       m = m_new;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -188,15 +193,15 @@ __global__ void __launch_bounds__(1024) looped_kernel(RowArgs a) {
           const bool zero = !valid(t, c, j) || x == -__builtin_inff();  // weight 0, even when m is -inf
           acc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
         }
-      s += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      s += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
     });
     const float M = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
     // an all -inf row: M = -inf, every s = 0, sum 0 and 1/sum = inf, and
     // the map's exp(-inf - -inf) makes the row NaN, as in one pass
-    const float term = (m == M) ? s : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
-    const float S = row_allreduce<SumOp>(term, lanes_log2, partials[1]);
+    const double term = (m == M) ? s : s * (double)__builtin_amdgcn_exp2f((m - M) * kLog2e);
+    const double S = row_allreduce<SumOp>(term, lanes_log2, partials_d[0]);
     m_row = M;
-    scale = __builtin_amdgcn_rcpf(S);
+    scale = __builtin_amdgcn_rcpf((float)S);
   } else {  // LayerNorm
     double n_l = 0.0, mean_l = 0.0, m2_l = 0.0;
     walk(std::false_type{}, [&](int t, const f32x4(&xv)[C], const f32x4(&rv)[C]) {

@@ -286,11 +286,12 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
     for (int k = lane; k < S; k += 64) m = fmaxf(m, (float)rec[k].v0);
     m = group_allreduce<MaxOp>(m, 6);
     // An all -inf row has m = -inf and s_k = 0 everywhere: 0 * exp(NaN)
-    // makes s NaN, and the row NaN, as in one pass.
-    float s = 0.0f;
+    // makes s NaN, and the row NaN, as in one pass.  The sum is FP64: a row
+    // of 2^31 columns has 2^19 segments, 2^13 per lane.
+    double s = 0.0;
 #pragma unroll 16
     for (int k = lane; k < S; k += 64)
-      s += (float)rec[k].v1 * __builtin_amdgcn_exp2f(((float)rec[k].v0 - m) * kLog2e);
+      s += rec[k].v1 * (double)__builtin_amdgcn_exp2f(((float)rec[k].v0 - m) * kLog2e);
     s = group_allreduce<SumOp>(s, 6);
     if (lane == 0) row_records(a)[row] = Rec{(double)m, (double)s};
   } else {  // LayerNorm

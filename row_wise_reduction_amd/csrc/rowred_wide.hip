@@ -186,6 +186,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
   constexpr int kTile = TC * L;
   __shared__ f32x4 held[CL * L];
   __shared__ float partials[2][16];
+  __shared__ double partials_d[16];
   constexpr int lanes_log2 = 10;
   const int li = threadIdx.x;
   const int width = a.width;
@@ -249,7 +250,9 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
     }
   };
 
-  // ---- pass 1: statistics over the head, then the tail tiles.
+  // ---- pass 1: statistics over the head, then the tail tiles.  The head's
+  // and each tile's terms are summed in FP32, the lane's running total in
+  // FP64: a lane of a 2^31-column row adds up 2^21 terms.
   float scale, m_row = 0.0f;
   if constexpr (OP == kOpRms) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -259,17 +262,20 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] = fmaf(v[j], v[j], acc[j]);
     }
+    double total = (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
     walk(std::false_type{}, [&](int t, const f32x4(&tv)[TC]) {
+      float tacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < TC; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float x = valid_k(tile_k(t, c), j) ? tv[c][j] : 0.0f;
-          acc[j] = fmaf(x, x, acc[j]);
+          tacc[j] = fmaf(x, x, tacc[j]);
         }
+      total += (double)((tacc[0] + tacc[1]) + (tacc[2] + tacc[3]));
     }, false);
-    const float ss = row_allreduce<SumOp>((acc[0] + acc[1]) + (acc[2] + acc[3]), lanes_log2, partials[0]);
-    scale = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_width, a.eps));
+    const double ss = row_allreduce<SumOp>(total, lanes_log2, partials_d);
+    scale = __builtin_amdgcn_rsqf(fmaf((float)ss, a.inv_width, a.eps));
   } else {  // softmax: online (max m, sum s of exp(x - m)) per lane
     float m = -__builtin_inff();
 #pragma unroll
@@ -285,7 +291,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] += v[j] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f((v[j] - m) * kLog2e);
     }
-    float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    double s = (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
     walk(std::false_type{}, [&](int t, const f32x4(&tv)[TC]) {
       float mt = -__builtin_inff();
 #pragma unroll
@@ -295,7 +301,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
       const float m_new = fmaxf(m, mt);
       // rescale the running sum to the new max (no rescale while the max
       // stays, which also covers a lane that has seen only -inf)
-      if (m_new != m) s *= __builtin_amdgcn_exp2f((m - m_new) * kLog2e);
+      if (m_new != m) s *= (double)__builtin_amdgcn_exp2f((m - m_new) * kLog2e);
       m = m_new;
       float tacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -306,15 +312,15 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
           const bool zero = !valid_k(tile_k(t, c), j) || x == -__builtin_inff();
           tacc[j] += zero ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
         }
-      s += (tacc[0] + tacc[1]) + (tacc[2] + tacc[3]);
+      s += (double)((tacc[0] + tacc[1]) + (tacc[2] + tacc[3]));
     }, false);
     const float M = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
     // an all -inf row: M = -inf, every s = 0, sum 0 and 1/sum = inf, and the
     // map's exp(-inf - -inf) makes the row NaN, as in one pass
-    const float term = (m == M) ? s : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
-    const float S = row_allreduce<SumOp>(term, lanes_log2, partials[1]);
+    const double term = (m == M) ? s : s * (double)__builtin_amdgcn_exp2f((m - M) * kLog2e);
+    const double S = row_allreduce<SumOp>(term, lanes_log2, partials_d);
     m_row = M;
-    scale = __builtin_amdgcn_rcpf(S);
+    scale = __builtin_amdgcn_rcpf((float)S);
   }
 
   // ---- pass 2: map and store, the head from registers and LDS, the tail
