@@ -731,6 +731,12 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
   a.policy = p.policy;
   a.r_vec = c.r_vec ? 1 : 0;
   a.y_vec = c.y_vec ? 1 : 0;
+  a.spin_limit = kExchangeSpinLimit;
+  if (const char *env = getenv("ROWRED_EXCHANGE_SPIN_LIMIT")) {
+    char *end = nullptr;
+    const unsigned long v = strtoul(env, &end, 10);
+    if (end != env && *end == '\0' && v <= UINT32_MAX) a.spin_limit = (uint32_t)v;
+  }
   // Row blocks run one after another; offsetting every operand by whole
   // rows keeps r and y at x's 16-byte phase.  The workspace is reused.
   for (int64_t r0 = 0; r0 < c.rows; r0 += p.block_rows) {

@@ -129,7 +129,14 @@ struct SegArgs {
   int32_t policy;      // ROWRED_POLICY_NT_LOADS / NT_STORES (apply kernel), ROWRED_POLICY_REVERSE
   int32_t r_vec;
   int32_t y_vec;
+  uint32_t spin_limit;  // exchange kernels: polls of one slot before a wait gives up
 };
+
+// Polls of one exchange slot before the wait gives up (about 60 ms at
+// 2.4 GHz with s_sleep 2 between polls).  The environment variable
+// ROWRED_EXCHANGE_SPIN_LIMIT overrides it, for tests of the give-up path
+// (0: a wait gives up at its first empty poll).
+constexpr uint32_t kExchangeSpinLimit = 1u << 20;
 
 // Chunk counts (16-byte slots per lane) of the split kernels.
 constexpr int kSplitChunkSet[] = {1, 2, 4};

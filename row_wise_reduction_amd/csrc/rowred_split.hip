@@ -444,10 +444,9 @@ __global__ void __launch_bounds__(1024) seg_apply_kernel(SegArgs a) {
 // or of earlier rows, and earlier rows can all finish: the oldest waiting
 // row always completes.  S is capped (kMaxExchangeSegments) far below the
 // workgroups the chip holds at once.  Every wait is bounded all the same:
-// after kSpinLimit polls a lane gives up, sets the status word and the row
-// comes out NaN.
+// after a.spin_limit polls (kExchangeSpinLimit unless the host overrides
+// it) a lane gives up, sets the status word and the row comes out NaN.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kSpinLimit = 1u << 20;
 
 __device__ __forceinline__ uint64_t encode(double v) {
   if (v != v) v = __builtin_nan("");
@@ -477,7 +476,7 @@ __device__ __forceinline__ uint64_t await_slot(const SegArgs &a, const uint64_t 
   uint64_t w = __hip_atomic_load(slots + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma nounroll
   for (uint32_t it = 0; w == 0; ++it) {
-    if (it == kSpinLimit) {
+    if (it >= a.spin_limit) {
       __hip_atomic_store(reinterpret_cast<uint64_t *>(a.ws), (uint64_t)1, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       break;

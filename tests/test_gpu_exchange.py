@@ -268,3 +268,37 @@ def test_two_streams_at_once():
         yh = ys[i].cpu().numpy()
         for rr in (0, 255, 511):
             check(op, yh[rr:rr + 1], reference(op, xs[i][rr:rr + 1], None, None, None), f"{op} stream {i} row {rr}")
+
+
+def test_wait_give_up_path(monkeypatch):
+    """The bounded wait's give-up path, forced from the host: with
+    ROWRED_EXCHANGE_SPIN_LIMIT=0 a wait gives up at its first empty poll, so
+    every kernel still ends.  Then each output is either NaN (its segment
+    gave up) or the oracle's value (its segment saw every record); some
+    segment gives up and raises the status word.  The next call with the
+    default bound, on the same workspace, clears the word and is exact."""
+    t = torch()
+    rows, width = 256, 65536
+    gave_up = False
+    for op in ("softmax", "rmsnorm", "layernorm_residual"):
+        x, r, g, b = make_inputs(op, rows, width, seed=4242)
+        ref = reference(op, x, r, g, b)
+        plan = R.rowred_split_plan_query(c_op(op), shifted_input(x, 0))
+        assert plan.policy & EXCHANGE and plan.segments > 1
+        ws = workspace(op, rows, width, plan, shifted_input(x, 0))
+        monkeypatch.setenv("ROWRED_EXCHANGE_SPIN_LIMIT", "0")
+        print_case("exchange give-up", op, rows, width, plan)
+        got = run(op, x, r, g, b, ws=ws)
+        status = int(ws[:8].view(t.int64).item())
+        nan = np.isnan(got)
+        ok = ~nan & ~np.isnan(ref)
+        assert np.all(np.abs(got[ok] - ref[ok]) <= 1e-5 + 1e-5 * np.abs(ref[ok])), op
+        assert status in (0, 1)
+        assert (status == 1) == bool(nan.any()), (op, status, int(nan.sum()))
+        gave_up |= status == 1
+        monkeypatch.delenv("ROWRED_EXCHANGE_SPIN_LIMIT")
+        print_case("exchange after give-up", op)
+        again = run(op, x, r, g, b, ws=ws)
+        assert status_ok(ws)
+        assert_close(again, ref, f"{op} after a give-up")
+    assert gave_up, "no wait gave up at a spin limit of 0"
