@@ -363,7 +363,7 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
  * Calls that run concurrently need separate workspaces.  An exchange
  * workgroup waits only for workgroups of its own row, which the hardware
  * dispatches no later than those of later rows, so every wait ends; each is
- * bounded all the same (2^20 polls, about 60 ms), and one that gives up
+ * bounded all the same (2^20 polls, a second or so), and one that gives up
  * (not observed) writes NaN to its segment of the row and a nonzero value to
  * the workspace's first 8 bytes.  The environment variable
  * ROWRED_EXCHANGE_SPIN_LIMIT, read on every call, replaces the bound (for

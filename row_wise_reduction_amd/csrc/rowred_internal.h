@@ -132,8 +132,8 @@ struct SegArgs {
   uint32_t spin_limit;  // exchange kernels: polls of one slot before a wait gives up
 };
 
-// Polls of one exchange slot before the wait gives up (about 60 ms at
-// 2.4 GHz with s_sleep 2 between polls).  The environment variable
+// Polls of one exchange slot before the wait gives up (a second or so: each
+// poll is a load that goes past the XCD's L2, then s_sleep 2).  The environment variable
 // ROWRED_EXCHANGE_SPIN_LIMIT overrides it, for tests of the give-up path
 // (0: a wait gives up at its first empty poll).
 constexpr uint32_t kExchangeSpinLimit = 1u << 20;
