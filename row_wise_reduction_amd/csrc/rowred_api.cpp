@@ -371,6 +371,22 @@ void choose_plan(const Call &c, rowred_plan *p) {
     if (l5 * round_up_chunks((w + l5 - 1) / l5) < l4 * round_up_chunks((w + l4 - 1) / l4)) max_chunks = 5;
   }
   int64_t L = lanes_for(max_chunks);
+  // LayerNorm (plain, residual, affine) on rows longer than 256 granules
+  // that do not start on 16-byte boundaries, beyond 32 MiB: 4 slots per lane
+  // (5 beyond 1024 granules) with at most 512 lanes while that takes at most
+  // 8 slots, one row per workgroup (at least 256 threads), rows remapped over
+  // the XCDs (not affine: 1-2% slower there).  7-40% faster than the rules
+  // above at 1023-12287 columns (MI355X, plain 16384x8191 299 -> 179 us,
+  // 131200x1023 236 -> 170 us, residual 16384x8191 366 -> 262 us, affine
+  // 16386x8191 468 -> 365 us, 32776x4095 407 -> 317 us); 16383 columns keep
+  // 1024 x 5.
+  const bool ln_ragged =
+      (kop == ROWRED_OP_LAYERNORM_RESIDUAL || affine) && !rows_aligned && !small && w > 256;
+  if (ln_ragged) {
+    L = lanes_for(w <= 1024 ? 4 : 5);
+    if (w > 384 && w <= 512) L = 256;  // 2 slots: 1537 columns 1-6% faster than 128 x 4
+    if (L > 512 && (w + 511) / 512 <= 8) L = 512;
+  }
   int chunks = round_up_chunks((w + L - 1) / L);
   // A stripe too wide for a 1024-lane workgroup of this kernel: halve the
   // lanes (and so double the stripe) until the kernel exists and fits.
@@ -388,7 +404,7 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // Row sum and min/max take 512 threads, except calls of at most 2^19
   // elements, where 256 are 0.05-0.2 us faster (1x4096 2.41 -> 2.24 us,
   // 256x1024 2.84 -> 2.68 us).
-  const int64_t t_min = (small && !scalar_out) || affine_256 || (scalar_out && tiny) ? 256 : 512;
+  const int64_t t_min = (small && !scalar_out) || affine_256 || (scalar_out && tiny) || ln_ragged ? 256 : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = 0;
@@ -398,7 +414,7 @@ void choose_plan(const Call &c, rowred_plan *p) {
   if (!can_stage && !(scalar_out && w <= 40)) policy |= kPolicyNtLoads;
   if (!scalar_out && (rows_aligned || can_stage || p->chunks <= 2 || w > 256)) policy |= kPolicyNtStores;
   if (can_stage) policy |= kPolicyStageStores;
-  if (rows_aligned && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
+  if ((rows_aligned || (ln_ragged && !affine)) && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
   // Rows of 5-8 slots per 1024-lane workgroup, up to 2048 rows of 8192
   // granules: half the stripe in LDS lets two workgroups share a CU.
   // Softmax 512x32768 and 2048x32768: 14% and 7% faster, RMSNorm 512x32768

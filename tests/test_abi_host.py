@@ -670,7 +670,8 @@ def test_looped_layernorm_needs_two_chunks():
 def test_layernorm_plan_query_affine(rows, width, want):
     """Affine LayerNorm's own geometry rule (256-thread workgroups, 4 slots,
     8 for rows of 1024-2048 granules beyond 32 MiB) on aligned rows; plain
-    LayerNorm keeps the general rules; misaligned affine rows too."""
+    LayerNorm keeps the general rules; misaligned affine rows take plain
+    LayerNorm's geometry (without its XCD remap)."""
     G, B = 0x7F4000000000, 0x7F5000000000
     p = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows=rows, width=width)
     assert (p.lanes_per_row, p.chunks, p.threads) == want
@@ -678,7 +679,9 @@ def test_layernorm_plan_query_affine(rows, width, want):
     q = R.rowred_layernorm_plan_query(X, None, None, None, Y, rows=rows, width=width)
     assert q == R.rowred_plan_query("layernorm_residual", X, None, Y, rows=rows, width=width)
     m = R.rowred_layernorm_plan_query(X + 4, None, G, B, Y + 4, rows=rows, width=width - 1)
-    assert m == R.rowred_layernorm_plan_query(X + 4, None, None, None, Y + 4, rows=rows, width=width - 1)
+    n = R.rowred_layernorm_plan_query(X + 4, None, None, None, Y + 4, rows=rows, width=width - 1)
+    assert (m.lanes_per_row, m.chunks, m.threads) == (n.lanes_per_row, n.chunks, n.threads)
+    assert m.policy == n.policy & ~R.ROWRED_POLICY_XCD_REMAP
 
 
 def test_layernorm_plan_query_errors():
@@ -722,3 +725,22 @@ def test_workspace_size_covers_every_chosen_plan(op):
             for shift in (0, 4, 8, 12):
                 p = R.rowred_split_plan_query(op, X + shift, rows, width)
                 assert p.workspace_bytes <= need, (op, rows, width, shift, p, need)
+
+
+def test_ragged_layernorm_rule():
+    """LayerNorm on misaligned rows of more than 256 granules beyond 32 MiB:
+    4 slots (5 beyond 1024 granules, 2 at 385-512), at most 512 lanes while
+    that takes at most 8 slots, one row per workgroup, XCD remap (not
+    affine).  RMSNorm keeps the general rules."""
+    nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
+    G, B = RR + (1 << 30), RR + (1 << 31)
+    for width, want in ((1023, (128, 3, 256)), (1537, (256, 2, 256)), (2047, (256, 3, 256)), (4095, (256, 5, 256)),
+                        (8191, (512, 5, 512)), (12287, (512, 7, 512)), (16383, (1024, 5, 1024))):
+        rows = (1 << 27) // width
+        for r in (None, RR):
+            p = R.rowred_layernorm_plan_query(X, r, None, None, Y, rows, width)
+            assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (*want, nl | ns | rm), (width, r, p)
+        a = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows, width)
+        assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*want, nl | ns), (width, a)
+    p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=16386, width=8191)
+    assert (p.lanes_per_row, p.chunks, p.threads) == (1024, 3, 1024)
