@@ -71,7 +71,13 @@ def test_variants_alignment(variant, shift, width):
 
 @pytest.mark.parametrize("variant", ["plain", "residual_affine"])
 @pytest.mark.parametrize("width", [100, 1000, 4096])
-def test_variants_every_plan(variant, width):
+@pytest.mark.parametrize("gshift", [1, 0], ids=["gamma_4B", "gamma_16B"])
+def test_variants_every_plan(variant, width, gshift):
+    """Rows one float past 16-byte boundaries; gamma/beta at another phase
+    (4-byte loads) or 16-byte aligned (two 16-byte loads per granule,
+    shifted into the row's phase)."""
+    if variant == "plain" and gshift == 0:
+        pytest.skip("no gamma/beta")
     rows = 67
     x, r, g, b = make(rows, width, 3 * width, variant)
     ref = oracle.layernorm(x, r, eps=1e-5, gamma=g, beta=b)
@@ -79,8 +85,8 @@ def test_variants_every_plan(variant, width):
     for plan in all_plans((width + 6) // 4):
         if g is not None and (plan.chunks > 12 or (plan.chunks >= 7 and plan.threads > 512)):
             continue
-        print_case(variant, width, plan)
-        assert_close(run(x, r, g, b, shift=(1, 1, 1, 1), plan=plan), ref, f"{variant} {width} {plan}")
+        print_case(variant, width, gshift, plan)
+        assert_close(run(x, r, g, b, shift=(1, 1, 1, gshift), plan=plan), ref, f"{variant} {width} {plan}")
         n += 1
     assert n >= 3
 
