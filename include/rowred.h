@@ -365,9 +365,13 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
  * dispatches no later than those of later rows, so every wait ends; each is
  * bounded all the same (2^20 polls, a second or so), and one that gives up
  * (not observed) writes NaN to its segment of the row and a nonzero value to
- * the workspace's first 8 bytes.  The environment variable
- * ROWRED_EXCHANGE_SPIN_LIMIT, read on every call, replaces the bound (for
- * tests of that path: 0 gives up at the first empty poll).  A NULL,
+ * the workspace's first 8 bytes (zeroed once per call).  An explicit plan
+ * (rowred_split_run_plan) may set a smaller bound, for tests of that path.
+ * A row's segments must all be resident on the device at once: when the
+ * current device (its compute units times the exchange kernel's occupancy)
+ * cannot hold twice a row's segments, the entry points run the three
+ * split kernels instead, and an explicit exchange plan gets
+ * ROWRED_ERR_UNSUPPORTED.  A NULL,
  * misaligned or short workspace -> ROWRED_ERR_INVALID_ARG when the split
  * kernels are needed;
  * overlap -> ROWRED_ERR_ALIAS.  Everything else as for the entry points
@@ -406,6 +410,11 @@ typedef struct rowred_split_plan {
   int64_t segments;        /* derived: S = ceil(window / (threads * chunks)) */
   int64_t grid;            /* derived: block_rows * S workgroups per kernel launch */
   int64_t workspace_bytes; /* derived: (block_rows * S + block_rows) * 16 */
+  int32_t wait_polls;      /* exchange plans run by rowred_split_run_plan: polls of an empty slot
+                              after which a wait gives up (0: the default bound, 2^20 polls).
+                              For tests of the give-up path; the _ws entry points always use
+                              the default */
+  int32_t reserved;        /* 0 */
 } rowred_split_plan;
 
 /* Host only.  threads == 0 in *plan: fill in the plan the _ws entry points

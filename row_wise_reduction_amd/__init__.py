@@ -81,7 +81,8 @@ class Plan:
 class _SplitPlan(ctypes.Structure):
     _fields_ = [("threads", ctypes.c_int32), ("chunks", ctypes.c_int32), ("policy", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("block_rows", ctypes.c_int64), ("segments", ctypes.c_int64),
-                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("wait_polls", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 @dataclass
@@ -94,10 +95,12 @@ class SplitPlan:
     segments: int = 0
     grid: int = 0
     workspace_bytes: int = 0
+    wait_polls: int = 0
+    reserved: int = 0
 
     def _c(self) -> _SplitPlan:
         return _SplitPlan(self.threads, self.chunks, self.policy, self.window, self.block_rows, self.segments,
-                          self.grid, self.workspace_bytes)
+                          self.grid, self.workspace_bytes, self.wait_polls, self.reserved)
 
 
 _lib = None
@@ -437,7 +440,8 @@ def rowred_split_plan_query(op, x, rows=None, width=None, plan: SplitPlan = None
     rows, width = _shape([("x", mx)], rows, width)
     c = (plan or SplitPlan())._c()
     _check(lib().rowred_split_plan_query(_op_id(op), mx[0], rows, width, ctypes.byref(c)), "rowred_split_plan_query")
-    return SplitPlan(c.threads, c.chunks, c.policy, c.window, c.block_rows, c.segments, c.grid, c.workspace_bytes)
+    return SplitPlan(c.threads, c.chunks, c.policy, c.window, c.block_rows, c.segments, c.grid, c.workspace_bytes,
+                     c.wait_polls, c.reserved)
 
 
 def rowred_split_run_plan(op, x, r, gamma, beta, y, y2, plan: SplitPlan, workspace, rows=None, width=None, eps=0.0,

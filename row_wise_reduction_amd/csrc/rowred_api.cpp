@@ -3,7 +3,6 @@
 // live in rowred_kernels.hip.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "rowred_internal.h"
 
@@ -705,7 +704,7 @@ int finish_split(const Call &c, rowred_split_plan *p) {
       return ROWRED_ERR_INVALID_ARG;
   }
   if (exchange && ((p->policy & kPolicyReverse) || c.op > ROWRED_OP_SOFTMAX)) return ROWRED_ERR_INVALID_ARG;
-  if (p->block_rows < 0) return ROWRED_ERR_INVALID_ARG;
+  if (p->block_rows < 0 || p->wait_polls < 0 || p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   const int64_t G = T * p->chunks;
   const int64_t br = p->block_rows == 0 || p->block_rows > c.rows ? c.rows : p->block_rows;
   p->block_rows = br;
@@ -718,6 +717,16 @@ int finish_split(const Call &c, rowred_split_plan *p) {
   if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
   p->workspace_bytes = (p->grid + br) * 16;
   return ROWRED_OK;
+}
+
+// The S workgroups of a row wait for each other, so they must all be
+// resident at once.  Workgroups reach each XCD in index order and a row's
+// segments have consecutive indices, so the oldest unfinished row always
+// has its segments dispatched as long as the device holds more than S of
+// them; twice S leaves room for workgroups of the next row (and for other
+// kernels that hold compute units for a while).  Needs the current device.
+bool exchange_fits(int op, const rowred_split_plan &p) {
+  return exchange_resident_groups(op, p.chunks, p.threads, p.policy) >= 2 * p.segments;
 }
 
 int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -747,14 +756,10 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
   a.policy = p.policy;
   a.r_vec = c.r_vec ? 1 : 0;
   a.y_vec = c.y_vec ? 1 : 0;
-  a.spin_limit = kExchangeSpinLimit;
-  if (const char *env = getenv("ROWRED_EXCHANGE_SPIN_LIMIT")) {
-    char *end = nullptr;
-    const unsigned long v = strtoul(env, &end, 10);
-    if (end != env && *end == '\0' && v <= UINT32_MAX) a.spin_limit = (uint32_t)v;
-  }
+  a.spin_limit = p.wait_polls > 0 ? (uint32_t)p.wait_polls : kExchangeSpinLimit;
   // Row blocks run one after another; offsetting every operand by whole
-  // rows keeps r and y at x's 16-byte phase.  The workspace is reused.
+  // rows keeps r and y at x's 16-byte phase.  The workspace is reused; the
+  // exchange status word is cleared by the first block only.
   for (int64_t r0 = 0; r0 < c.rows; r0 += p.block_rows) {
     const int64_t n = c.rows - r0 < p.block_rows ? c.rows - r0 : p.block_rows;
     const int64_t e0 = r0 * c.width;
@@ -765,8 +770,9 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
     a.rows = n;
     // kernel operator = the public op: LayerNorm (any of r, gamma, beta) 0,
     // RMSNorm 1, softmax 2, row sum 3, row min/max 4
-    const int err = (p.policy & kPolicyExchange) ? launch_exchange(c.op, p.chunks, n * p.segments, p.threads, a, stream)
-                                                 : launch_split(c.op, p.chunks, n * p.segments, p.threads, a, stream);
+    const int err = (p.policy & kPolicyExchange)
+                        ? launch_exchange(c.op, p.chunks, n * p.segments, p.threads, a, r0 == 0, stream)
+                        : launch_split(c.op, p.chunks, n * p.segments, p.threads, a, stream);
     if (err != 0) return ROWRED_ERR_HIP;
   }
   return ROWRED_OK;
@@ -807,7 +813,14 @@ int ws_entry(int op, const float *x, const float *r, const float *gamma, const f
   int st = check_ws_call(op, x, r, gamma, beta, y, y2, rows, width, eps, &c);
   if (st != ROWRED_OK || rows == 0 || width == 0) return st;
   rowred_split_plan sp;
-  const bool exchange = !plan && c.window > kMaxWindow && choose_exchange(op, c.rows, c.window, &sp);
+  bool exchange = !plan && c.window > kMaxWindow && choose_exchange(op, c.rows, c.window, &sp);
+  if (exchange) {
+    // the device must hold twice a row's segments at once (else: the other
+    // paths below)
+    st = finish_split(c, &sp);
+    if (st != ROWRED_OK) return st;
+    exchange = exchange_fits(op, sp);
+  }
   if (!plan && !exchange && (c.window <= kMaxWindow || c.rows >= kLoopedMinRows)) {
     rowred_plan p;
     choose_plan(c, &p);
@@ -827,6 +840,7 @@ int ws_entry(int op, const float *x, const float *r, const float *gamma, const f
   }
   st = finish_split(c, &p);
   if (st != ROWRED_OK) return st;
+  if ((p.policy & kPolicyExchange) && !exchange_fits(op, p)) return ROWRED_ERR_UNSUPPORTED;
   return run_split(c, p, eps, ws, ws_bytes, stream);
 }
 

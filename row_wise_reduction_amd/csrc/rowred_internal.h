@@ -133,9 +133,9 @@ struct SegArgs {
 };
 
 // Polls of one exchange slot before the wait gives up (a second or so: each
-// poll is a load that goes past the XCD's L2, then s_sleep 2).  The environment variable
-// ROWRED_EXCHANGE_SPIN_LIMIT overrides it, for tests of the give-up path
-// (0: a wait gives up at its first empty poll).
+// poll is a load that goes past the XCD's L2, then s_sleep 2).  An explicit
+// split plan may set a smaller bound (rowred_split_plan.wait_polls), for
+// tests of the give-up path.
 constexpr uint32_t kExchangeSpinLimit = 1u << 20;
 
 // Chunk counts (16-byte slots per lane) of the split kernels.
@@ -176,7 +176,17 @@ int launch_split(int op, int chunks, int64_t grid, int threads, const SegArgs &a
 // zeroes exchange_words() 64-bit words of the workspace, then one workgroup
 // per (row, segment) keeps its segment in registers and swaps statistics
 // with its row's other segments through those words.
+// clear_status: also zero the status word (the first launch of a call; a
+// call that runs in row blocks clears only the slots for the later blocks,
+// so a give-up in an earlier block stays visible).
 int64_t exchange_words(int op, int64_t rows, int64_t segments);
-int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream);
+int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, bool clear_status,
+                    hipStream_t stream);
+// Workgroups of the exchange kernel for (op, chunks, threads, policy) that
+// the current device holds at once: its compute units times the kernel's
+// occupancy per compute unit (cached per device and kernel).  0 on any HIP
+// error.  A row's S segments wait for each other, so S must stay well below
+// this.
+int64_t exchange_resident_groups(int op, int chunks, int threads, int policy);
 
 }  // namespace rowred

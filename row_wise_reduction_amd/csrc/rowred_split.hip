@@ -40,7 +40,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "rowred_device.h"
 #include "rowred_internal.h"
@@ -918,11 +921,15 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
   else store_all(std::false_type{});
 }
 
-// Zero the status word and the slots (n64 words, 16-byte aligned, n64 even).
-__global__ void __launch_bounds__(256) exchange_clear_kernel(uint64_t *w, int64_t n128) {
+// Zero the 64-bit words [first, 2 * n128) of the exchange area (16-byte
+// aligned): first = 0 clears the status word with the slots, first = 1 the
+// slots only.
+__global__ void __launch_bounds__(256) exchange_clear_kernel(uint64_t *w, int64_t first, int64_t n128) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-  if (i < n128) reinterpret_cast<u64x2 *>(w)[i] = u64x2{0, 0};
+  if (i >= n128) return;
+  if (i == 0 && first == 1) w[1] = 0;  // keep the status word
+  else reinterpret_cast<u64x2 *>(w)[i] = u64x2{0, 0};
 }
 
 using SegFn = void (*)(SegArgs);
@@ -969,22 +976,54 @@ int64_t exchange_words(int op, int64_t rows, int64_t segments) {
   return 1 + (op == kOpLayerNorm ? 2 : 1) * rows * segments;
 }
 
-int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, hipStream_t stream) {
-  SegFn fn = nullptr;
-  if (args.policy & kPolicyLdsStripe) {
+namespace {
+
+// The exchange kernel of a plan, or nullptr.
+SegFn exchange_kernel(int op, int chunks, int threads, int policy) {
+  if (op < 0 || op > 2) return nullptr;
+  if (policy & kPolicyLdsStripe) {
     const int si = xlds_stripe_index(op, chunks);
-    if (op < 0 || op > 2 || si < 0 || threads != kXldsThreads) return (int)hipErrorInvalidValue;
-    fn = kXlds[op][si];
-  } else {
-    const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : chunks == 8 ? 3 : -1;
-    if (op < 0 || op > 2 || ci < 0 || !exchange_kernel_exists(op, chunks) || threads > exchange_max_threads(chunks))
-      return (int)hipErrorInvalidValue;
-    fn = kExchange[op][ci];
+    return si < 0 || threads != kXldsThreads ? nullptr : kXlds[op][si];
   }
+  const int ci = chunks == 1 ? 0 : chunks == 2 ? 1 : chunks == 4 ? 2 : chunks == 8 ? 3 : -1;
+  if (ci < 0 || !exchange_kernel_exists(op, chunks) || threads > exchange_max_threads(chunks)) return nullptr;
+  return kExchange[op][ci];
+}
+
+}  // namespace
+
+int64_t exchange_resident_groups(int op, int chunks, int threads, int policy) {
+  const SegFn fn = exchange_kernel(op, chunks, threads, policy);
+  if (!fn) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, int64_t> cache;
+  const std::pair<int, const void *> key{dev, reinterpret_cast<const void *>(fn)};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), threads, 0) !=
+      hipSuccess)
+    return 0;
+  const int64_t groups = (int64_t)cus * per_cu;
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = groups;
+  return groups;
+}
+
+int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs &args, bool clear_status,
+                    hipStream_t stream) {
+  const SegFn fn = exchange_kernel(op, chunks, threads, args.policy);
   if (!fn || args.segments > threads || args.segments > kMaxExchangeSegments) return (int)hipErrorInvalidValue;
   uint64_t *w = reinterpret_cast<uint64_t *>(args.ws);
   int64_t n128 = (exchange_words(op, args.rows, args.segments) + 1) / 2;
-  void *clear_params[] = {&w, &n128};
+  int64_t first = clear_status ? 0 : 1;  // 64-bit word to start clearing at
+  void *clear_params[] = {&w, &first, &n128};
   int err = (int)hipLaunchKernel(reinterpret_cast<const void *>(exchange_clear_kernel),
                                  dim3((uint32_t)((n128 + kClearThreads - 1) / kClearThreads)), dim3(kClearThreads),
                                  clear_params, 0, stream);

@@ -196,7 +196,8 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
   const int off = (int)(((uintptr_t)xrow >> 2) & 3);
   const int nwin = (width + off + 3) >> 2;
   const int kmax = nwin - 1;
-  const int ntiles = (nwin - kHead + kTile - 1) / kTile;  // >= 1: the row is wider than the head
+  // >= 0: nwin >= kHead (see the head below); 0 when the row ends in the head
+  const int ntiles = (nwin - kHead + kTile - 1) / kTile;
   auto valid_k = [&](int k, int j) -> bool { return (unsigned)(4 * k + j - off) < (unsigned)width; };
   const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
   f32x4 *wave_held = held + (li & ~63);
@@ -219,12 +220,23 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
   if (a.policy & kPolicyNtLoads) load_head(std::true_type{});
   else load_head(std::false_type{});
   __builtin_amdgcn_s_waitcnt(0);
-  // head granule of slot c: c * L + li (all inside the row's window: the row
-  // is wider than the head)
+  // Head granule of slot c: c * L + li.  The plan needs some row's window to
+  // exceed the head, and windows at the four 16-byte phases differ by at
+  // most one granule, so every head granule lies inside this row's window.
+  // Only the first granule (a register slot) can start before the row, and
+  // only the last (an LDS slot) can run past its end -- when this row's
+  // window is exactly the head.  Both are masked to the identity.
 #pragma unroll
   for (int c = 0; c < CR; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) xv[c][j] = valid_k(c * L + li, j) ? xv[c][j] : kIdent;
+  {
+    f32x4 &last = held[(CL - 1) * L + li];  // this lane's own entry of the last LDS slot
+    f32x4 v = last;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = valid_k((C - 1) * L + li, j) ? v[j] : kIdent;
+    last = v;
+  }
   auto head_at = [&](int c) -> f32x4 { return c < CR ? xv[c < CR ? c : 0] : held[(c - CR) * L + li]; };
 
   // ---- the tail: tiles of TC slots, two deep.
@@ -240,6 +252,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_tail_kernel(RowArgs a) {
   // rev: the tiles last to first (the second walk then starts on what the
   // first walk read last, the likeliest to be still in cache)
   auto walk = [&](auto nt, auto f, bool rev) {
+    if (ntiles == 0) return;  // the row ends inside the head
     auto at = [&](int t) { return rev ? ntiles - 1 - t : t; };
     load_tile(nt, at(0), ta);
     for (int t = 0; t < ntiles; t += 2) {
@@ -404,7 +417,8 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
   const int off = (int)(((uintptr_t)xrow >> 2) & 3);
   const int nwin = (width + off + 3) >> 2;
   const int kmax = nwin - 1;
-  const int ntiles = (nwin - kHead + kTile - 1) / kTile;  // >= 1: the row is wider than the head
+  // >= 0: nwin >= kHead (see the head below); 0 when the row ends in the head
+  const int ntiles = (nwin - kHead + kTile - 1) / kTile;
   auto valid_k = [&](int k, int j) -> bool { return (unsigned)(4 * k + j - off) < (unsigned)width; };
   const f32x4 *xw = reinterpret_cast<const f32x4 *>(xrow - off);
   const f32x4 *rw = has_r ? reinterpret_cast<const f32x4 *>(rrow - off) : nullptr;
@@ -455,14 +469,34 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
 #pragma unroll
     for (int c = 0; c < CL; ++c) held_r[c * L + li] = load_r(std::false_type{}, (CR + c) * L + li);
   }
-  // Head granules are all inside the row but the first, which may start
-  // before it: its elements outside the row become 0 (x and r).
+  // The plan needs some row's window to exceed the head, and windows at the
+  // four 16-byte phases differ by at most one granule, so every head granule
+  // lies inside this row's window.  Only the first (a register slot) can
+  // start before the row, and only the last (an LDS slot) can run past its
+  // end -- when this row's window is exactly the head.  Their elements
+  // outside the row become 0 (x and r).
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bool in = valid_k(li, j);
     xv[0][j] = in ? xv[0][j] : 0.0f;
     rv[0][j] = in ? rv[0][j] : 0.0f;
   }
+  {
+    f32x4 &lx = held_x[(CL - 1) * L + li], &lr = held_r[(CL - 1) * L + li];  // this lane's own entries
+    f32x4 vx = lx, vr = lr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = valid_k((C - 1) * L + li, j);
+      vx[j] = in ? vx[j] : 0.0f;
+      vr[j] = in ? vr[j] : 0.0f;
+    }
+    lx = vx;
+    lr = vr;
+  }
+  // Elements of the head inside the row: slots 1 .. C-2 are whole.
+  int n_head = 4 * (C - 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) n_head += (valid_k(li, j) ? 1 : 0) + (valid_k((C - 1) * L + li, j) ? 1 : 0);
   auto head_x = [&](int c) -> f32x4 { return c < CR ? xv[c < CR ? c : 0] : held_x[(c - CR) * L + li]; };
   auto head_r = [&](int c) -> f32x4 { return c < CR ? rv[c < CR ? c : 0] : held_r[(c - CR) * L + li]; };
   // x + r as the exact pair (h, l) (TwoSum).
@@ -486,6 +520,7 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
   f32x4 xa[TC], ra[TC], xb[TC], rb[TC];
   // rev: the tiles last to first (as in the RMSNorm/softmax kernel)
   auto walk = [&](auto nt, auto f, bool rev) {
+    if (ntiles == 0) return;  // the row ends inside the head
     auto at = [&](int t) { return rev ? ntiles - 1 - t : t; };
     load_tile(nt, at(0), xa, ra);
     for (int t = 0; t < ntiles; t += 2) {
@@ -512,7 +547,7 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
         acc_lo += l;
       }
     }
-    const int n_h = 4 * C - (li == 0 ? off : 0);  // the first granule may start before the row
+    const int n_h = n_head;
     const double s_h = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (double)acc_lo;
     const double mu = s_h / (double)n_h;
     const float th = (float)mu;
@@ -525,7 +560,7 @@ __global__ void __launch_bounds__(kWideLanes) ln_tail_kernel(RowArgs a) {
       for (int j = 0; j < 4; ++j) {
         float h, l;
         pair(xx[j], r4[j], h, l);
-        const float d = (c == 0 && !valid_k(li, j)) ? 0.0f : (h - th) + (l - tl);
+        const float d = ((c == 0 || c == C - 1) && !valid_k(c * L + li, j)) ? 0.0f : (h - th) + (l - tl);
         sq[j] = fmaf(d, d, sq[j]);
       }
     }

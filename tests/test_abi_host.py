@@ -744,3 +744,38 @@ def test_ragged_layernorm_rule():
         assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*want, nl | ns), (width, a)
     p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=16386, width=8191)
     assert (p.lanes_per_row, p.chunks, p.threads) == (1024, 3, 1024)
+
+
+def undefined_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", R.LIB_PATH], capture_output=True, text=True).stdout
+    return {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+
+
+def test_library_reads_no_environment():
+    """No entry point reads the environment (getenv racing a setenv on
+    another thread is undefined behaviour, and the library is documented as
+    safe to call from several threads)."""
+    und = undefined_symbols()
+    assert not {"getenv", "secure_getenv", "__secure_getenv"} & und
+
+
+def test_library_never_allocates_device_memory():
+    """The caller owns every buffer: the library references no HIP allocator."""
+    und = undefined_symbols()
+    alloc = {n for n in und if re.match(r"hip(Ext)?(Malloc|Free|MallocAsync|FreeAsync|HostMalloc|HostFree|"
+                                        r"MallocManaged|MallocPitch|Malloc3D|MallocArray|MemPool)", n)}
+    assert not alloc, alloc
+
+
+@pytest.mark.parametrize("kw", [dict(wait_polls=-1), dict(reserved=1)])
+def test_split_plan_rejects_bad_wait_fields(kw):
+    base = dict(threads=256, chunks=8, policy=R.ROWRED_POLICY_EXCHANGE)
+    base.update(kw)
+    with pytest.raises(R.RowRedError) as e:
+        R.rowred_split_plan_query("softmax", X, 8, 100000, plan=R.SplitPlan(**base))
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+    ok = R.rowred_split_plan_query("softmax", X, 8, 100000, plan=R.SplitPlan(threads=256, chunks=8,
+                                                                               policy=R.ROWRED_POLICY_EXCHANGE,
+                                                                               wait_polls=5))
+    assert ok.wait_polls == 5 and ok.segments == 13

@@ -270,13 +270,13 @@ def test_two_streams_at_once():
             check(op, yh[rr:rr + 1], reference(op, xs[i][rr:rr + 1], None, None, None), f"{op} stream {i} row {rr}")
 
 
-def test_wait_give_up_path(monkeypatch):
-    """The bounded wait's give-up path, forced from the host: with
-    ROWRED_EXCHANGE_SPIN_LIMIT=0 a wait gives up at its first empty poll, so
-    every kernel still ends.  Then each output is either NaN (its segment
-    gave up) or the oracle's value (its segment saw every record); some
-    segment gives up and raises the status word.  The next call with the
-    default bound, on the same workspace, clears the word and is exact."""
+def test_wait_give_up_path():
+    """The bounded wait's give-up path, forced from the host: an explicit plan
+    with wait_polls = 1 gives up after one empty re-poll, so every kernel
+    still ends.  Then each output is either NaN (its segment gave up) or the
+    oracle's value (its segment saw every record); some segment gives up and
+    raises the status word.  The next call through the entry point (the
+    default bound), on the same workspace, clears the word and is exact."""
     t = torch()
     rows, width = 256, 65536
     gave_up = False
@@ -286,9 +286,9 @@ def test_wait_give_up_path(monkeypatch):
         plan = R.rowred_split_plan_query(c_op(op), shifted_input(x, 0))
         assert plan.policy & EXCHANGE and plan.segments > 1
         ws = workspace(op, rows, width, plan, shifted_input(x, 0))
-        monkeypatch.setenv("ROWRED_EXCHANGE_SPIN_LIMIT", "0")
+        plan.wait_polls = 1
         print_case("exchange give-up", op, rows, width, plan)
-        got = run(op, x, r, g, b, ws=ws)
+        got = run(op, x, r, g, b, plan=plan, ws=ws)
         status = int(ws[:8].view(t.int64).item())
         nan = np.isnan(got)
         ok = ~nan & ~np.isnan(ref)
@@ -296,9 +296,31 @@ def test_wait_give_up_path(monkeypatch):
         assert status in (0, 1)
         assert (status == 1) == bool(nan.any()), (op, status, int(nan.sum()))
         gave_up |= status == 1
-        monkeypatch.delenv("ROWRED_EXCHANGE_SPIN_LIMIT")
         print_case("exchange after give-up", op)
         again = run(op, x, r, g, b, ws=ws)
         assert status_ok(ws)
         assert_close(again, ref, f"{op} after a give-up")
-    assert gave_up, "no wait gave up at a spin limit of 0"
+    assert gave_up, "no wait gave up at wait_polls = 1"
+
+
+def test_status_survives_row_blocks():
+    """A call in row blocks zeroes the status word once: a give-up in the
+    first block stays visible after the later blocks ran."""
+    t = torch()
+    rows, width = 64, 65536
+    x, r, g, b = make_inputs("softmax", rows, width, seed=4343)
+    plan = R.rowred_split_plan_query(c_op("softmax"), shifted_input(x, 0))
+    assert plan.policy & EXCHANGE
+    ws = workspace("softmax", rows, width, plan, shifted_input(x, 0))
+    for _ in range(3):
+        plan.wait_polls = 1
+        plan.block_rows = rows // 4
+        print_case("exchange blocks give-up", plan)
+        got = run("softmax", x, r, g, b, plan=plan, ws=ws)
+        status = int(ws[:8].view(t.int64).item())
+        nan_rows = np.isnan(got).any(axis=1)
+        assert (status == 1) == bool(nan_rows.any()), (status, int(nan_rows.sum()))
+    plan.wait_polls = 0
+    got = run("softmax", x, r, g, b, plan=plan, ws=ws)
+    assert status_ok(ws)
+    assert_close(got, reference("softmax", x, r, g, b), "softmax blocks after give-up")

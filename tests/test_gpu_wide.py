@@ -272,3 +272,67 @@ def test_layernorm_head_tail_affine_loads(which):
     t.cuda.synchronize()
     assert out.guards_intact()
     assert_close(out.host(), ref, f"affine {which}")
+
+
+def offset_rows(seed, rows, width):
+    """N(0, 8^2) rows shifted by per-row offsets in [-80, 80] (the softmax
+    stress recipe), so a row's max is far from its neighbour's."""
+    x = synthetic.random_matrix(seed, rows, width, "normal") * 8.0
+    off = np.linspace(-80.0, 80.0, rows)[::-1].copy()
+    off[1::2] *= -1.0
+    return (x + off[:, None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("width", [65534, 65535])
+@pytest.mark.parametrize("op", ["rmsnorm", "softmax"])
+def test_head_boundary_widths(op, width):
+    """Widths whose row windows straddle the 16384-granule head: at some
+    16-byte phases a row's window is exactly the head (nothing left for the
+    tail) and its last head granule holds elements of the next row, at others
+    it is one granule longer.  Every x phase, rows at every phase, y at x's
+    phase and at another; the entry point and explicit plans."""
+    t = torch()
+    rows = 8
+    x = offset_rows(width + 7, rows, width)
+    ref = oracle_of(op, x)
+    for shift, y_shift in ((0, 0), (1, 1), (2, 3), (3, 3)):
+        xd = shifted_input(x, shift)
+        out = Guarded(rows, width, y_shift)
+        plan = R.rowred_plan_query(op, xd, None, out.y)
+        print_case("head boundary", op, width, shift, y_shift, plan)
+        if op == "rmsnorm":
+            R.rowred_rmsnorm(xd, out.y, eps=synthetic.EPS["rmsnorm"])
+        else:
+            R.rowred_softmax(xd, out.y)
+        t.cuda.synchronize()
+        assert out.guards_intact()
+        assert_close(out.host(), ref, f"{op} {width} shift {shift} entry point {plan}")
+        if plan.policy & TAIL == TAIL:
+            for pol in (R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_REVERSE):
+                p = R.Plan(1024, 0, 16, 1024, 0, policy=pol | TAIL)
+                assert_close(run(op, xd, p, rows, width, shift, y_shift), ref, f"{op} {width} shift {shift} {p}")
+
+
+@pytest.mark.parametrize("width", [32766, 32767])
+@pytest.mark.parametrize("variant", ["residual", "plain", "affine"])
+def test_layernorm_head_boundary_widths(variant, width):
+    """LayerNorm widths whose row windows straddle the 8192-granule head (x
+    and r held): rows whose window is exactly the head must count and centre
+    only their own elements.  Every x phase, r and y at x's phase and at
+    others, the entry point and explicit plans."""
+    import oracle
+    rows = 8
+    x = offset_rows(width + 51, rows, width)
+    r = synthetic.random_matrix(width + 52, rows, width, "uniform", tensor="r") if variant == "residual" else None
+    g = b = None
+    if variant == "affine":
+        g = (1.0 + 0.1 * synthetic.random_matrix(width + 53, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
+        b = (0.1 * synthetic.random_matrix(width + 54, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
+    ref = oracle.layernorm(x, r, eps=1e-5, gamma=g, beta=b)
+    for sx, sr, sy in ((0, 0, 0), (1, 1, 1), (2, 3, 2), (3, 3, 0)):
+        print_case("layernorm head boundary", variant, width, sx, sr, sy)
+        assert_close(run_ln(x, r, g, b, None, sx, sr, sy), ref, f"{variant} {width} {sx} entry point")
+        if (width + sx + 3) // 4 > 8192 or (width + (sx + width) % 4 + 3) // 4 > 8192:
+            for pol in (R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_REVERSE):
+                p = R.Plan(1024, 0, 8, 1024, 0, policy=pol | TAIL)
+                assert_close(run_ln(x, r, g, b, p, sx, sr, sy), ref, f"{variant} {width} {sx} {p}")
