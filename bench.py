@@ -1,33 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark of the fused FP32 row reductions on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 12] [--lean]
 
 A step is one call of every operator of the workload on one batch of seeded
-synthetic input (the default workload: residual LayerNorm, RMSNorm and
-softmax on 1024x4096 FP32, inputs U[-1, 1]).  Inputs and outputs are
-resident in HBM before timing starts.  Each operator's K timed calls run on
-its own rotation of >= 3 buffer sets totalling >= 2 GiB, so no call finds its
-data in the 256 MB last-level cache; the K calls are captured in one HIP graph per
-operator so the host's launch cost does not gate 5-10 us kernels.  After W
-eager warm-up steps the graphs are replayed, untimed, for 0.2 s; then the
-timed region replays each graph once (exactly K steps), with HIP events on
-the launch stream around each replay: an operator's average call time is
-its replay time / K.  Five more replays give the spread (median, min, max)
-of that measurement; each operator also reports one cold call after a 1 GiB
-flush, a warm rate (K calls on one buffer set, cache-resident where it
-fits) and its fraction of the library's copy moving the same bytes.
+synthetic input.  The default workload is the largest single-GPU one: the
+wide-row configuration (residual LayerNorm, RMSNorm and softmax on
+16384x8192 FP32, inputs U[-1, 1]) plus the softmax stress configuration
+(8192x32768, 8*N(0,1) + U[-80,80] row offsets, 1% -inf): four calls, 6.0 GiB
+of algorithmic traffic per step.  Inputs and outputs are resident in HBM
+before timing starts.  Each operator's K calls run on its own rotation of
+>= 3 buffer sets totalling >= 2 GiB, so no call finds its data in the 256 MB
+last-level cache; the K calls are captured in one HIP graph per operator so
+the host's launch cost does not gate short kernels.  After W eager warm-up
+steps the graphs are replayed, untimed, for 0.2 s; then the timed region is
+ROUNDS rounds, each replaying every operator's graph once (K steps per
+round), with HIP events on the launch stream around each replay.  An
+operator's time per call is the median over the rounds of replay time / K,
+reported with the min-max range; the step time is the median over rounds of
+the round's total / K (the pages' protocol: the median of per-round
+figures, with ranges rather than confidence intervals).  Each operator
+also reports one cold call after a 1 GiB flush, a warm rate (K calls on one
+buffer set) and its fraction of the library's copy moving the same bytes.
+With --lean those extras, the A/A control and the CPU baseline are skipped,
+so that a kernel trace of the run holds only the rotated graphs' calls
+(plus the W eager warm-up calls).
 
 `value` is the whole step's algorithmic bytes (one read of each input and
 one write of the output, 4 B per element each) divided by its time.  The
 JSON line also carries the roofline of the dominant kernel, the FP64 CPU
 oracle's throughput on host cores, and per-operator figures.
 
+    python bench.py --config 2  # one workload (1..12; see WORKLOAD_NAMES)
     python bench.py --pmc --all # counter pass: one dispatch of each kernel of
-                                # workloads 1..7 on cold buffers, + a 256 MiB
+                                # workloads 1..11 on cold buffers, + a 256 MiB
                                 # copy per workload for calibration
     python bench.py --all       # one JSON line per core workload (1..5)
-    python bench.py --next      # plain and affine LayerNorm, row sum / min-max, any width (6-10)
+    python bench.py --next      # plain and affine LayerNorm, row sum / min-max, any width (6-11)
     python bench.py --reload    # resident vs per-phase reload kernels, workloads 2-5
     python bench.py --pmc --reload  # its counter pass
 """
@@ -52,7 +61,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "HBM GB/s and % of peak, FP32 row LayerNorm/RMSNorm/softmax, µs per call"
 POOL_BYTES = 2 * 2 ** 30  # >= 8x the 256 MB last-level cache
 WARMUP_SECONDS = 0.2  # graph replays before the timed region
-ROUNDS = 5  # repeats of the timed measurement, reported as its spread
+ROUNDS = 5  # timed rounds of K steps; figures are their medians, with min-max
 
 # The pages' Apple M1 Max numbers at 1024x4096 (context only, other hardware):
 # "Immutable input reuse in Metal reductions", section "Fixed-width GPU and
@@ -74,11 +83,21 @@ WORKLOAD_NAMES = {
         "4096x65536, RMSNorm 2048x131072, residual LayerNorm 1024x65536, row sum 2048x131072",
     11: "many wide rows (_ws entry points: exchange kernels, row sum looped): softmax 4096x65536, "
         "RMSNorm 2048x131072, residual LayerNorm 1024x65536, row sum 2048x131072",
+    12: "largest single-GPU configurations: residual LayerNorm + RMSNorm + softmax 16384x8192 U[-1,1], "
+        "and softmax stress 8192x32768 (8*N(0,1) + U[-80,80] row offsets, 1% -inf)",
 }
 CORE = (1, 2, 3, 4, 5)
 NEXT = (6, 7, 8, 9, 10, 11)
+LARGEST = 12  # the default: workloads 4 and 5 in one step
+PMC_CFGS = tuple(sorted(set(WORKLOAD_NAMES) - {LARGEST}))  # counter passes: each case once
 WS_WORKLOADS = (9, 11)  # run through the _ws entry points (caller workspace)
-WORKLOADS = {**synthetic.CORE_WORKLOADS, **synthetic.NEXT_WORKLOADS}
+WORKLOADS = {**synthetic.CORE_WORKLOADS, **synthetic.NEXT_WORKLOADS,
+             LARGEST: synthetic.CORE_WORKLOADS[4] + synthetic.CORE_WORKLOADS[5]}
+
+
+def log(*parts):
+    """A progress line on stderr (the JSON result goes to stdout)."""
+    print("bench:", *parts, file=sys.stderr, flush=True)
 
 
 def n_inputs(op):
@@ -197,7 +216,10 @@ def rotation_sets(case):
 def time_workload(cfg, steps, warmup):
     import torch
     cases = WORKLOADS[cfg]
-    bufs = [CaseBuffers(c, rotation_sets(c)) for c in cases]
+    bufs = []
+    for c in cases:
+        bufs.append(CaseBuffers(c, rotation_sets(c)))
+        log(f"inputs of {c.op} {c.rows}x{c.width} resident ({bufs[-1].sets} buffer sets)")
     sets = [b.sets for b in bufs]
     torch.cuda.synchronize()
     for w in range(warmup):
@@ -227,16 +249,15 @@ def time_workload(cfg, steps, warmup):
         if time.perf_counter() - t >= WARMUP_SECONDS:
             break
 
-    # Timed region: exactly `steps` steps -- each case's graph replayed once
-    # between HIP events on the stream the kernels run on (torch's current
-    # stream).
+    # Timed region: ROUNDS rounds of exactly `steps` steps -- each round
+    # replays every case's graph once between HIP events on the stream the
+    # kernels run on (torch's current stream).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    per_case_ms, total_ms = replay_timed(graphs)
+    rounds = [replay_timed(graphs) for _ in range(ROUNDS)]
     wall = time.perf_counter() - t0
-    # The same measurement repeated, outside the reported value: its spread.
-    rounds = [replay_timed(graphs)[0] for _ in range(ROUNDS)]
-    return cases, bufs, sets, per_case_ms, total_ms, wall, rounds
+    log(f"timed {ROUNDS} rounds of {steps} steps in {wall:.3f} s")
+    return cases, bufs, sets, rounds, wall
 
 
 def replay_timed(graphs):
@@ -341,13 +362,34 @@ def cpu_baseline(cases, bufs, seconds, threads=None):
         done_bytes += reps * algo_bytes(dataclasses.replace(c, rows=rows))
         sample_desc.append(f"{c.op} {rows}x{c.width} x{reps}")
     return {"value": round(done_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(sample_desc) + f" ({elapsed:.1f} s, FP64, row blocks over {threads} threads)"}
+            "sample": "; ".join(sample_desc) + f" ({elapsed:.1f} s, FP64, row blocks over {threads} threads)",
+            "cpu_model": cpu_model(), "affinity_cores": affinity_cores(),
+            "thread_rule": "one thread per core of the affinity mask, at most 16 (a GPU's share of the host)"}
 
 
-def read_traffic(cfg, case):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"pmc_traffic_cfg{cfg}.txt")
+def affinity_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def read_traffic(case):
+    """HBM bytes per launch from the committed counter summary of the case's
+    workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_cfg{case.cfg}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -361,55 +403,64 @@ def read_traffic(cfg, case):
     return int(float(v)) if v else None
 
 
-def bench(cfg, steps, warmup, cpu_seconds):
-    cases, bufs, sets, per_case_ms, total_ms, wall, rounds = time_workload(cfg, steps, warmup)
+def spread(v):
+    return {"n": len(v), "median": round(float(np.median(v)), 3), "min": round(min(v), 3), "max": round(max(v), 3)}
+
+
+def bench(cfg, steps, warmup, cpu_seconds, lean=False):
+    cases, bufs, sets, rounds, wall = time_workload(cfg, steps, warmup)
     step_bytes = sum(algo_bytes(c) for c in cases)
-    ms_per_step = total_ms / steps
-    value = step_bytes * steps / (total_ms / 1e3) / 1e9
+    # per round: each case's us per call, and the round's step time in ms
+    case_us = [[r[0][i] * 1e3 / steps for r in rounds] for i in range(len(cases))]
+    step_ms = [sum(r[0]) / steps for r in rounds]
+    ms_per_step = float(np.median(step_ms))
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
     ops = {}
-    for i, (c, b, ms) in enumerate(zip(cases, bufs, per_case_ms)):
-        us = ms * 1e3 / steps
+    for i, (c, b) in enumerate(zip(cases, bufs)):
+        us = float(np.median(case_us[i]))
         gbs = algo_bytes(c) / (us * 1e-6) / 1e9
-        r_us = [r[i] * 1e3 / steps for r in rounds]
-        cold, warm = single_and_warm(b, steps)
-        copy = copy_ceiling(algo_bytes(c))
-        ops[f"{c.op} {c.rows}x{c.width}"] = {
-            "us_per_call": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "frac_of_copy": round(gbs / copy["GB_s"], 4),
-            "rounds_us": {"n": len(r_us), "median": round(float(np.median(r_us)), 3),
-                          "min": round(min(r_us), 3), "max": round(max(r_us), 3)},
-            "single_call_cold_us": round(cold, 3), "warm_us_per_call": round(warm, 3),
-            "inputs": b.inputs}
-    dom = int(np.argmax(per_case_ms))
+        entry = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                 "rounds_us": spread(case_us[i]), "inputs": b.inputs}
+        if not lean:
+            cold, warm = single_and_warm(b, steps)
+            copy = copy_ceiling(algo_bytes(c))
+            entry.update({"frac_of_copy": round(gbs / copy["GB_s"], 4), "single_call_cold_us": round(cold, 3),
+                          "warm_us_per_call": round(warm, 3)})
+        ops[f"{c.op} {c.rows}x{c.width}"] = entry
+    dom = int(np.argmax([np.median(u) for u in case_us]))
     dc = cases[dom]
-    dom_us = per_case_ms[dom] * 1e3 / steps
+    dom_us = float(np.median(case_us[dom]))
     achieved = algo_bytes(dc) / (dom_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(cfg, dc),
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(dc),
             "kernel": f"{dc.op} {dc.rows}x{dc.width}", "bytes_per_launch": algo_bytes(dc),
-            "avg_launch_us": round(dom_us, 3)}
-    aa = aa_control(bufs[dom], steps)
+            "avg_launch_us": round(dom_us, 3), "avg_launch_us_rounds": spread(case_us[dom])}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[cfg], "config_id": cfg,
                    "cases": [f"{c.op} {c.rows}x{c.width} {c.dist}" for c in cases],
-                   "rotation_sets": sets, "timing": f"one HIP graph of {steps} calls per operator on rotating "
-                                                     f"buffer sets (>= 2 GiB per operator), HIP events per replay"},
+                   "rotation_sets": sets,
+                   "timing": f"{ROUNDS} rounds of {steps} steps; each operator's calls in one HIP graph on rotating "
+                             f"buffer sets (>= 2 GiB per operator), HIP events per replay; medians over rounds"},
         "roofline": roof,
         "ops": ops,
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "ms_per_step_rounds": spread(step_ms),
+        "rounds": ROUNDS,
         "wall_s": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
-    out["copy_ceiling"] = {"same_bytes_as_dominant": copy_ceiling(algo_bytes(dc)),
-                           "1GiB": copy_ceiling(2 ** 30, reps=10)}
-    out["launch_floor_us"] = launch_floor()
-    out["aa_control"] = dict(kernel=f"{dc.op} {dc.rows}x{dc.width}", **aa)
+    if not lean:
+        out["copy_ceiling"] = {"same_bytes_as_dominant": copy_ceiling(algo_bytes(dc)),
+                               "1GiB": copy_ceiling(2 ** 30, reps=10)}
+        out["launch_floor_us"] = launch_floor()
+        out["aa_control"] = dict(kernel=f"{dc.op} {dc.rows}x{dc.width}", **aa_control(bufs[dom], steps))
     if cfg == 2:
         out["context_m1max_us"] = M1MAX_CONTEXT_US
-    if cpu_seconds > 0:
+    if cpu_seconds > 0 and not lean:
+        log("oracle on host cores (cpu_baseline)")
         out["cpu_baseline"] = cpu_baseline(cases, bufs, cpu_seconds)
         out["cpu_baseline_1core"] = cpu_baseline(cases, bufs, cpu_seconds / 4, threads=1)
     return out
@@ -615,7 +666,7 @@ def pmc_reload_pass(cfg):
 PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {ctr} --output-format csv -d <out_{ctr}> -o run -- "
            "python3 <repo>/bench.py --pmc --all > <log_{ctr}>")
 TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-             "python3 <repo>/bench.py{args} --cpu-seconds 0")
+             "python3 <repo>/bench.py{args} --lean")
 
 
 def _csv_rows(path):
@@ -654,7 +705,7 @@ def traffic_summary(fetch_csv, write_csv, out_dir, fetch_log=None, write_log=Non
     workload's pass."""
     # One call per case, each after a flush fill: the library dispatches
     # between two other kernels are one call (1 to 3 dispatches).
-    expected = [(cfg, c) for cfg in sorted(WORKLOAD_NAMES) for c in WORKLOADS[cfg]]
+    expected = [(cfg, c) for cfg in PMC_CFGS for c in WORKLOADS[cfg]]
     per_cfg = {}
     for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         i = 0
@@ -781,14 +832,16 @@ def reload_traffic_summary(fetch_csv, write_csv, out_path, fetch_log=None, write
     return out_path
 
 
-def trace_summary(stats_csv, bench_json, out_path):
-    """Write the rocprofv3 kernel statistics of the default benchmark command
-    next to the benchmark's own HIP-event averages."""
+def trace_summary(stats_csv, bench_json, out_path, trace_csv=None):
+    """Write the rocprofv3 kernel statistics of a benchmark command next to
+    the benchmark's own HIP-event figures (its JSON line).  With the
+    per-dispatch trace, also each kernel's median duration."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     lines = [f"# rocprofv3 kernel statistics, workload {b['config']['config_id']}: {b['config']['workload']}",
-             "#   " + TRACE_CMD.format(args=("" if b["config"]["config_id"] == 2 else f" --config {b['config']['config_id']}")
+             "#   " + TRACE_CMD.format(args=("" if b["config"]["config_id"] == LARGEST
+                                         else f" --config {b['config']['config_id']}")
                                    + ("" if b["steps"] == 50 else f" --steps {b['steps']}")),
              f"# kernel_source_hash: {b.get('kernel_source_hash', 'unknown')}",
              "# name | calls | total_ns | average_ns | min_ns | max_ns | percentage"]
@@ -796,7 +849,16 @@ def trace_summary(stats_csv, bench_json, out_path):
         nm = kernel_short_name(r["Name"])
         lines.append(" | ".join([nm, r["Calls"], r["TotalDurationNs"], f"{float(r['AverageNs']):.0f}",
                                  r["MinNs"], r["MaxNs"], f"{float(r['Percentage']):.2f}"]))
-    lines.append("# benchmark (same command without the profiler): HIP-event average per call")
+    if trace_csv:
+        per = {}
+        for r in csv.DictReader(open(trace_csv)):
+            per.setdefault(kernel_short_name(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines.append("# per-dispatch durations from the kernel trace: name | dispatches | median_ns | p10_ns | p90_ns")
+        for nm, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            q = np.percentile(d, [50, 10, 90])
+            lines.append(f"{nm} | {len(d)} | {q[0]:.0f} | {q[1]:.0f} | {q[2]:.0f}")
+    lines.append("# the same run's HIP-event figures (median over rounds of replay time / calls)")
     for k, v in b["ops"].items():
         lines.append(f"bench[{k}]: {v['us_per_call']} us, {v['GB_s']} GB/s")
     lines.append(f"roofline: {json.dumps(b['roofline'])}")
@@ -809,7 +871,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", type=int, default=LARGEST, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--lean", action="store_true",
+                    help="time the rotated graphs only (no cold/warm calls, copy ceiling, A/A control or CPU "
+                         "baseline): the command a kernel trace is taken of")
     ap.add_argument("--all", action="store_true", help="one line per core workload 1..5 (with --pmc: 1..7)")
     ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-11)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
@@ -821,8 +886,8 @@ def main(argv=None):
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_LOG", "WRITE_LOG"),
                     help="write profiles/pmc_traffic_cfg*.txt from two counter passes and their stdout logs "
                          "(no GPU)")
-    ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "BENCH_JSON", "OUT"),
-                    help="write a kernel-trace summary (no GPU)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="FILE",
+                    help="KERNEL_STATS_CSV BENCH_JSON OUT [KERNEL_TRACE_CSV]: write a kernel-trace summary (no GPU)")
     args = ap.parse_args(argv)
     if args.traffic_summary:
         fc, wc, fl, wl = args.traffic_summary
@@ -851,7 +916,7 @@ def main(argv=None):
             pmc_reload_pass(cfg)
         return 0
     if args.pmc:
-        for cfg in (sorted(WORKLOAD_NAMES) if args.all else [args.config]):
+        for cfg in (PMC_CFGS if args.all else [args.config]):
             pmc_pass(cfg)
         return 0
     if args.reload:
@@ -860,7 +925,7 @@ def main(argv=None):
         return 0
     cfgs = list(CORE) if args.all else list(NEXT) if args.next else [args.config]
     for cfg in cfgs:
-        res = bench(cfg, args.steps, args.warmup, args.cpu_seconds if cfg == cfgs[0] else 0.0)
+        res = bench(cfg, args.steps, args.warmup, args.cpu_seconds if cfg == cfgs[0] else 0.0, lean=args.lean)
         print(json.dumps(res), flush=True)
     return 0
 

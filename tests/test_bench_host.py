@@ -30,6 +30,20 @@ def test_rotation_pool_defeats_the_last_level_cache():
             assert n >= 3 and n * bench.algo_bytes(c) >= 2 * 2 ** 30 > 256 * 2 ** 20
 
 
+def test_default_workload_is_the_largest_single_gpu_one():
+    """The default bench line times the wide-row configuration's three
+    operators and the softmax stress configuration: the largest shapes that
+    fit one GPU."""
+    cases = bench.WORKLOADS[bench.LARGEST]
+    assert [(c.op, c.rows, c.width) for c in cases] == [
+        ("layernorm_residual", 16384, 8192), ("rmsnorm", 16384, 8192), ("softmax", 16384, 8192),
+        ("softmax", 8192, 32768)]
+    assert max(bench.algo_bytes(c) for c in cases) == max(bench.algo_bytes(c) for cfg in bench.CORE
+                                                          for c in bench.WORKLOADS[cfg])
+    name = bench.WORKLOAD_NAMES[bench.LARGEST]
+    assert "16384x8192" in name and "8192x32768" in name
+
+
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     msg = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
@@ -47,7 +61,7 @@ def _fake_counter_csv(path, ctr, per_case_kib, copy_kib):
         rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": ctr, "Counter_Value": value})
         did += 1
 
-    for cfg in sorted(bench.WORKLOAD_NAMES):
+    for cfg in bench.PMC_CFGS:
         for c in bench.WORKLOADS[cfg]:
             add("void at::native::vectorized_elementwise_kernel<4, FillFunctor<float> >(int, ...)", 1.0)
             kib = per_case_kib(c)
@@ -78,8 +92,8 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     out.mkdir()
     written = bench.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out),
                                     str(tmp_path / "f.log"), str(tmp_path / "w.log"))
-    assert len(written) == len(bench.WORKLOAD_NAMES)
-    for cfg in bench.WORKLOAD_NAMES:
+    assert len(written) == len(bench.PMC_CFGS)
+    for cfg in bench.PMC_CFGS:
         text = (out / f"pmc_traffic_cfg{cfg}.txt").read_text()
         assert "kernel_source_hash: abc" in text
         for c in bench.WORKLOADS[cfg]:
@@ -117,9 +131,9 @@ def test_committed_traffic_is_used_only_on_matching_sources(tmp_path, monkeypatc
     real_hash = bench.kernel_source_hash()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: real_hash)
-    assert bench.read_traffic(2, case) == 123
+    assert bench.read_traffic(case) == 123
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.read_traffic(2, case) is None
+    assert bench.read_traffic(case) is None
 
 
 def test_short_names():

@@ -36,6 +36,20 @@ def status_ok(ws):
     return int(ws[:8].view(torch().int64).item()) == 0
 
 
+def assert_refused(op, x, r, g, b, plan):
+    """A plan the library does not support: ROWRED_ERR_INVALID_ARG from the
+    host-side query and from the run, with the output untouched."""
+    t = torch()
+    xd = shifted_input(x, 0)
+    with pytest.raises(R.RowRedError) as e:
+        R.rowred_split_plan_query(c_op(op), xd, plan=plan)
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+    with pytest.raises(R.RowRedError) as e:
+        run(op, x, r, g, b, plan=plan)
+    assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+    t.cuda.synchronize()
+
+
 def run_exchange(op, x, r, g, b, plan, shift=0):
     ws = workspace(op, x.shape[0], x.shape[1], plan, shifted_input(x, shift))
     got = run(op, x, r, g, b, plan=plan, shift=shift, ws=ws)
@@ -50,7 +64,11 @@ def test_every_exchange_geometry(op, geom):
     misaligned."""
     T, C = geom
     if C == 8 and op.startswith("layernorm"):
-        pytest.skip("LayerNorm exchanges at up to 4 chunks")
+        # LayerNorm exchanges at up to 4 chunks: the plan is refused before
+        # anything runs
+        x, r, g, b = make_inputs(op, 2, 40000, seed=5)
+        assert_refused(op, x, r, g, b, R.SplitPlan(threads=T, chunks=C, policy=EXCHANGE))
+        return
     G = T * C
     for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 32 - 5, 1), (4 * G * min(128, T) - 9, 2)):
         rows = max(2, min(6, (1 << 21) // width))
@@ -72,7 +90,11 @@ def test_lds_stripe_exchange(op, chunks):
     segments per row, ragged, misaligned (r and y at another 16-byte phase
     than x too), both memory policies."""
     if op.startswith("layernorm") and chunks != 8:
-        pytest.skip("LayerNorm keeps 4 + 4 slots")
+        # LayerNorm keeps 4 + 4 slots: other stripes are refused before
+        # anything runs
+        x, r, g, b = make_inputs(op, 2, 40000, seed=6)
+        assert_refused(op, x, r, g, b, R.SplitPlan(threads=256, chunks=chunks, policy=EXCHANGE | LDS))
+        return
     G = 256 * chunks
     for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 128 - 9, 2)):
         rows = max(2, min(6, (1 << 21) // width))

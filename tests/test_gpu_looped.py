@@ -76,7 +76,13 @@ def test_explicit_looped_plans(op, geom):
     tail), a partial last tile, misaligned rows, both memory policies."""
     T, C = geom
     if op.startswith("layernorm") and C == 4:
-        pytest.skip("LayerNorm loops at 2 chunks only")
+        # LayerNorm loops at 2 chunks only: the plan is refused before
+        # anything runs
+        x, r, g, b = make_inputs(op, 2, 40000, seed=9)
+        with pytest.raises(R.RowRedError) as e:
+            run(op, x, r, g, b, plan=looped_plan(T, C))
+        assert e.value.status == R.ROWRED_ERR_INVALID_ARG
+        return
     G = T * C
     for width, shift in ((4 * G * 3 - 7, 1), (4 * G * 4 + 5, 3), (4 * G, 0), (5, 2)):
         x, r, g, b = make_inputs(op, 4, width, seed=width * 7 + T)
