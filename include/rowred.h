@@ -431,6 +431,35 @@ int rowred_split_run_plan(int op, const float *x, const float *r, const float *g
                           float *y2, int64_t rows, int64_t width, float eps, const rowred_split_plan *plan,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory at all -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * _ws entry points with a workspace that the library itself holds, a static
+ * device array of ROWRED_STATIC_WORKSPACE_BYTES on each GPU, kept from the
+ * first call on that GPU until the process ends.  Nothing is allocated per
+ * call.
+ *
+ * op (enum rowred_op) selects the operator; the arguments are those of
+ * rowred_split_run_plan without plan and workspace (r, gamma, beta only with
+ * ROWRED_OP_LAYERNORM_RESIDUAL, each optional: rowred_layernorm_ws; y2 only
+ * with ROWRED_OP_ROW_MINMAX: y = out_min, y2 = out_max; y = out for
+ * ROWRED_OP_ROW_SUM; eps only where the operator has one).  Plans and results
+ * are those of the matching _ws entry point (bitwise, for the same device).
+ * Call it with the stream's device current: the first call on a device looks
+ * up that device's copy of the array.
+ *
+ * A call whose plan needs more workspace than the array holds (rows * (S + 1)
+ * * 16 bytes with S segments per row, see rowred_workspace_size) returns
+ * ROWRED_ERR_UNSUPPORTED before anything is enqueued; calls whose rows fit
+ * the register-resident or looped kernels use no workspace and have no such
+ * limit.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind: calls that may overlap in time on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller.
+ */
+#define ROWRED_STATIC_WORKSPACE_BYTES (8LL << 20)
+int rowred_static_ws(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y,
+                     float *y2, int64_t rows, int64_t width, float eps, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,6 +145,7 @@ def lib():
             "rowred_split_plan_query": [ctypes.c_int, _P, _I64, _I64, ctypes.POINTER(_SplitPlan)],
             "rowred_split_run_plan": [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float,
                                       ctypes.POINTER(_SplitPlan), _P, ctypes.c_size_t, _P],
+            "rowred_static_ws": [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P],
         }
         for name, argtypes in sigs.items():
             fn = getattr(L, name)
@@ -463,6 +464,27 @@ def rowred_split_run_plan(op, x, r, gamma, beta, y, y2, plan: SplitPlan, workspa
                                      ay, ay2, rows, width, float(eps), ctypes.byref(c), wa, wn,
                                      _stream(stream, x, r, gamma, beta, y, y2, workspace))
     _check(st, "rowred_split_run_plan")
+
+
+ROWRED_STATIC_WORKSPACE_BYTES = 8 << 20  # the library's static workspace per GPU (rowred_static_ws)
+
+
+def rowred_static_ws(op, x, r, gamma, beta, y, y2=None, rows=None, width=None, eps=0.0, stream=None):
+    """The _ws entry point of `op` on the library's static workspace (no
+    workspace argument; nothing allocated).  For row_sum / row_minmax, y
+    (and y2) are row vectors."""
+    op = _op_id(op)
+    mx, mr = _matrix(x, "x", rows, width), _matrix(r, "r", rows, width)
+    if op in (ROWRED_OP_ROW_SUM, ROWRED_OP_ROW_MINMAX):
+        rows, width = _shape([("x", mx)], rows, width)
+        ay, ay2 = _row_vector(y, "y", rows), _row_vector(y2, "y2", rows)
+    else:
+        my = _matrix(y, "y", rows, width)
+        rows, width = _shape([("x", mx), ("r", mr), ("y", my)], rows, width)
+        ay, ay2 = my[0], _row_vector(y2, "y2", rows)
+    st = lib().rowred_static_ws(op, mx[0], mr[0], _vector(gamma, "gamma", width), _vector(beta, "beta", width),
+                                ay, ay2, rows, width, float(eps), _stream(stream, x, r, gamma, beta, y, y2))
+    _check(st, "rowred_static_ws")
 
 
 def rowred_copy(x, y, n=None, stream=None):

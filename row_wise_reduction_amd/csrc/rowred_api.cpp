@@ -729,9 +729,12 @@ bool exchange_fits(int op, const rowred_split_plan &p) {
   return exchange_resident_groups(op, p.chunks, p.threads, p.policy) >= 2 * p.segments;
 }
 
-int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, hipStream_t stream) {
+// static_ws: the library's own workspace (rowred_static_ws), whose size is
+// a limit of the library rather than an argument error.
+int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, bool static_ws,
+              hipStream_t stream) {
   if (!ws || ((uintptr_t)ws & 15)) return ROWRED_ERR_INVALID_ARG;
-  if ((int64_t)ws_bytes < p.workspace_bytes) return ROWRED_ERR_INVALID_ARG;
+  if ((int64_t)ws_bytes < p.workspace_bytes) return static_ws ? ROWRED_ERR_UNSUPPORTED : ROWRED_ERR_INVALID_ARG;
   // the workspace overlaps none of the operands
   const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)p.workspace_bytes;
   auto hit = [&](const void *b, int64_t nb) {
@@ -808,7 +811,7 @@ constexpr int64_t kLoopedMinRows = 2048;
 // three split kernels.
 int ws_entry(int op, const float *x, const float *r, const float *gamma, const float *beta, float *y, float *y2,
              int64_t rows, int64_t width, float eps, const rowred_split_plan *plan, void *ws, size_t ws_bytes,
-             hipStream_t stream) {
+             hipStream_t stream, bool static_ws = false) {
   Call c;
   int st = check_ws_call(op, x, r, gamma, beta, y, y2, rows, width, eps, &c);
   if (st != ROWRED_OK || rows == 0 || width == 0) return st;
@@ -841,7 +844,12 @@ int ws_entry(int op, const float *x, const float *r, const float *gamma, const f
   st = finish_split(c, &p);
   if (st != ROWRED_OK) return st;
   if ((p.policy & kPolicyExchange) && !exchange_fits(op, p)) return ROWRED_ERR_UNSUPPORTED;
-  return run_split(c, p, eps, ws, ws_bytes, stream);
+  if (static_ws) {  // the library's array, looked up only once a call needs it
+    const int e = static_workspace(&ws);
+    if (e != 0) return ROWRED_ERR_HIP;
+    ws_bytes = (size_t)ROWRED_STATIC_WORKSPACE_BYTES;
+  }
+  return run_split(c, p, eps, ws, ws_bytes, static_ws, stream);
 }
 
 }  // namespace
@@ -996,6 +1004,11 @@ ROWRED_API int rowred_row_minmax_ws(const float *x, float *out_min, float *out_m
                                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
   return ws_entry(ROWRED_OP_ROW_MINMAX, x, nullptr, nullptr, nullptr, out_min, out_max, rows, width, 0.0f, nullptr,
                   workspace, workspace_bytes, stream);
+}
+
+ROWRED_API int rowred_static_ws(int op, const float *x, const float *r, const float *gamma, const float *beta,
+                                float *y, float *y2, int64_t rows, int64_t width, float eps, hipStream_t stream) {
+  return ws_entry(op, x, r, gamma, beta, y, y2, rows, width, eps, nullptr, nullptr, 0, stream, true);
 }
 
 ROWRED_API int rowred_split_plan_query(int op, const float *x, int64_t rows, int64_t width,

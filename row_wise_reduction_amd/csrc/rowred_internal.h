@@ -189,4 +189,10 @@ int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs
 // this.
 int64_t exchange_resident_groups(int op, int chunks, int threads, int policy);
 
+// The library's static workspace on the current device (rowred_static_ws):
+// ROWRED_STATIC_WORKSPACE_BYTES, 256-byte aligned.  The first call on a
+// device looks up that device's copy of the array; later calls reuse the
+// address.  Returns the hipError_t of the lookup (0 = success).
+int static_workspace(void **ptr);
+
 }  // namespace rowred

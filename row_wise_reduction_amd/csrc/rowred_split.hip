@@ -992,6 +992,33 @@ SegFn exchange_kernel(int op, int chunks, int threads, int policy) {
 
 }  // namespace
 
+// The workspace of rowred_static_ws, for callers that cannot allocate: one
+// copy per GPU, held until the process ends.  Host code must not pass the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// static_workspace() looks up each device's address once and hands that out.
+static __device__ __align__(256) uint8_t scratch[ROWRED_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+int static_workspace(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p || ((uintptr_t)p & 255)) return (int)hipErrorInvalidValue;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
+}
+
 int64_t exchange_resident_groups(int op, int chunks, int threads, int policy) {
   const SegFn fn = exchange_kernel(op, chunks, threads, policy);
   if (!fn) return 0;
