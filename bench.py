@@ -125,7 +125,7 @@ def kernel_source_hash():
     for p in ("row_wise_reduction_amd/csrc/rowred_kernels.hip", "row_wise_reduction_amd/csrc/rowred_api.cpp",
               "row_wise_reduction_amd/csrc/rowred_internal.h", "row_wise_reduction_amd/csrc/rowred_device.h",
               "row_wise_reduction_amd/csrc/rowred_split.hip", "row_wise_reduction_amd/csrc/rowred_looped.hip",
-              "row_wise_reduction_amd/csrc/rowred_wide.hip"):
+              "row_wise_reduction_amd/csrc/rowred_wide.hip", "row_wise_reduction_amd/csrc/rowred_flat.hip"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -850,11 +850,13 @@ def trace_summary(stats_csv, bench_json, out_path, trace_csv=None):
         lines.append(" | ".join([nm, r["Calls"], r["TotalDurationNs"], f"{float(r['AverageNs']):.0f}",
                                  r["MinNs"], r["MaxNs"], f"{float(r['Percentage']):.2f}"]))
     if trace_csv:
+        # one kernel may serve several shapes: keyed by kernel and grid size
         per = {}
         for r in csv.DictReader(open(trace_csv)):
-            per.setdefault(kernel_short_name(r["Kernel_Name"]), []).append(
-                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        lines.append("# per-dispatch durations from the kernel trace: name | dispatches | median_ns | p10_ns | p90_ns")
+            key = f"{kernel_short_name(r['Kernel_Name'])} [grid {r['Grid_Size_X']}]"
+            per.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines.append("# per-dispatch durations from the kernel trace, by kernel and grid size (work-items): "
+                     "name | dispatches | median_ns | p10_ns | p90_ns")
         for nm, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
             q = np.percentile(d, [50, 10, 90])
             lines.append(f"{nm} | {len(d)} | {q[0]:.0f} | {q[1]:.0f} | {q[2]:.0f}")

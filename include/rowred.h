@@ -246,7 +246,7 @@ enum rowred_policy {
                                      (threads <= 512; not LayerNorm).
                                      NT_LOADS / NT_STORES apply to its loads and stores;
                                      REVERSE may not be set */
-  ROWRED_POLICY_LDS_STRIPE = 256  /* row plans: RMSNorm and softmax, lanes_per_row == threads
+  ROWRED_POLICY_LDS_STRIPE = 256, /* row plans: RMSNorm and softmax, lanes_per_row == threads
                                      == 1024, chunks 5-16: slots 0-3 (from 9 chunks on 0-7)
                                      of each lane stay in registers and the rest are loaded
                                      straight into LDS (16-byte loads that write LDS).  At
@@ -259,6 +259,18 @@ enum rowred_policy {
                                      (4 in registers + 4 in LDS), 12 (8 + 4) or 16 (8 + 8),
                                      LayerNorm at 8 only; x (and r) of the LDS slots go
                                      straight into LDS */
+  ROWRED_POLICY_FLAT = 512        /* row plans, RMSNorm and softmax, width >= 4: a workgroup of
+                                     `threads` (64-512) lanes takes rows_per_group consecutive
+                                     rows as one run of 16-byte granules, lane after lane
+                                     (chunks 1, 2 or 4 granules per lane), so no lane slot
+                                     idles past a row's end; each granule's partial
+                                     statistics (its two rows' parts) are folded per row in
+                                     LDS, and whole granules are stored.  Derived:
+                                     rows_per_group = min(threads, (4 * threads * chunks - 3)
+                                     / width), lanes_per_row = the lanes that fold one
+                                     row (the largest power of two <= threads / rows_per_group,
+                                     at most 64).  NT_LOADS / NT_STORES / XCD_REMAP apply; no
+                                     other bit may be set */
 };
 
 /*

@@ -37,6 +37,7 @@ ROWRED_POLICY_REVERSE = 32
 ROWRED_POLICY_LOOPED = 64
 ROWRED_POLICY_EXCHANGE = 128
 ROWRED_POLICY_LDS_STRIPE = 256
+ROWRED_POLICY_FLAT = 512
 ROWRED_MAX_WIDTH = 2146435071  # widest row any entry point takes (2^31 - 2^20 - 1)
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0

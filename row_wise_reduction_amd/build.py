@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "librowred.so")
 ASM = os.path.join(PKG, "_build", "rowred_kernels-gfx950.s")
 
 DEVICE_SOURCES = [os.path.join(CSRC, "rowred_kernels.hip"), os.path.join(CSRC, "rowred_split.hip"),
-                  os.path.join(CSRC, "rowred_looped.hip"), os.path.join(CSRC, "rowred_wide.hip")]
+                  os.path.join(CSRC, "rowred_looped.hip"), os.path.join(CSRC, "rowred_wide.hip"),
+                  os.path.join(CSRC, "rowred_flat.hip")]
 SOURCES = DEVICE_SOURCES + [os.path.join(CSRC, "rowred_api.cpp")]
 HEADERS = [os.path.join(CSRC, "rowred_internal.h"), os.path.join(CSRC, "rowred_device.h"),
            os.path.join(INCLUDE, "rowred.h")]

@@ -154,7 +154,34 @@ int finish_wide_tail_plan(const Call &c, rowred_plan *p) {
   return ROWRED_OK;
 }
 
+// A flat plan (ROWRED_POLICY_FLAT): RMSNorm or softmax, rows of at least 4
+// elements; the workgroup takes rows_per_group consecutive rows as one run of
+// threads * chunks granules, lane after lane.
+int finish_flat_plan(const Call &c, rowred_plan *p) {
+  const int kop = kernel_op(c);
+  const int64_t T = p->threads, C = p->chunks;
+  if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || c.width < 4) return ROWRED_ERR_INVALID_ARG;
+  if (T < 64 || T > kFlatMaxThreads || T % 64 != 0 || (C != 1 && C != 2 && C != 4))
+    return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyFlat | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
+  if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
+  // rows_per_group: the run of P rows at any 16-byte phase fits T * C granules
+  int64_t P = (4 * T * C - 3) / c.width;
+  if (P > T) P = T;
+  if (P < 1) return ROWRED_ERR_INVALID_ARG;
+  int64_t lpr = 1;
+  while (lpr < 64 && 2 * lpr * P <= T) lpr *= 2;
+  p->lanes_per_row = (int32_t)lpr;
+  p->rows_per_group = (int32_t)P;
+  p->window = c.window;
+  p->vector_io = c.y_vec ? 1 : 0;
+  p->grid = (c.rows + P - 1) / P;
+  if (p->grid > INT32_MAX || p->grid * T > (int64_t)UINT32_MAX) return ROWRED_ERR_UNSUPPORTED;
+  return ROWRED_OK;
+}
+
 int finish_plan(const Call &c, rowred_plan *p) {
+  if (p->policy & kPolicyFlat) return finish_flat_plan(c, p);
   if ((p->policy & kPolicyLooped) && (p->policy & kPolicyLdsStripe)) return finish_wide_tail_plan(c, p);
   if (p->policy & kPolicyLooped) return finish_looped_plan(c, p);
   if (p->policy & kPolicyLdsStripe) return finish_lds_plan(c, p);
@@ -327,6 +354,27 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->reserved = 0;
     return;
   }
+  // RMSNorm and softmax rows that do not start on 16-byte boundaries, up to
+  // 384 granules (1536 columns): the flat kernels, whose lanes take a
+  // workgroup's rows as one run of granules (no slot idles past a row's end,
+  // whole-granule stores).  MI355X, 2^25 elements per matrix, against the
+  // rules below: RMSNorm 63, 127, 257 and 1023 columns 46.6 -> 43.2,
+  // 46.2 -> 43.4, 46.2 -> 45.3, 54.2 -> 45.5 us (512 lanes x 2 granules);
+  // softmax 63, 127, 257, 509, 1023 columns 51.4 -> 46.0, 50.5 -> 45.9,
+  // 51.2 -> 49.9, 48.4 -> 47.5, 64.6 -> 48.7 us (256 x 4; softmax keeps the
+  // rules below for rows of under 16 granules, 17 columns: 47.1 against 47.8).
+  // 1537 columns and up: within 1% either way.
+  const bool flat = (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && !rows_aligned && c.y_vec &&
+                    c.width >= 4 && w <= 384 && (c.op == ROWRED_OP_RMSNORM || w >= 16);
+  if (flat) {
+    const bool rms = c.op == ROWRED_OP_RMSNORM;
+    p->lanes_per_row = 0;  // derived by finish_plan
+    p->threads = rms ? 512 : 256;
+    p->chunks = rms ? 2 : 4;
+    p->policy = kPolicyFlat | kPolicyNtLoads | kPolicyNtStores;
+    p->reserved = 0;
+    return;
+  }
   // Outputs are staged only for rows of at most 256 granules, where a
   // workgroup holds many rows whose boundary lines it shares: at 127-769
   // columns staging is 1-40% faster at 65536-262144 rows; from 1537 columns
@@ -447,8 +495,10 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
                   ((uintptr_t)c.beta & 15) == 0)
                      ? 1
                      : 0;
+  a.group_rows = plan.rows_per_group;
   const bool looped = (plan.policy & kPolicyLooped) != 0, lds = (plan.policy & kPolicyLdsStripe) != 0;
-  const int err = looped && lds ? launch_wide_tail(kernel_op(c), plan.grid, a, stream)
+  const int err = (plan.policy & kPolicyFlat) ? launch_flat(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
+                  : looped && lds ? launch_wide_tail(kernel_op(c), plan.grid, a, stream)
                   : looped      ? launch_looped(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
                   : lds         ? launch_wide(kernel_op(c), plan.chunks, plan.grid, a, stream)
                                 : launch_rows(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream);

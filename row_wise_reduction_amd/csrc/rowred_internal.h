@@ -25,6 +25,7 @@ struct RowArgs {
   int32_t r_vec;       // 1: r shares x's address modulo 16 (16-byte loads)
   int32_t y_vec;       // 1: y shares x's address modulo 16 (16-byte stores)
   int32_t affine_vec;  // 1: rows start on 16-byte boundaries and gamma/beta are 16-byte aligned
+  int32_t group_rows;  // flat kernels: rows per workgroup (P)
 };
 
 constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;
@@ -34,6 +35,7 @@ constexpr int kPolicyStageStores = ROWRED_POLICY_STAGE_STORES;
 constexpr int kPolicyReload = ROWRED_POLICY_RELOAD;
 constexpr int kPolicyLooped = ROWRED_POLICY_LOOPED;
 constexpr int kPolicyLdsStripe = ROWRED_POLICY_LDS_STRIPE;
+constexpr int kPolicyFlat = ROWRED_POLICY_FLAT;
 constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload |
                            kPolicyLooped | kPolicyLdsStripe;
 // The per-phase reload variant exists for the three matrix operators (kernel
@@ -99,6 +101,16 @@ int launch_wide_tail(int op, int64_t rows, const RowArgs &args, hipStream_t stre
 // LayerNorm's head in that kernel: x and r of 8 granules per lane (4 in
 // registers, 4 in LDS).
 constexpr int kLnTailHeadChunks = 8;
+
+// Enqueue the flat kernel (ROWRED_POLICY_FLAT): RMSNorm (op 1) or softmax
+// (op 2), rows of at least 4 elements, args.group_rows rows per workgroup of
+// `threads` (64..512) lanes holding `chunks` (1, 2 or 4) granules each,
+// args.lanes_log2 = log2 of the lanes that fold one row (<= 6).
+constexpr int kFlatMaxThreads = 512;
+constexpr size_t flat_lds_bytes(int chunks, int threads, int group_rows) {
+  return (4 * (size_t)threads * chunks + 2 * ((size_t)group_rows + 1)) * 4;
+}
+int launch_flat(int op, int chunks, int64_t grid, int threads, const RowArgs &args, hipStream_t stream);
 
 // Enqueue the streaming copy (n4 = number of 16-byte slots).
 int launch_copy(const float *x, float *y, int64_t n4, hipStream_t stream);

@@ -71,6 +71,17 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
         r = RR + 4 * mis
         p = R.rowred_plan_query(op, x, r, y, rows=rows, width=width)
         L, T = p.lanes_per_row, p.threads
+        if p.policy & R.ROWRED_POLICY_FLAT:
+            # short rows off 16-byte boundaries (RMSNorm, softmax): rows_per_group
+            # rows as one run of threads * chunks granules at any phase, and
+            # lanes_per_row lanes fold each row
+            assert op in ("rmsnorm", "softmax") and width >= 4 and p.policy & ~R.ROWRED_POLICY_FLAT == 3
+            P = p.rows_per_group
+            assert (T, p.chunks) in ((512, 2), (256, 4)) and P == min(T, (4 * T * p.chunks - 3) // width) >= 1
+            assert P * width + 3 <= 4 * T * p.chunks
+            assert L & (L - 1) == 0 and 1 <= L <= 64 and L * P <= T and (L == 64 or 2 * L * P > T)
+            assert p.grid == -(-rows // P) and p.window == window(x, rows, width) and p.vector_io == 1
+            continue
         assert L & (L - 1) == 0 and 1 <= L <= 1024
         assert T % 64 == 0 and 64 <= T <= 1024 and T % L == 0
         assert p.chunks in CHUNKS
@@ -95,8 +106,10 @@ def test_plan_for_workload_shapes():
     # the shapes of the five workloads, aligned buffers
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
     st = R.ROWRED_POLICY_STAGE_STORES
-    # short ragged rows (staged, <= 256 granules) keep cached loads
-    cases = {(131072, 127): (16, 3, ns | st), (131072, 257): (32, 3, ns | st),
+    # short ragged rows: flat plans (256 lanes x 4 granules for softmax;
+    # lanes_per_row is the lanes that fold one row)
+    fl = R.ROWRED_POLICY_FLAT
+    cases = {(131072, 127): (8, 4, fl | nl | ns), (131072, 257): (16, 4, fl | nl | ns),
              (131072, 1537): (256, 2, nl | ns), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
              (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
              (17, 257): (64, 2, nl), (7, 1537): (256, 2, nl), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
@@ -113,9 +126,12 @@ def test_plan_memory_policy():
     st = R.ROWRED_POLICY_STAGE_STORES
     # small, every row on a 16-byte boundary: streaming, no remap, no staging
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=64, width=4096).policy == nl | ns
-    # short rows share boundary lines: outputs staged in LDS, streaming
-    # stores, cached loads (each boundary granule is read twice)
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=16384, width=127).policy == ns | st
+    # short rows share boundary lines: RMSNorm and softmax read them as one
+    # run of granules (flat), streaming; LayerNorm stages its outputs in LDS,
+    # with streaming stores and cached loads (each boundary granule is read twice)
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=16384, width=127).policy == \
+        R.ROWRED_POLICY_FLAT | nl | ns
+    assert R.rowred_plan_query("layernorm_residual", X, RR, Y, rows=16384, width=127).policy == ns | st
     # longer ragged rows (> 256 granules): unstaged, streaming
     assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2049).policy == nl | ns

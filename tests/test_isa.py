@@ -61,8 +61,9 @@ def test_every_kernel_is_spill_free(asm):
     # and their clear kernel, the LDS-stripe kernels (2 operators x 12 stripes,
     # and 5 with a walked tail: RMSNorm, softmax, LayerNorm plain and with
     # gamma/beta read 4 or 16 bytes at a time), the LDS-stripe exchange kernels (LayerNorm 1,
-    # RMSNorm and softmax 3 each)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 5 + 7
+    # RMSNorm and softmax 3 each) and the flat kernels (RMSNorm and softmax at
+    # 1, 2, 4 chunks)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 5 + 7 + 2 * 3
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
