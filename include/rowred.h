@@ -120,7 +120,10 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
  * are the affine form named in the tolerance list of "Cooperating-program
  * packing: implementation and fixed-plan evidence", section "Predeclared
  * comparison and measurement".  gamma and beta hold `width` floats each
- * (4-byte aligned, read only, must not overlap y).  With all three NULL
+ * (4-byte aligned, read only, must not overlap y); when 16-byte aligned
+ * they are read 16 bytes at a time, as whole granules -- up to 12 bytes past
+ * the last element, inside its granule -- at any alignment of the rows.
+ * With all three NULL
  * this is the no-affine LayerNorm of the same page's "Validation" section.
  * With gamma or beta, rows of more than 6144 granules (24576 floats for
  * 16-byte aligned rows) take the looped kernels (gamma/beta need registers

@@ -425,7 +425,9 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // the XCDs (not affine: 1-2% slower there).  7-40% faster than the rules
   // above at 1023-12287 columns (MI355X, plain 16384x8191 299 -> 179 us,
   // 131200x1023 236 -> 170 us, residual 16384x8191 366 -> 262 us, affine
-  // 16386x8191 468 -> 365 us, 32776x4095 407 -> 317 us); 16383 columns keep
+  // 16386x8191 468 -> 365 us, 32776x4095 407 -> 317 us, and with gamma /
+  // beta on 16-byte boundaries read 16 bytes at a time and shifted into the
+  // row's phase: 285 and 256 us; 16384x8191 283.6 us); 16383 columns keep
   // 1024 x 5.
   const bool ln_ragged =
       (kop == ROWRED_OP_LAYERNORM_RESIDUAL || affine) && !rows_aligned && !small && w > 256;
@@ -496,6 +498,12 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
                      ? 1
                      : 0;
   a.group_rows = plan.rows_per_group;
+  // affine rows off 16-byte boundaries with gamma / beta on them: 16-byte
+  // gamma / beta loads shifted into each row's phase (a kernel of its own)
+  a.affine_shift = (c.gamma || c.beta) && !a.affine_vec && ((uintptr_t)c.gamma & 15) == 0 &&
+                           ((uintptr_t)c.beta & 15) == 0
+                       ? 1
+                       : 0;
   const bool looped = (plan.policy & kPolicyLooped) != 0, lds = (plan.policy & kPolicyLdsStripe) != 0;
   const int err = (plan.policy & kPolicyFlat) ? launch_flat(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
                   : looped && lds ? launch_wide_tail(kernel_op(c), plan.grid, a, stream)

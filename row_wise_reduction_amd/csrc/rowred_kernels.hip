@@ -47,7 +47,14 @@ namespace {
 // ---------------------------------------------------------------------------
 // `threads` is blockDim.x, read in the kernel itself: there the compiler
 // knows workgroups are uniform and reads it with a scalar load.
-template <int OP, int C, bool RELOAD>
+//
+// SHIFT (affine LayerNorm only): rows that do not start on 16-byte
+// boundaries, with gamma and beta on them.  Element e = 4k + j - off of a
+// row (k the slot's granule) is gamma[e], which lies in gamma granules k - 1
+// and k; both are read 16 bytes at a time and shifted into the row's phase,
+// instead of four 4-byte loads per vector.  A kernel of its own, so the
+// other affine kernels keep their code.
+template <int OP, int C, bool RELOAD, bool SHIFT = false>
 __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
   __shared__ float partials[2][16];
   __shared__ double partials_d[16];
@@ -75,6 +82,7 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
   // at the window edges and in slots past the window.
   auto elem = [&](int c, int j) -> int { return 4 * (c * L + li) + j - off; };
   auto valid = [&](int c, int j) -> bool { return (unsigned)elem(c, j) < (unsigned)width; };
+  auto gran = [&](int c) -> int { return min(c * L + li, kmax); };  // slot c's granule, clamped into the row
 
   float s[4 * C];
 
@@ -283,8 +291,32 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
     constexpr bool kAffine = OP == kOpLayerNormAffine;
     constexpr bool kEarlyAffine = kAffine && C <= 4;
     f32x4 gv[kEarlyAffine ? C : 1], bv[kEarlyAffine ? C : 1];
+    // SHIFT: gamma / beta elements 4k - off .. 4k + 3 - off, from granules
+    // k - 1 (its last off floats) and k (its first 4 - off), clamped into the
+    // vector (the clamped granules only feed elements outside the row).
+    auto shifted = [&](const float *v, int k, float dflt) -> f32x4 {
+      if (!v) return f32x4(dflt);
+      const f32x4 *vg = reinterpret_cast<const f32x4 *>(v);
+      const f32x4 lo = load_g<false>(vg + max(k - 1, 0));
+      const f32x4 hi = load_g<false>(vg + min(k, (width - 1) >> 2));
+      f32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // r[j] = (lo, hi)[4 - off + j]
+        const float s1 = j == 0 ? lo[3] : hi[j - 1];
+        const float s2 = j < 2 ? lo[2 + j] : hi[j - 2];
+        const float s3 = j < 3 ? lo[1 + j] : hi[j - 3];
+        r[j] = off == 0 ? hi[j] : off == 1 ? s1 : off == 2 ? s2 : s3;
+      }
+      return r;
+    };
     auto load_affine = [&]() {
-      if constexpr (kEarlyAffine) {
+      if constexpr (kEarlyAffine && SHIFT) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          gv[c] = shifted(a.gamma, gran(c), 1.0f);
+          bv[c] = shifted(a.beta, gran(c), 0.0f);
+        }
+      } else if constexpr (kEarlyAffine) {
         if (a.affine_vec) {  // rows start on 16-byte boundaries: row granule k is gamma/beta granule k
 #pragma unroll
           for (int c = 0; c < C; ++c) {
@@ -323,7 +355,10 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         f32x4 g, b;
-        if (a.affine_vec) {
+        if (SHIFT) {
+          g = shifted(a.gamma, gran(c), 1.0f);
+          b = shifted(a.beta, gran(c), 0.0f);
+        } else if (a.affine_vec) {
           const int k = min(c * L + li, kmax);
           g = a.gamma ? load_g<false>(reinterpret_cast<const f32x4 *>(a.gamma) + k) : f32x4(1.0f);
           b = a.beta ? load_g<false>(reinterpret_cast<const f32x4 *>(a.beta) + k) : f32x4(0.0f);
@@ -441,6 +476,13 @@ __global__ void __launch_bounds__(max_threads_for(OP, C)) rows_kernel(RowArgs a)
   row_body<OP, C, false>(a, blockDim.x);
 }
 
+// Affine LayerNorm on rows off 16-byte boundaries with gamma and beta on
+// them (see row_body).
+template <int C>
+__global__ void __launch_bounds__(max_threads_for(kOpLayerNormAffine, C)) affine_shift_kernel(RowArgs a) {
+  row_body<kOpLayerNormAffine, C, false, true>(a, blockDim.x);
+}
+
 // The per-phase reload variant (ROWRED_POLICY_RELOAD): same arithmetic, the
 // row read again in every phase after the first.
 template <int OP, int C>
@@ -485,6 +527,12 @@ static_assert(kOpLayerNormAffine == 5 && kOpRowSum == 3 && kOpRowMinMax == 4, "k
 
 static_assert(kNumChunkSizes == 11, "kernel table rows must match kChunkSet");
 
+// [chunk index in kChunkSet]; affine LayerNorm stops at 12 slots
+const KernelFn kAffineShift[kNumChunkSizes] = {
+    affine_shift_kernel<1>, affine_shift_kernel<2>, affine_shift_kernel<3>, affine_shift_kernel<4>,
+    affine_shift_kernel<5>, affine_shift_kernel<6>, affine_shift_kernel<7>, affine_shift_kernel<8>,
+    affine_shift_kernel<10>, affine_shift_kernel<12>, nullptr};
+
 template <int OP, int C>
 constexpr KernelFn reload_or_null() {
   if constexpr (reload_kernel_exists(OP, C)) return reload_kernel<OP, C>;
@@ -517,7 +565,8 @@ int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &ar
   if (op < 0 || op >= kNumKernelOps || ci < 0) return (int)hipErrorInvalidValue;
   const bool reload = (args.policy & kPolicyReload) != 0;
   if (reload && op > 2) return (int)hipErrorInvalidValue;
-  KernelFn fn = reload ? kReloadKernels[op][ci] : kKernels[op][ci];
+  const bool shift = op == kOpLayerNormAffine && args.affine_shift;
+  KernelFn fn = reload ? kReloadKernels[op][ci] : shift ? kAffineShift[ci] : kKernels[op][ci];
   if (!fn) return (int)hipErrorInvalidValue;
   RowArgs a = args;
   void *params[] = {&a};

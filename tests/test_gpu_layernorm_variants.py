@@ -106,3 +106,28 @@ def test_next_workloads_full_size(case):
         t = min(case.rows, s + blk)
         ref = oracle.layernorm(x[s:t], None, eps=case.eps, gamma=g, beta=b)
         assert_close(y[s:t], ref, f"{case.name} rows {s}:{t}")
+
+
+@pytest.mark.parametrize("width,xshift", [(8191, 0), (8192, 1), (4097, 3)])
+def test_misaligned_affine_full_size(width, xshift):
+    """Affine LayerNorm at full size on rows off 16-byte boundaries (odd width,
+    or the matrix one or three floats past a boundary) with gamma / beta
+    16-byte aligned: the chooser's own plan, sampled rows against the oracle,
+    every element checked for finiteness and the guards."""
+    rows = 16384
+    print_case("affine misaligned", rows, width, xshift)
+    x = synthetic.random_matrix(91 + width, rows, width, "uniform")
+    g = (1 + 0.1 * synthetic.random_matrix(92 + width, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
+    b = (0.1 * synthetic.random_matrix(93 + width, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
+    xd = shifted_input(x, xshift)
+    gd, bd = dev(g), dev(b)
+    out = Guarded(rows, width, xshift)
+    R.rowred_layernorm(xd, None, gd, bd, out.y, eps=1e-5)
+    torch().cuda.synchronize()
+    assert out.guards_intact()
+    y = out.host()
+    assert np.isfinite(y).all()
+    pick = np.unique(np.concatenate([np.arange(4), rows - 1 - np.arange(4),
+                                     np.random.default_rng(width).integers(0, rows, 120)]))
+    ref = oracle.layernorm(x[pick], None, eps=1e-5, gamma=g, beta=b)
+    assert_close(y[pick], ref, f"affine {rows}x{width} shift {xshift}")

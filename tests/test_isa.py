@@ -61,15 +61,16 @@ def test_every_kernel_is_spill_free(asm):
     # and their clear kernel, the LDS-stripe kernels (2 operators x 12 stripes,
     # and 5 with a walked tail: RMSNorm, softmax, LayerNorm plain and with
     # gamma/beta read 4 or 16 bytes at a time), the LDS-stripe exchange kernels (LayerNorm 1,
-    # RMSNorm and softmax 3 each) and the flat kernels (RMSNorm and softmax at
-    # 1, 2, 4 chunks)
-    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 5 + 7 + 2 * 3
+    # RMSNorm and softmax 3 each), the flat kernels (RMSNorm and softmax at
+    # 1, 2, 4 chunks) and the affine LayerNorm kernels for rows off 16-byte
+    # boundaries with 16-byte gamma/beta loads (10 chunk counts)
+    assert len(meta) == 5 * 11 + 10 + 3 * 8 + 1 + 15 + 9 + 5 + 9 + 11 + 1 + 24 + 5 + 7 + 2 * 3 + 10
     for name, m in meta.items():
         # No scratch memory at all.  The 10/12/16-chunk kernels (reachable only
         # through an explicit plan) may park SGPRs in VGPR lanes.
         assert m["private"] == 0 and m["vspill"] == 0, (demangle(name), m)
         dn = demangle(name)
-        wide = any(f", {c}>" in dn for c in (10, 12, 16))  # never picked by the chooser
+        wide = any(f", {c}>" in dn or f"<{c}>" in dn for c in (10, 12, 16))  # never picked by the chooser
         if not wide:
             assert m["sspill"] == 0, (dn, m)
 
