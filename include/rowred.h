@@ -200,7 +200,8 @@ typedef struct rowred_plan {
   int32_t reserved;       /* 0 */
 } rowred_plan;
 
-/* Memory policy bits of a plan.  They change speed, never results. */
+/* Policy bits of a plan.  They change speed; all but ROWRED_POLICY_ONLINE
+ * leave the results bit for bit unchanged. */
 enum rowred_policy {
   ROWRED_POLICY_NT_LOADS = 1,   /* loads carry the non-temporal (streaming) hint */
   ROWRED_POLICY_NT_STORES = 2,  /* stores carry the non-temporal hint */
@@ -256,11 +257,11 @@ enum rowred_policy {
                                      5-8 chunks two workgroups then fit a CU, with the
                                      register kernel's arithmetic in the same order (same
                                      bits); at 9-16 chunks rows of up to 16384 granules are
-                                     read once.  NT_LOADS / NT_STORES / XCD_REMAP apply; no
-                                     other bit may be set.
+                                     read once.  NT_LOADS / NT_STORES / XCD_REMAP (and for
+                                     softmax ONLINE) apply; no other bit may be set.
                                      split plans (with EXCHANGE only): 256 threads, chunks 8
                                      (4 in registers + 4 in LDS), 12 (8 + 4) or 16 (8 + 8),
-                                     LayerNorm at 8 only; x (and r) of the LDS slots go
+                                     x (and r) of the LDS slots go
                                      straight into LDS */
   ROWRED_POLICY_FLAT = 512        /* row plans, RMSNorm and softmax, width >= 4: a workgroup of
                                      `threads` (64-512) lanes takes rows_per_group consecutive
@@ -273,8 +274,30 @@ enum rowred_policy {
                                      / width), lanes_per_row = the lanes that fold one
                                      row (the largest power of two <= threads / rows_per_group,
                                      at most 64).  NT_LOADS / NT_STORES / XCD_REMAP apply; no
-                                     other bit may be set */
+                                     other bit may be set */,
+  ROWRED_POLICY_ONLINE = 1024     /* row plans, softmax only, with the register kernels (no
+                                     RELOAD, LOOPED or FLAT) or LDS_STRIPE at 5-16 chunks: the
+                                     row max and the exponential sum take one workgroup
+                                     collective instead of two.  Each lane keeps the max m of
+                                     its own elements and the sum of exp(x - m) over them; the
+                                     row max M is taken and every sum restated under it
+                                     (multiplied by exp(m - M)) before they are added, and
+                                     output element x of a lane with max m is exp(x - m) *
+                                     (exp(m - M) / S) for the row's M and S.  Same operator,
+                                     other rounding (within the softmax tolerance, not bit for
+                                     bit equal to the two-collective order); register and LDS
+                                     stripes of the same chunks still agree bit for bit */
 };
+
+/* Bits 12-15 of a row plan's policy (register kernels only, not FLAT, LOOPED or
+ * LDS_STRIPE): n = ROWRED_POLICY_CU_GROUPS_OF(policy), 1-14, caps the
+ * workgroups that share a compute unit at n by reserving for each
+ * floor(160 KiB / n) of LDS (rounded down to 1 KiB), most of it unused; 0
+ * sets no cap (register and LDS use alone decide).  A cap means fewer waves
+ * per SIMD.  Speed only; 15 is rejected. */
+#define ROWRED_POLICY_CU_GROUPS_SHIFT 12
+#define ROWRED_POLICY_CU_GROUPS(n) ((int32_t)(n) << ROWRED_POLICY_CU_GROUPS_SHIFT)
+#define ROWRED_POLICY_CU_GROUPS_OF(policy) (((policy) >> ROWRED_POLICY_CU_GROUPS_SHIFT) & 15)
 
 /*
  * Host-only: fill *out with the plan the matching entry point would launch

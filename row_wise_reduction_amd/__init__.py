@@ -38,6 +38,15 @@ ROWRED_POLICY_LOOPED = 64
 ROWRED_POLICY_EXCHANGE = 128
 ROWRED_POLICY_LDS_STRIPE = 256
 ROWRED_POLICY_FLAT = 512
+ROWRED_POLICY_ONLINE = 1024
+ROWRED_POLICY_CU_GROUPS_SHIFT = 12
+
+
+def ROWRED_POLICY_CU_GROUPS(n: int) -> int:
+    """Policy bits capping the workgroups per compute unit at n (1-14)."""
+    return int(n) << ROWRED_POLICY_CU_GROUPS_SHIFT
+
+
 ROWRED_MAX_WIDTH = 2146435071  # widest row any entry point takes (2^31 - 2^20 - 1)
 
 ROWRED_OP_LAYERNORM_RESIDUAL = 0

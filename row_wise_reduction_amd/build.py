@@ -60,13 +60,16 @@ def device_asm(path: str = ASM) -> str:
     one file (for resource/ISA checks)."""
     os.makedirs(os.path.dirname(path), exist_ok=True)
     parts = []
+    tag = f"{os.getpid()}"  # concurrent callers (parallel test workers) write their own files
     for i, src in enumerate(DEVICE_SOURCES):
-        part = f"{path}.{i}"
+        part = f"{path}.{tag}.{i}"
         _run([HIPCC, *COMMON, "--cuda-device-only", "-S", "-o", part, src])
         parts.append(open(part).read())
         os.remove(part)
-    with open(path, "w") as f:
+    tmp = f"{path}.{tag}"
+    with open(tmp, "w") as f:
         f.write("\n".join(parts))
+    os.replace(tmp, path)
     return path
 
 

@@ -121,7 +121,9 @@ int finish_lds_plan(const Call &c, rowred_plan *p) {
   if ((kop != ROWRED_OP_RMSNORM && kop != ROWRED_OP_SOFTMAX) || p->lanes_per_row != 1024 || p->threads != 1024 ||
       p->chunks < kWideMinChunks || p->chunks > kWideMaxChunks)
     return ROWRED_ERR_INVALID_ARG;
-  if (p->policy & ~(kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap)) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyOnline))
+    return ROWRED_ERR_INVALID_ARG;
+  if ((p->policy & kPolicyOnline) && kop != ROWRED_OP_SOFTMAX) return ROWRED_ERR_INVALID_ARG;
   if (p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
   p->window = c.window;
   p->vector_io = c.y_vec ? 1 : 0;
@@ -192,6 +194,10 @@ int finish_plan(const Call &c, rowred_plan *p) {
   if (!chunks_supported(p->chunks) || !kernel_exists(kop, p->chunks) || T > max_threads_for(kop, p->chunks))
     return ROWRED_ERR_INVALID_ARG;
   if (p->policy & ~kPolicyAll) return ROWRED_ERR_INVALID_ARG;
+  const int cap = ROWRED_POLICY_CU_GROUPS_OF(p->policy);
+  if (cap == 15) return ROWRED_ERR_INVALID_ARG;
+  if ((p->policy & kPolicyOnline) && (kop != ROWRED_OP_SOFTMAX || (p->policy & kPolicyReload)))
+    return ROWRED_ERR_INVALID_ARG;
   if ((p->policy & kPolicyReload) &&
       (!reload_kernel_exists(kop, p->chunks) || T > reload_max_threads_for(kop, p->chunks)))
     return ROWRED_ERR_INVALID_ARG;
@@ -279,8 +285,11 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->lanes_per_row = 1024;
     p->threads = 1024;
     p->chunks = (int32_t)((c.window + 1023) / 1024);
+    // softmax with one (max, sum) collective: 1024x50257 86.7 -> 83.4 us,
+    // 4096x65536 383 -> 377 us (MI355X)
     p->policy = kPolicyLdsStripe | kPolicyNtLoads | kPolicyNtStores |
-                (aligned && c.rows * c.width * 4 > (int64_t(64) << 20) ? kPolicyXcdRemap : 0);
+                (aligned && c.rows * c.width * 4 > (int64_t(64) << 20) ? kPolicyXcdRemap : 0) |
+                (c.op == ROWRED_OP_SOFTMAX ? kPolicyOnline : 0);
     p->reserved = 0;
     return;
   }
@@ -375,6 +384,60 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->reserved = 0;
     return;
   }
+  // Large calls (beyond 64 MiB per input) on 16-byte aligned rows of
+  // 128-2048 granules (RMSNorm, softmax, LayerNorm without gamma/beta;
+  // residual LayerNorm to 8192 granules): a geometry per width band and a cap
+  // on the workgroups sharing a CU (ROWRED_POLICY_CU_GROUPS).  Sweeps of
+  // geometry x cap (0-10) at 2^27 elements per matrix (MI355X) put the
+  // fastest plans at about 40-64 KiB of loads in flight per CU (threads per
+  // CU x slots x 16 bytes) for one input and 64-128 KiB with r; more waves
+  // than that only queue behind one another.  Against the rules below:
+  //   RMSNorm    512, 1024, 2048, 4096, 8192 columns: 173.9 -> 164.0,
+  //              170.1 -> 164.6, 170.1 -> 166.1, 169.3 -> 167.8, 170.0 -> 166.9 us
+  //   softmax    170.0 -> 165.6, 170.5 -> 165.3, 169.0 -> 165.7, 167.9 -> 166.0,
+  //              176.3 -> 166.0 us
+  //   residual LayerNorm 1024, 2048, 4096, 8192, 16384, 32768 columns:
+  //              261.6 -> 246.8, 260.4 -> 252.6, 256.3 -> 247.9, 253.2 -> 247.4,
+  //              291.4 -> 269.1, 290.5 -> 280.6 us
+  // (caps of 3 and 5 measured as 2 and 4: use even caps above 1).
+  const bool two_in = c.r != nullptr && c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
+  if (rows_aligned && in_bytes > (int64_t(64) << 20) && !scalar_out && !affine && w >= 128 &&
+      w <= (two_in ? 8192 : 2048)) {
+    const bool sm = c.op == ROWRED_OP_SOFTMAX;
+    int64_t L = 0, C = 0, T = 0, cap = 0;
+    if (w <= 256) {
+      L = 1;
+      while (2 * L < w) L *= 2;
+      C = 2;
+      T = sm ? 256 : (L > 128 ? L : 128);
+      cap = sm ? 6 : 10;
+    } else if (w <= 512) {
+      L = 256;
+      C = 2;
+      T = 256;
+      cap = 6;
+    } else if (w <= 1024) {
+      L = two_in ? 256 : 128;
+      C = two_in ? 4 : 8;
+      T = two_in ? 512 : 256;
+      cap = 2;
+    } else if (w <= 2048) {
+      L = two_in ? 512 : 256;
+      C = two_in ? 4 : 8;
+      T = two_in ? 512 : 256;
+      cap = two_in ? 0 : 2;
+    } else {  // residual LayerNorm: 512 lanes, 8 or 16 slots
+      L = 512;
+      C = w <= 4096 ? 8 : 16;
+      T = 512;
+    }
+    p->lanes_per_row = (int32_t)L;
+    p->chunks = (int32_t)C;
+    p->threads = (int32_t)T;
+    p->policy = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | ROWRED_POLICY_CU_GROUPS(cap);
+    p->reserved = 0;
+    return;
+  }
   // Outputs are staged only for rows of at most 256 granules, where a
   // workgroup holds many rows whose boundary lines it shares: at 127-769
   // columns staging is 1-40% faster at 65536-262144 rows; from 1537 columns
@@ -464,13 +527,21 @@ void choose_plan(const Call &c, rowred_plan *p) {
   if (!scalar_out && (rows_aligned || can_stage || p->chunks <= 2 || w > 256)) policy |= kPolicyNtStores;
   if (can_stage) policy |= kPolicyStageStores;
   if ((rows_aligned || (ln_ragged && !affine)) && in_bytes > (int64_t(64) << 20)) policy |= kPolicyXcdRemap;
-  // Rows of 5-8 slots per 1024-lane workgroup, up to 2048 rows of 8192
-  // granules: half the stripe in LDS lets two workgroups share a CU.
-  // Softmax 512x32768 and 2048x32768: 14% and 7% faster, RMSNorm 512x32768
-  // 6%; from 8192 rows within +-2% (measured on MI355X), so not used there.
+  // Rows of 5-8 slots per 1024-lane workgroup: half the stripe in LDS lets
+  // two workgroups share a CU.  Softmax 512x32768 and 2048x32768: 14% and 7%
+  // faster, RMSNorm 512x32768 6% (MI355X).  Softmax, whose exponentials add
+  // ALU work to overlap, keeps the LDS stripe at every row count (8192x32768
+  // 383 -> 364 us, 16384x32768 763 -> 720 us, with one (max, sum)
+  // collective); RMSNorm only up to 2048 rows of 8192 granules (8192x32768
+  // 355 us in registers, 363 with the LDS stripe).
   if ((c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && L == 1024 && p->threads == 1024 &&
-      p->chunks >= 5 && p->chunks <= 8 && c.rows * w <= kLdsStripeMaxGranules)
+      p->chunks >= 5 && p->chunks <= 8 && (c.op == ROWRED_OP_SOFTMAX || c.rows * w <= kLdsStripeMaxGranules))
     policy |= kPolicyLdsStripe;
+  // Softmax across a 1024-lane row beyond 64 MiB: one (max, sum) collective
+  // instead of two (8192x16384 177.4 -> 174.9 us; 2048x32768 97.7 -> 94.1 us
+  // with the LDS stripe).
+  if (c.op == ROWRED_OP_SOFTMAX && L == 1024 && ((policy & kPolicyLdsStripe) || in_bytes > (int64_t(64) << 20)))
+    policy |= kPolicyOnline;
   p->policy = policy;
   p->reserved = 0;
 }
@@ -660,32 +731,40 @@ void choose_split(int op, int64_t rows, int64_t width, rowred_split_plan *p) {
 // call on buffers rotated through >= 2 GiB.  A workgroup pays a fixed
 // latency (its loads, then the wait for its row's other segments) that only
 // more bytes per workgroup amortise:
-//   * RMSNorm and softmax: 256 threads x 8 register slots, best or within 4%
-//     at every wide shape (2 slots per lane were 1.5-2x slower).  Rows that
-//     would take more than 64 such segments: 8 register + 8 LDS slots
-//     (LDS_STRIPE; 64x1048576 softmax 108 us against 120 for 512 x 8), then
-//     512 x 8.  The LDS stripe is 2-23% slower where 256 x 8 fits.
+//   * the time a row's workgroups spend waiting for each other grows with the
+//     segments per row S, at any segment size (2^26-element matrices,
+//     softmax at 256 x 8: S = 8, 16, 32, 64, 128 take 93, 96, 106, 118, 140
+//     us; 8 + 8 LDS slots: S = 8, 16, 32, 64, 128: 96, 97, 101, 109, 124 us),
+//     so the segment grows with the row to keep S low;
+//   * RMSNorm and softmax: 256 threads x 8 register slots up to 16 segments
+//     (2 slots per lane were 1.5-2x slower), then 8 register + 8 LDS slots
+//     (LDS_STRIPE) up to 64 (256x262144 softmax 106 -> 97 us, 128x524288
+//     118 -> 101 us, RMSNorm 102 -> 95 and 115 -> 100 us); wider rows take
+//     the three split kernels (32x2097152 softmax 121 us against 124 for
+//     128 segments of 8 + 8);
 //   * LayerNorm, whose x and r both take slots: 4 register + 4 LDS slots
-//     (LDS_STRIPE), 10% faster than 256 x 4 registers at 1024x65536 and 25%
-//     at 256x262144; rows beyond 64 of those segments: 1024 x 4.
+//     (LDS_STRIPE; 10% faster than 256 x 4 registers at 1024x65536, 25% at
+//     256x262144) up to 32 segments, then 8 + 8 up to 128 (64x1048576 194 ->
+//     174 us, 32x2097152 211 -> 188 us), then 1024 x 4.
 //   * rows narrower than two segments of the first geometry take the first
 //     of 256 x 4, 256 x 2, 128 x 2, 64 x 2 whose segment is at most half the
 //     row (else 64 x 1): few-row shapes are latency bound and gain from more,
 //     shorter segments;
 //   * streaming loads and stores, as everywhere on rows read once.
 // `window`: the row's 16-byte granules (the x at hand's, or the worst phase's
-// for sizing).  False when no geometry cuts the row into at most
-// kExchangeChosenSegments.  More, shorter segments per row measured slower:
-// 256 x 8 at 128 segments was 15% behind 512 x 8 at 64 on 64x1048576
-// softmax.  Keeping a row's segments on one XCD was 25-60% slower everywhere.
+// for sizing).  False when no geometry cuts the row into at most its
+// max_segments.  Keeping a row's segments on one XCD was 25-60% slower
+// everywhere.  kExchangeChosenSegments bounds the halved segments of calls
+// with few workgroups (below).
 constexpr int64_t kExchangeChosenSegments = 64;
 struct ExchangeGeometry {
   int threads, chunks;
   bool lds;
+  int max_segments;  // the widest row (in segments) the geometry is chosen for
 };
 constexpr ExchangeGeometry kExchangeWide[2][3] = {
-    {{256, 8, true}, {1024, 4, false}, {0, 0, false}},  // LayerNorm
-    {{256, 8, false}, {256, 16, true}, {512, 8, false}},  // RMSNorm, softmax
+    {{256, 8, true, 32}, {256, 16, true, 128}, {1024, 4, false, 64}},  // LayerNorm
+    {{256, 8, false, 16}, {256, 16, true, 64}, {0, 0, false, 0}},      // RMSNorm, softmax
 };
 constexpr int kExchangeNarrow[][2] = {{256, 4}, {256, 2}, {128, 2}, {64, 2}, {64, 1}};
 
@@ -706,7 +785,7 @@ bool choose_exchange(int op, int64_t rows, int64_t window, rowred_split_plan *p)
       if (!g.threads) break;
       const int64_t G = (int64_t)g.threads * g.chunks;
       const int64_t S = (w + G - 1) / G;
-      if (S <= kExchangeChosenSegments && S <= g.threads) {
+      if (S <= g.max_segments && S <= g.threads) {
         T = g.threads;
         C = g.chunks;
         lds = g.lds;

@@ -168,6 +168,42 @@ __device__ __forceinline__ void row_allreduce_pair(float &v1, float &v2, int lan
   }
 }
 
+// Softmax statistics as (max m, sum s of exp(x - m)) pairs.  A sum taken
+// under max m restated under a max M >= m: s * exp(m - M) (s itself when
+// m == M, which also keeps (-inf, 0) from becoming NaN).
+__device__ __forceinline__ float rescale_sum(float s, float m, float M) {
+  return m == M ? s : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+}
+
+// Row all-reduce of (max, sum) pairs with one barrier: the max over the lane
+// group (butterfly), each lane's sum restated under it, the sum over the
+// group; then one pair per wave through LDS and a fixed-order fold (the row
+// max, then the waves' sums restated under it and added in wave order).  All
+// lanes of a row end with the same bits.  Special values: a NaN or +inf in
+// any sum gives a NaN sum; pairs (-inf, 0) add nothing.
+__device__ __forceinline__ void row_allreduce_online(float &m, float &s, int lanes_log2, float *pm, float *ps) {
+  const int g = lanes_log2 < 6 ? lanes_log2 : 6;
+  const float mg = group_allreduce<MaxOp>(m, g);
+  s = group_allreduce<SumOp>(rescale_sum(s, m, mg), g);
+  m = mg;
+  if (lanes_log2 > 6) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      pm[wave] = m;
+      ps[wave] = s;
+    }
+    __syncthreads();
+    const int per_row_log2 = lanes_log2 - 6;
+    const int first = (wave >> per_row_log2) << per_row_log2;
+    float M = pm[first];
+    for (int w = 1; w < (1 << per_row_log2); ++w) M = fmaxf(M, pm[first + w]);
+    float S = 0.0f;
+    for (int w = 0; w < (1 << per_row_log2); ++w) S += rescale_sum(ps[first + w], pm[first + w], M);
+    m = M;
+    s = S;
+  }
+}
+
 // Workgroup -> row block.  The dispatcher deals workgroups to the 8 XCDs in
 // turn; give XCD x the contiguous block range [x*q + min(x, rem), ...).
 __device__ __forceinline__ int64_t row_block(uint32_t bid, uint32_t nblk, bool remap) {

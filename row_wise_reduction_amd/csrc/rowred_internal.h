@@ -37,8 +37,16 @@ constexpr int kPolicyReload = ROWRED_POLICY_RELOAD;
 constexpr int kPolicyLooped = ROWRED_POLICY_LOOPED;
 constexpr int kPolicyLdsStripe = ROWRED_POLICY_LDS_STRIPE;
 constexpr int kPolicyFlat = ROWRED_POLICY_FLAT;
+constexpr int kPolicyOnline = ROWRED_POLICY_ONLINE;
+constexpr int kPolicyCuGroups = ROWRED_POLICY_CU_GROUPS(15);  // the field's mask
 constexpr int kPolicyAll = kPolicyNtLoads | kPolicyNtStores | kPolicyXcdRemap | kPolicyStageStores | kPolicyReload |
-                           kPolicyLooped | kPolicyLdsStripe;
+                           kPolicyLooped | kPolicyLdsStripe | kPolicyOnline | kPolicyCuGroups;
+// LDS per compute unit (gfx950), and the LDS a register-kernel workgroup
+// reserves so that at most n (1-14) share a CU: floor(160 KiB / n) rounded
+// down to 1 KiB, less 256 bytes for the kernel's own partials -- (n + 1) such
+// workgroups never fit.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr size_t cu_groups_lds_bytes(int n) { return (kLdsPerCu / n) / 1024 * 1024 - 256; }
 // The per-phase reload variant exists for the three matrix operators (kernel
 // ops 0-2) at up to 8 chunks.
 constexpr int kMaxReloadChunks = 8;
@@ -173,11 +181,11 @@ constexpr int exchange_max_threads(int chunks) { return chunks >= 8 ? 512 : 1024
 constexpr bool exchange_kernel_exists(int op, int chunks) { return chunks != 8 || op != 0; }
 // Exchange kernels with part of the segment in LDS (ROWRED_POLICY_LDS_STRIPE
 // on a split plan): 256 threads; chunks 8 (4 in registers + 4 in LDS), 12
-// (8 + 4) or 16 (8 + 8); LayerNorm at 8 only.  -1: no such kernel.
+// (8 + 4) or 16 (8 + 8), for x and, LayerNorm, r alike.  -1: no such kernel.
 constexpr int kXldsThreads = 256;
 constexpr int kNumXldsStripes = 3;
 constexpr int xlds_stripe_index(int op, int chunks) {
-  return chunks == 8 ? 0 : (op != 0 && chunks == 12) ? 1 : (op != 0 && chunks == 16) ? 2 : -1;
+  return chunks == 8 ? 0 : chunks == 12 ? 1 : chunks == 16 ? 2 : -1;
 }
 
 // Enqueue the statistics kernel (op: LayerNorm 0, RMSNorm 1, softmax 2, row

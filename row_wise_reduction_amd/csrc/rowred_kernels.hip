@@ -199,29 +199,47 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
 #pragma unroll
     for (int i = 4; i < 4 * C; ++i) mx[i & 3] = fmaxf(mx[i & 3], s[i]);
     float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
-    auto exp_stripe = [&]() {
+    if (!RELOAD && (a.policy & kPolicyOnline)) {
+      // One collective (ROWRED_POLICY_ONLINE): this lane's exp(x - m) and
+      // their sum, (max, sum) merged over the row, then each value scaled by
+      // exp(m - M) / S.  A lane holding nothing but -inf (or no element of
+      // the row) sums exp(-inf - 0) = 0s.
+      const float ms = m == -__builtin_inff() ? 0.0f : m;
 #pragma unroll
-      for (int i = 0; i < 4 * C; ++i) s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);  // exp(x - m); -inf -> 0
-    };
-    if constexpr (RELOAD) {
-      reload();
-      fill_stripe();
-    }
-    exp_stripe();
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4 * C; ++i) s[i] = __builtin_amdgcn_exp2f((s[i] - ms) * kLog2e);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4 * C; ++i) acc[i & 3] += s[i];
-    float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
-    const float inv = __builtin_amdgcn_rcpf(sum);
-    if constexpr (RELOAD) {
-      reload();
-      fill_stripe();
+      for (int i = 0; i < 4 * C; ++i) acc[i & 3] += s[i];
+      float M = m, S = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      row_allreduce_online(M, S, lanes_log2, partials[0], partials[1]);
+      const float f = __builtin_amdgcn_exp2f((m - M) * kLog2e) * __builtin_amdgcn_rcpf(S);
+#pragma unroll
+      for (int i = 0; i < 4 * C; ++i) s[i] *= f;
+    } else {
+      m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+      auto exp_stripe = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4 * C; ++i) s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);  // exp(x - m); -inf -> 0
+      };
+      if constexpr (RELOAD) {
+        reload();
+        fill_stripe();
+      }
       exp_stripe();
-    }
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4 * C; ++i) s[i] *= inv;
+      for (int i = 0; i < 4 * C; ++i) acc[i & 3] += s[i];
+      float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
+      const float inv = __builtin_amdgcn_rcpf(sum);
+      if constexpr (RELOAD) {
+        reload();
+        fill_stripe();
+        exp_stripe();
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * C; ++i) s[i] *= inv;
+    }
   } else {  // LayerNorm
     // The centred values d = (x + r) - mean must be correct to FP32 rounding
     // even when a row's spread is far below its magnitude (a large common
@@ -570,7 +588,9 @@ int launch_rows(int op, int chunks, int64_t grid, int threads, const RowArgs &ar
   if (!fn) return (int)hipErrorInvalidValue;
   RowArgs a = args;
   void *params[] = {&a};
-  const size_t lds = (a.policy & kPolicyStageStores) ? stage_lds_bytes(chunks, threads) : 0;
+  size_t lds = (a.policy & kPolicyStageStores) ? stage_lds_bytes(chunks, threads) : 0;
+  const int cap = ROWRED_POLICY_CU_GROUPS_OF(a.policy);
+  if (cap >= 1 && cap <= 14 && cu_groups_lds_bytes(cap) > lds) lds = cu_groups_lds_bytes(cap);
   return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)grid), dim3(threads), params, lds,
                               stream);
 }

@@ -958,7 +958,7 @@ const SegFn kExchange[3][kNumExchangeChunks] = {
 // [op][stripe: 0 = 4 + 4 slots, 1 = 8 + 4, 2 = 8 + 8] (registers + LDS);
 // LayerNorm at 4 + 4 only (its x and r both take the slots).
 const SegFn kXlds[3][kNumXldsStripes] = {
-    {seg_xlds_kernel<kOpLayerNorm, 4, 4>, nullptr, nullptr},
+    {seg_xlds_kernel<kOpLayerNorm, 4, 4>, seg_xlds_kernel<kOpLayerNorm, 8, 4>, seg_xlds_kernel<kOpLayerNorm, 8, 8>},
     {seg_xlds_kernel<kOpRms, 4, 4>, seg_xlds_kernel<kOpRms, 8, 4>, seg_xlds_kernel<kOpRms, 8, 8>},
     {seg_xlds_kernel<kOpSoftmax, 4, 4>, seg_xlds_kernel<kOpSoftmax, 8, 4>, seg_xlds_kernel<kOpSoftmax, 8, 8>},
 };

@@ -79,8 +79,7 @@ __global__ void __launch_bounds__(kWideLanes) wide_kernel(RowArgs a) {
     for (int j = 0; j < 4; ++j) s[4 * c + j] = valid(c, j) ? xv[c][j] : identity<OP>();
   auto lds_value = [&](const f32x4 &v, int c, int j) -> float { return valid(CR + c, j) ? v[j] : identity<OP>(); };
 
-  float scale;  // RMSNorm: 1/rms; softmax: 1/sum
-  float m = 0.0f;
+  float scale;  // RMSNorm: 1/rms; softmax: 1/sum (ROWRED_POLICY_ONLINE: exp(m - M)/sum)
   if constexpr (OP == kOpRms) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -107,31 +106,50 @@ __global__ void __launch_bounds__(kWideLanes) wide_kernel(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], lds_value(v, c, j));
     }
-    m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
+    float m = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    // ROWRED_POLICY_ONLINE: exponentials against this lane's own max (0
+    // for a lane with nothing but -inf), one (max, sum) collective, and the
+    // lane's factor exp(m - M) / S folded into scale; as in the register
+    // kernels, in the same order.
+    const bool online = (a.policy & kPolicyOnline) != 0;
+    const float m_lane = m;
+    if (online) m = m == -__builtin_inff() ? 0.0f : m;
+    else m = row_allreduce<MaxOp>(m, lanes_log2, partials[0]);
 #pragma unroll
     for (int i = 0; i < 4 * CR; ++i) s[i] = __builtin_amdgcn_exp2f((s[i] - m) * kLog2e);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4 * CR; ++i) acc[i & 3] += s[i];
+    // The LDS slots' exponentials replace their x in LDS (each lane its
+    // own entries), so the output pass only scales them.
 #pragma unroll
     for (int c = 0; c < CL; ++c) {
       const f32x4 v = lds_slot(c);
+      f32x4 e;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += __builtin_amdgcn_exp2f((lds_value(v, c, j) - m) * kLog2e);
+      for (int j = 0; j < 4; ++j) {
+        e[j] = __builtin_amdgcn_exp2f((lds_value(v, c, j) - m) * kLog2e);
+        acc[j] += e[j];
+      }
+      held[c * L + li] = e;
     }
     float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
-    scale = __builtin_amdgcn_rcpf(sum);
+    if (online) {
+      float M = m_lane;
+      row_allreduce_online(M, sum, lanes_log2, partials[0], partials[1]);
+      scale = __builtin_amdgcn_exp2f((m_lane - M) * kLog2e) * __builtin_amdgcn_rcpf(sum);
+    } else {
+      sum = row_allreduce<SumOp>(sum, lanes_log2, partials[1]);
+      scale = __builtin_amdgcn_rcpf(sum);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4 * CR; ++i) s[i] *= scale;
 
   // ---- store: register slots, then the LDS slots mapped on the way out.
   auto out_value = [&](const f32x4 &v, int c, int j) -> float {
-    const float t = lds_value(v, c, j);
-    if constexpr (OP == kOpRms) return t * scale;
-    else return __builtin_amdgcn_exp2f((t - m) * kLog2e) * scale;
+    if constexpr (OP == kOpRms) return lds_value(v, c, j) * scale;
+    else return v[j] * scale;  // softmax: the slot holds exp(x - m) by now
   };
   auto store_all = [&](auto nt) {
     constexpr bool NT = decltype(nt)::value;

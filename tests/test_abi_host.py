@@ -94,12 +94,17 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
         assert L * p.chunks >= p.window
         # stripe within the private budget: <= 64 floats per lane
         assert 4 * p.chunks <= 64
-        lds = R.ROWRED_POLICY_LDS_STRIPE
-        assert 0 <= p.policy & ~lds < 16 and p.reserved == 0
-        if p.policy & lds:  # RMSNorm / softmax, 1024 lanes, 5-8 slots up to 2048 x 8192 granules, 9-16 slots
+        lds, on = R.ROWRED_POLICY_LDS_STRIPE, R.ROWRED_POLICY_ONLINE
+        cap = (p.policy >> R.ROWRED_POLICY_CU_GROUPS_SHIFT) & 15
+        assert 0 <= p.policy & ~(lds | on | R.ROWRED_POLICY_CU_GROUPS(15)) < 16 and p.reserved == 0
+        if p.policy & lds:  # RMSNorm / softmax, 1024 lanes, 5-8 slots (RMSNorm up to 2048 x 8192 granules), 9-16 slots
             assert op in ("rmsnorm", "softmax") and L == T == 1024 and 5 <= p.chunks <= 16
-            assert p.chunks > 8 or rows * p.window <= 2048 * 8192
+            assert p.chunks > 8 or op == "softmax" or rows * p.window <= 2048 * 8192
             assert not p.policy & R.ROWRED_POLICY_STAGE_STORES
+        if p.policy & on:  # softmax only, across 1024 lanes
+            assert op == "softmax" and L == 1024
+        if cap:  # large calls on 16-byte aligned rows only, even caps
+            assert mis == 0 and width % 4 == 0 and rows * width * 4 > 64 << 20 and cap in (2, 6, 10)
 
 
 def test_plan_for_workload_shapes():
@@ -109,13 +114,17 @@ def test_plan_for_workload_shapes():
     # short ragged rows: flat plans (256 lanes x 4 granules for softmax;
     # lanes_per_row is the lanes that fold one row)
     fl = R.ROWRED_POLICY_FLAT
+    lds, on = R.ROWRED_POLICY_LDS_STRIPE, R.ROWRED_POLICY_ONLINE
     cases = {(131072, 127): (8, 4, fl | nl | ns), (131072, 257): (16, 4, fl | nl | ns),
              (131072, 1537): (256, 2, nl | ns), (1024, 4096): (128, 8, nl | ns), (64, 4096): (256, 4, nl | ns),
-             (16384, 8192): (1024, 2, nl | ns | rm), (8192, 32768): (1024, 8, nl | ns | rm),
-             (17, 257): (64, 2, nl), (7, 1537): (256, 2, nl), (512, 32768): (1024, 8, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
-             (2048, 32768): (1024, 8, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE),
-             (1024, 50257): (1024, 13, nl | ns | R.ROWRED_POLICY_LDS_STRIPE),
-             (4096, 65536): (1024, 16, nl | ns | rm | R.ROWRED_POLICY_LDS_STRIPE)}
+             (16384, 8192): (256, 8, nl | ns | rm | R.ROWRED_POLICY_CU_GROUPS(2)),
+             (8192, 32768): (1024, 8, nl | ns | rm | lds | on),
+             (17, 257): (64, 2, nl), (7, 1537): (256, 2, nl), (512, 32768): (1024, 8, nl | ns | lds | on),
+             (2048, 32768): (1024, 8, nl | ns | rm | lds | on),
+             (1024, 50257): (1024, 13, nl | ns | lds | on),
+             (4096, 65536): (1024, 16, nl | ns | rm | lds | on),
+             (131072, 1024): (128, 2, nl | ns | rm | R.ROWRED_POLICY_CU_GROUPS(6)),
+             (8192, 16384): (1024, 4, nl | ns | rm | on)}
     for (rows, width), (L, C, pol) in cases.items():
         p = R.rowred_plan_query("softmax", X, None, Y, rows=rows, width=width)
         assert (p.lanes_per_row, p.chunks, p.policy) == (L, C, pol), (rows, width, p)
@@ -137,8 +146,9 @@ def test_plan_memory_policy():
     assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2049).policy == nl | ns
     # shared lines but y at another phase (no staging), > 2 slots per lane: cached stores
     assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=16384, width=127).policy == nl
-    # large aligned matrix: streaming + remap
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=4096).policy == nl | ns | rm
+    # large aligned matrix: streaming + remap, at most 2 workgroups per CU
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=4096).policy == \
+        nl | ns | rm | R.ROWRED_POLICY_CU_GROUPS(2)
 
 
 def test_plan_for_latency_bound_calls():
@@ -493,15 +503,18 @@ def test_workspace_size_covers_every_alignment(op, rows, width):
         assert p.threads in (64, 128, 256, 512, 1024)
         if p.policy & R.ROWRED_POLICY_EXCHANGE:
             # LayerNorm, RMSNorm and softmax rows of at most 64 segments
-            assert op in ("layernorm_residual", "rmsnorm", "softmax") and p.segments <= 64
+            # (LayerNorm's 8 + 8 LDS-stripe segments: 128)
+            assert op in ("layernorm_residual", "rmsnorm", "softmax")
+            assert p.segments <= (128 if op == "layernorm_residual" and p.chunks == 16 else 64)
             if p.policy & R.ROWRED_POLICY_LDS_STRIPE:
-                assert p.threads == 256 and p.chunks in ((8,) if op == "layernorm_residual" else (8, 12, 16))
+                assert p.threads == 256 and p.chunks in ((8, 16) if op == "layernorm_residual" else (8, 12, 16))
             else:
                 assert p.chunks in ((1, 2, 4) if op == "layernorm_residual" else (1, 2, 4, 8))
         else:
             assert p.chunks in (1, 2, 4)
             if op in ("layernorm_residual", "rmsnorm", "softmax"):
-                assert p.window > 64 * 4096  # no exchange geometry fits
+                # no exchange geometry fits
+                assert p.window > (128 if op == "layernorm_residual" else 64) * 4096
         # the chooser never cuts a row into segments wider than the row, unless
         # the smallest one already is
         assert G <= max(p.window + 3, 64)
@@ -546,17 +559,17 @@ def test_exchange_plan_rejects(op, width, kw):
 
 
 def test_lds_stripe_split_plans():
-    """LDS-stripe exchange plans: 256 threads, 8 slots (4 + 4) for every
-    matrix operator, 12 and 16 (8 + 4, 8 + 8) for RMSNorm and softmax; only
-    with EXCHANGE."""
+    """LDS-stripe exchange plans: 256 threads, 8, 12 or 16 slots (4 + 4,
+    8 + 4, 8 + 8) for every matrix operator; only with EXCHANGE."""
     E, L = R.ROWRED_POLICY_EXCHANGE, R.ROWRED_POLICY_LDS_STRIPE
-    for op, chunks in (("layernorm_residual", 8), ("rmsnorm", 8), ("rmsnorm", 12), ("softmax", 16)):
+    for op, chunks in (("layernorm_residual", 8), ("layernorm_residual", 12), ("layernorm_residual", 16),
+                       ("rmsnorm", 8), ("rmsnorm", 12), ("softmax", 16)):
         p = R.rowred_split_plan_query(op, X, 8, 100000, plan=R.SplitPlan(threads=256, chunks=chunks, policy=E | L))
         assert p.segments == -(-p.window // (256 * chunks))
     for op, kw in (("softmax", dict(threads=256, chunks=8, policy=L)),          # without EXCHANGE
                    ("softmax", dict(threads=512, chunks=8, policy=E | L)),      # 256 threads only
                    ("softmax", dict(threads=256, chunks=4, policy=E | L)),
-                   ("layernorm_residual", dict(threads=256, chunks=12, policy=E | L)),
+                   ("layernorm_residual", dict(threads=256, chunks=10, policy=E | L)),
                    ("row_sum", dict(threads=256, chunks=8, policy=E | L))):
         with pytest.raises(R.RowRedError) as e:
             R.rowred_split_plan_query(op, X, 8, 100000, plan=R.SplitPlan(**kw))
@@ -582,9 +595,13 @@ def test_exchange_plan_limits(op, T, C):
 @pytest.mark.parametrize("op,rows,width,want", [
     ("softmax", 4096, 1 << 16, (256, 8, 8, 0)), ("rmsnorm", 2048, 1 << 17, (256, 8, 16, 0)),
     ("layernorm_residual", 1024, 1 << 16, (256, 8, 8, 1)), ("layernorm_residual", 256, 1 << 18, (256, 8, 32, 1)),
-    ("rmsnorm", 1024, 1 << 18, (256, 8, 32, 0)), ("rmsnorm", 64, 1 << 19, (256, 8, 64, 0)),
+    # RMSNorm / softmax beyond 16 segments of 256 x 8: 8 + 8 LDS-stripe segments
+    ("rmsnorm", 1024, 1 << 18, (256, 16, 16, 1)), ("rmsnorm", 64, 1 << 19, (256, 16, 32, 1)),
     ("rmsnorm", 64, 600000, (256, 16, 37, 1)), ("softmax", 64, 1 << 20, (256, 16, 64, 1)),
-    ("layernorm_residual", 16, 1 << 20, (1024, 4, 64, 0)), ("softmax", 7, 1537, (64, 2, 4, 0)),
+    ("softmax", 512, 1 << 17, (256, 8, 16, 0)),
+    # LayerNorm beyond 32 segments of 4 + 4: 8 + 8 up to 128 segments
+    ("layernorm_residual", 16, 1 << 20, (256, 16, 64, 1)), ("layernorm_residual", 16, 1 << 21, (256, 16, 128, 1)),
+    ("layernorm_residual", 64, 1 << 18, (256, 8, 32, 1)), ("softmax", 7, 1537, (64, 2, 4, 0)),
     # no more (row, segment) workgroups than CUs: the segment is halved
     ("softmax", 16, 32768, (256, 4, 8, 0)), ("layernorm_residual", 8, 1 << 16, (256, 4, 16, 0)),
     ("softmax", 32, 1 << 16, (256, 4, 16, 0)), ("softmax", 33, 1 << 16, (256, 8, 8, 0)),
@@ -795,3 +812,72 @@ def test_split_plan_rejects_bad_wait_fields(kw):
                                                                                policy=R.ROWRED_POLICY_EXCHANGE,
                                                                                wait_polls=5))
     assert ok.wait_polls == 5 and ok.segments == 13
+
+
+def test_online_policy_preconditions():
+    """ROWRED_POLICY_ONLINE: softmax only, on the register kernels (not
+    RELOAD) or LDS_STRIPE at 5-16 chunks; not with LOOPED or FLAT plans."""
+    on = R.ROWRED_POLICY_ONLINE
+    lds, lp, fl = R.ROWRED_POLICY_LDS_STRIPE, R.ROWRED_POLICY_LOOPED, R.ROWRED_POLICY_FLAT
+    lib = R.lib()
+
+    def st(op, plan, width, rows=8):  # the plan is checked before any device call
+        return lib.rowred_run_plan(op, X, None, Y, rows, width, f(0), ctypes.byref(plan._c()), None)
+
+    # accepted plans get past the checks (here the launch then fails: no GPU)
+    for plan, width in ((bad_plan(lanes_per_row=256, policy=on | 3), 4096),
+                        (bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=on | lds), 32768),
+                        (bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=on | lds), 65536),
+                        (bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=on | 7), 32768),
+                        (bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=on | 11), 127)):
+        assert st(2, plan, width) != R.ROWRED_ERR_INVALID_ARG, plan
+    for plan in (bad_plan(policy=on), bad_plan(lanes_per_row=256, policy=on | 3)):
+        assert st(2, plan, 4096, rows=0) == R.ROWRED_OK  # zero rows: nothing to check or launch
+    for op, plan, width in ((1, bad_plan(lanes_per_row=256, policy=on), 4096),  # RMSNorm
+                            (0, bad_plan(lanes_per_row=256, policy=on), 4096),  # LayerNorm
+                            (2, bad_plan(lanes_per_row=256, policy=on | R.ROWRED_POLICY_RELOAD), 4096),
+                            (1, bad_plan(lanes_per_row=1024, chunks=8, threads=1024, policy=on | lds), 32768),
+                            (2, bad_plan(lanes_per_row=1024, chunks=4, threads=1024, policy=on | lp), 65536),
+                            (2, bad_plan(lanes_per_row=1024, chunks=16, threads=1024, policy=on | lp | lds), 131072),
+                            (2, bad_plan(lanes_per_row=0, chunks=4, threads=256, policy=on | fl), 127)):
+        assert st(op, plan, width) == R.ROWRED_ERR_INVALID_ARG, (op, plan)
+    # not for the scalar-output reductions
+    c = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=on)._c()
+    assert lib.rowred_row_reduce_run_plan(3, X, 0x7F4000000000, None, 8, 127, ctypes.byref(c), None) == \
+        R.ROWRED_ERR_INVALID_ARG
+
+
+def test_cu_groups_field():
+    """Bits 12-15 of a row plan's policy: a cap of 1-14 workgroups per CU on
+    the register kernels; 15 rejected, as is a cap on FLAT, LOOPED or
+    LDS_STRIPE plans."""
+    lib = R.lib()
+    cap = R.ROWRED_POLICY_CU_GROUPS
+    assert cap(5) == 5 << 12
+
+    def st(op, plan, width, rows=8):
+        return lib.rowred_run_plan(op, X, None, Y, rows, width, f(1e-6), ctypes.byref(plan._c()), None)
+
+    for n in range(1, 15):
+        for pol in (3, 3 | R.ROWRED_POLICY_STAGE_STORES):
+            assert st(1, bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=pol | cap(n)), 250) != \
+                R.ROWRED_ERR_INVALID_ARG, n
+    assert st(1, bad_plan(lanes_per_row=256, policy=3 | cap(15)), 4096) == R.ROWRED_ERR_INVALID_ARG
+    for plan, width in ((bad_plan(lanes_per_row=1024, chunks=8, threads=1024,
+                                  policy=R.ROWRED_POLICY_LDS_STRIPE | cap(2)), 32768),
+                        (bad_plan(lanes_per_row=1024, chunks=4, threads=1024, policy=R.ROWRED_POLICY_LOOPED | cap(4)),
+                         65536),
+                        (bad_plan(lanes_per_row=0, chunks=4, threads=256, policy=R.ROWRED_POLICY_FLAT | cap(4)), 127)):
+        assert st(1, plan, width) == R.ROWRED_ERR_INVALID_ARG, plan
+
+
+def test_binding_constants_match_header():
+    """Every ROWRED_POLICY_* / ROWRED_OP_* / ROWRED_ERR_* value the header
+    defines has the same value in the binding."""
+    import re
+    text = open(HEADER).read()
+    pairs = re.findall(r"\b(ROWRED_(?:POLICY|OP|ERR)_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)
+    pairs += re.findall(r"#define\s+(ROWRED_POLICY_CU_GROUPS_SHIFT)\s+(\d+)", text)
+    assert len(pairs) >= 20
+    for name, value in pairs:
+        assert getattr(R, name) == int(value), name

@@ -89,12 +89,6 @@ def test_lds_stripe_exchange(op, chunks):
     """Exchange kernels with part of each segment in LDS: one, three and 128
     segments per row, ragged, misaligned (r and y at another 16-byte phase
     than x too), both memory policies."""
-    if op.startswith("layernorm") and chunks != 8:
-        # LayerNorm keeps 4 + 4 slots: other stripes are refused before
-        # anything runs
-        x, r, g, b = make_inputs(op, 2, 40000, seed=6)
-        assert_refused(op, x, r, g, b, R.SplitPlan(threads=256, chunks=chunks, policy=EXCHANGE | LDS))
-        return
     G = 256 * chunks
     for width, shift in ((1000, 1), (4 * G * 3 - 7, 3), (4 * G * 128 - 9, 2)):
         rows = max(2, min(6, (1 << 21) // width))
@@ -106,16 +100,17 @@ def test_lds_stripe_exchange(op, chunks):
             check(op, run_exchange(op, x, r, g, b, plan, shift=shift), ref, f"{op} {width} {plan}")
 
 
-def test_lds_stripe_misaligned_residual():
+@pytest.mark.parametrize("chunks", LDS_STRIPES, ids=lambda c: f"C{c}")
+def test_lds_stripe_misaligned_residual(chunks):
     """LayerNorm with r at another 16-byte phase than x: the LDS slots of r are
     filled by 4-byte loads."""
     t = torch()
-    rows, width = 5, 40003
-    x, r, g, b = make_inputs("layernorm_residual", rows, width, seed=77)
+    rows, width = 5, 40003 + 20000 * (chunks // 8 - 1)
+    x, r, g, b = make_inputs("layernorm_residual", rows, width, seed=77 + chunks)
     ref = reference("layernorm_residual", x, r, None, None)
     xd, rd = shifted_input(x, 1), shifted_input(r, 3)
     out = t.empty(rows, width, device="cuda")
-    plan = R.SplitPlan(threads=256, chunks=8, policy=EXCHANGE | LDS | STREAM)
+    plan = R.SplitPlan(threads=256, chunks=chunks, policy=EXCHANGE | LDS | STREAM)
     ws = workspace("layernorm_residual", rows, width, plan, xd)
     R.rowred_split_run_plan("layernorm_residual", xd, rd, None, None, out, None, plan, ws, eps=1e-5)
     t.cuda.synchronize()
@@ -139,7 +134,7 @@ def test_special_values(op):
     ref = reference(op, x, None, None, None)
     # 128-granule segments (10 per row), and 8 + 8 LDS-stripe ones (2 per row)
     for plan in (R.SplitPlan(threads=64, chunks=2, policy=EXCHANGE),
-                 R.SplitPlan(threads=256, chunks=8 if op == "layernorm" else 16, policy=EXCHANGE | LDS)):
+                 R.SplitPlan(threads=256, chunks=16, policy=EXCHANGE | LDS)):
         got = run_exchange(op, x, None, None, None, plan)
         check(op, got, ref, f"{op} special {plan}")
     if op == "softmax":

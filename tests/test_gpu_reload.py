@@ -57,14 +57,18 @@ def test_reload_matches_resident_bitwise(op, width):
 
 @pytest.mark.parametrize("case", [synthetic.CORE_WORKLOADS[4][0], synthetic.CORE_WORKLOADS[5][0]], ids=lambda c: c.name)
 def test_reload_full_size(case):
-    """The chooser's plan with the reload bit at a full workload shape:
-    bitwise the resident result."""
+    """The chooser's geometry with the reload bit at a full workload shape:
+    bitwise the resident result (the register kernel of that geometry, with
+    two softmax collectives: the reload kernels have no LDS-stripe or
+    one-collective form)."""
     print_case(case.name)
     x = synthetic.case_input(case, "x")
     r = synthetic.case_input(case, "r") if case.op == "layernorm_residual" else None
     xd = shifted_input(x, 0)
     rd = shifted_input(r, 0) if r is not None else None
-    p = R.rowred_plan_query(case.op, xd, rd, Guarded(case.rows, case.width, 0).y)
+    q = R.rowred_plan_query(case.op, xd, rd, Guarded(case.rows, case.width, 0).y)
+    p = R.Plan(q.lanes_per_row, 0, q.chunks, q.threads, 0,
+               policy=q.policy & ~(R.ROWRED_POLICY_LDS_STRIPE | R.ROWRED_POLICY_ONLINE))
     y0 = run(case.op, xd, rd, p, case.rows, case.width, 0)
     pr = R.Plan(p.lanes_per_row, 0, p.chunks, p.threads, 0, policy=p.policy | R.ROWRED_POLICY_RELOAD)
     y1 = run(case.op, xd, rd, pr, case.rows, case.width, 0)
