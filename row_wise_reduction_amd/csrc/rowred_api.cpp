@@ -438,6 +438,24 @@ void choose_plan(const Call &c, rowred_plan *p) {
     p->reserved = 0;
     return;
   }
+  // RMSNorm and softmax rows off 16-byte boundaries of 513-3072 granules
+  // beyond 64 MiB: three slots per lane in one row per workgroup (L the
+  // smallest power of two >= a third of the window, at least 256), at most 6
+  // workgroups per CU at 256 lanes.  MI355X, against the rules below: RMSNorm
+  // 65536x2047, 32768x4095, 16384x8191: 190.6 -> 173.8, 199.7 -> 174.5,
+  // 180.1 -> 178.5 us; softmax 224.9 -> 173.7, 280.1 -> 177.4, 195.2 -> 180.8
+  // us (the rules below leave up to half of each lane's slots past the row).
+  if ((c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && !rows_aligned && in_bytes > (int64_t(64) << 20) &&
+      w > 512 && w <= 3072) {
+    int64_t L = 256;
+    while (3 * L < w) L *= 2;
+    p->lanes_per_row = (int32_t)L;
+    p->chunks = (int32_t)((w + L - 1) / L);
+    p->threads = (int32_t)L;
+    p->policy = kPolicyNtLoads | kPolicyNtStores | (L == 256 ? ROWRED_POLICY_CU_GROUPS(6) : 0);
+    p->reserved = 0;
+    return;
+  }
   // Outputs are staged only for rows of at most 256 granules, where a
   // workgroup holds many rows whose boundary lines it shares: at 127-769
   // columns staging is 1-40% faster at 65536-262144 rows; from 1537 columns
@@ -461,10 +479,13 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // lane, 8 for rows of 1024-2048 granules beyond 32 MiB: 8-19% faster than
   // the rules above at 16384x8192, 32768x4096, 65536x2048, 131072x1024 and
   // 1024x4096, within 2% at 262144x512 (sweep of every geometry on MI355X).
-  // Wider rows keep the rules above (16384 columns: 1024 x 4 best).
+  // Wider rows keep the rules above (16384 columns: 1024 x 4 best).  Beyond
+  // 32 MiB, rows of at most 256 granules take 2 slots (131072x1024 175.5 ->
+  // 168.8 us) and 8-slot stripes at most 4 workgroups per CU (16384x8192
+  // 182.3 -> 179.0 us).
   bool affine_256 = false;
   if (affine && rows_aligned && w <= 2048) {
-    max_chunks = !small && w >= 1024 ? 8 : 4;
+    max_chunks = !small && w >= 1024 ? 8 : !small && w <= 256 ? 2 : 4;
     affine_256 = true;
   }
   // Row sum and min/max on rows of 33-160 granules: of 4 and 5 slots per
@@ -492,9 +513,18 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // beta on 16-byte boundaries read 16 bytes at a time and shifted into the
   // row's phase: 285 and 256 us; 16384x8191 283.6 us); 16383 columns keep
   // 1024 x 5.
+  // Affine rows of at most 2560 granules whose gamma and beta sit on 16-byte
+  // boundaries (read 16 bytes at a time and shifted into the row's phase)
+  // take 5 slots per lane: 131072x1023 335 -> 245 us, 65536x2047 333 -> 255
+  // us (32768x4095 and 16384x8191 already 5).
   const bool ln_ragged =
       (kop == ROWRED_OP_LAYERNORM_RESIDUAL || affine) && !rows_aligned && !small && w > 256;
-  if (ln_ragged) {
+  const bool affine_shift = affine && ((uintptr_t)c.gamma & 15) == 0 && ((uintptr_t)c.beta & 15) == 0;
+  if (ln_ragged && affine_shift && w <= 2560) {
+    L = 1;
+    while (5 * L < w) L *= 2;
+    if (L > 1024) L = 1024;
+  } else if (ln_ragged) {
     L = lanes_for(w <= 1024 ? 4 : 5);
     if (w > 384 && w <= 512) L = 256;  // 2 slots: 1537 columns 1-6% faster than 128 x 4
     if (L > 512 && (w + 511) / 512 <= 8) L = 512;
@@ -539,9 +569,12 @@ void choose_plan(const Call &c, rowred_plan *p) {
     policy |= kPolicyLdsStripe;
   // Softmax across a 1024-lane row beyond 64 MiB: one (max, sum) collective
   // instead of two (8192x16384 177.4 -> 174.9 us; 2048x32768 97.7 -> 94.1 us
-  // with the LDS stripe).
-  if (c.op == ROWRED_OP_SOFTMAX && L == 1024 && ((policy & kPolicyLdsStripe) || in_bytes > (int64_t(64) << 20)))
+  // with the LDS stripe) -- on 16-byte aligned rows: rows off the boundaries
+  // in registers measured slower with it (32768x4095 in 1024 x 2: 234 -> 280 us).
+  if (c.op == ROWRED_OP_SOFTMAX && L == 1024 &&
+      ((policy & kPolicyLdsStripe) || (rows_aligned && in_bytes > (int64_t(64) << 20))))
     policy |= kPolicyOnline;
+  if (affine_256 && !small && max_chunks == 8) policy |= ROWRED_POLICY_CU_GROUPS(4);
   p->policy = policy;
   p->reserved = 0;
 }

@@ -103,8 +103,9 @@ def test_plan_covers_rows_and_respects_limits(op, width, mis):
             assert not p.policy & R.ROWRED_POLICY_STAGE_STORES
         if p.policy & on:  # softmax only, across 1024 lanes
             assert op == "softmax" and L == 1024
-        if cap:  # large calls on 16-byte aligned rows only, even caps
-            assert mis == 0 and width % 4 == 0 and rows * width * 4 > 64 << 20 and cap in (2, 6, 10)
+        if cap:  # large calls only, even caps; off 16-byte boundaries RMSNorm / softmax at 256 lanes
+            assert rows * width * 4 > 64 << 20 and cap in (2, 6, 10)
+            assert (mis == 0 and width % 4 == 0) or (op != "layernorm_residual" and L == T == 256 and cap == 6)
 
 
 def test_plan_for_workload_shapes():
@@ -143,7 +144,12 @@ def test_plan_memory_policy():
     assert R.rowred_plan_query("layernorm_residual", X, RR, Y, rows=16384, width=127).policy == ns | st
     # longer ragged rows (> 256 granules): unstaged, streaming
     assert R.rowred_plan_query("rmsnorm", X + 4, None, Y + 4, rows=64, width=4096).policy == nl | ns
-    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2049).policy == nl | ns
+    assert R.rowred_plan_query("rmsnorm", X, None, Y, rows=2048, width=2049).policy == nl | ns
+    # beyond 64 MiB: three slots per lane, at most 6 workgroups per CU at 256 lanes
+    p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2049)
+    assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (256, 3, 256, nl | ns | R.ROWRED_POLICY_CU_GROUPS(6))
+    p = R.rowred_plan_query("softmax", X, None, Y, rows=32768, width=4095)
+    assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (512, 3, 512, nl | ns)
     # shared lines but y at another phase (no staging), > 2 slots per lane: cached stores
     assert R.rowred_plan_query("rmsnorm", X, None, Y + 4, rows=16384, width=127).policy == nl
     # large aligned matrix: streaming + remap, at most 2 workgroups per CU
@@ -697,24 +703,33 @@ def test_looped_layernorm_needs_two_chunks():
 
 @pytest.mark.parametrize("rows,width,want", [
     ((16384, 8192, (256, 8, 256))), ((32768, 4096, (128, 8, 256))), ((65536, 2048, (128, 4, 256))),
-    ((131072, 1024, (64, 4, 256))), ((1024, 4096, (256, 4, 256))), ((512, 8192, (512, 4, 512))),
+    ((131072, 1024, (128, 2, 256))), ((1024, 4096, (256, 4, 256))), ((512, 8192, (512, 4, 512))),
     ((8192, 16384, (1024, 4, 1024))),
 ])
 def test_layernorm_plan_query_affine(rows, width, want):
     """Affine LayerNorm's own geometry rule (256-thread workgroups, 4 slots,
-    8 for rows of 1024-2048 granules beyond 32 MiB) on aligned rows; plain
-    LayerNorm keeps the general rules; misaligned affine rows take plain
-    LayerNorm's geometry (without its XCD remap)."""
+    8 for rows of 1024-2048 granules beyond 32 MiB, 2 for rows of at most 256)
+    on aligned rows; plain LayerNorm keeps the general rules; misaligned affine
+    rows take 5 slots per lane beyond 32 MiB when gamma and beta sit on 16-byte
+    boundaries, else plain LayerNorm's geometry (without its XCD remap)."""
     G, B = 0x7F4000000000, 0x7F5000000000
     p = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows=rows, width=width)
     assert (p.lanes_per_row, p.chunks, p.threads) == want
     assert p.lanes_per_row * p.chunks >= p.window
     q = R.rowred_layernorm_plan_query(X, None, None, None, Y, rows=rows, width=width)
     assert q == R.rowred_plan_query("layernorm_residual", X, None, Y, rows=rows, width=width)
-    m = R.rowred_layernorm_plan_query(X + 4, None, G, B, Y + 4, rows=rows, width=width - 1)
     n = R.rowred_layernorm_plan_query(X + 4, None, None, None, Y + 4, rows=rows, width=width - 1)
+    m = R.rowred_layernorm_plan_query(X + 4, None, G + 4, B + 4, Y + 4, rows=rows, width=width - 1)
     assert (m.lanes_per_row, m.chunks, m.threads) == (n.lanes_per_row, n.chunks, n.threads)
     assert m.policy == n.policy & ~R.ROWRED_POLICY_XCD_REMAP
+    s = R.rowred_layernorm_plan_query(X + 4, None, G, B, Y + 4, rows=rows, width=width - 1)
+    if rows * width * 4 > 32 << 20:
+        L = 1
+        while 5 * L < s.window:
+            L *= 2
+        assert (s.lanes_per_row, s.chunks, s.threads) == (min(L, 1024), -(-s.window // min(L, 1024)), max(256, L))
+    else:
+        assert (s.lanes_per_row, s.chunks, s.threads) == (n.lanes_per_row, n.chunks, n.threads)
 
 
 def test_layernorm_plan_query_errors():
@@ -764,19 +779,27 @@ def test_ragged_layernorm_rule():
     """LayerNorm on misaligned rows of more than 256 granules beyond 32 MiB:
     4 slots (5 beyond 1024 granules, 2 at 385-512), at most 512 lanes while
     that takes at most 8 slots, one row per workgroup, XCD remap (not
-    affine).  RMSNorm keeps the general rules."""
+    affine).  Affine rows of up to 2560 granules with gamma and beta on
+    16-byte boundaries: 5 slots per lane (with them off the boundaries the
+    plain rule).  RMSNorm rows of 513-3072 granules: 3 slots."""
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
     G, B = RR + (1 << 30), RR + (1 << 31)
+    shifted = {1023: (64, 5, 256), 1537: (128, 4, 256), 2047: (128, 5, 256), 4095: (256, 5, 256),
+               8191: (512, 5, 512)}
     for width, want in ((1023, (128, 3, 256)), (1537, (256, 2, 256)), (2047, (256, 3, 256)), (4095, (256, 5, 256)),
                         (8191, (512, 5, 512)), (12287, (512, 7, 512)), (16383, (1024, 5, 1024))):
         rows = (1 << 27) // width
         for r in (None, RR):
             p = R.rowred_layernorm_plan_query(X, r, None, None, Y, rows, width)
             assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (*want, nl | ns | rm), (width, r, p)
-        a = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows, width)
+        a = R.rowred_layernorm_plan_query(X, None, G + 4, B + 4, Y, rows, width)
         assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*want, nl | ns), (width, a)
+        a = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows, width)
+        assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*shifted.get(width, want), nl | ns), (width, a)
     p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=16386, width=8191)
     assert (p.lanes_per_row, p.chunks, p.threads) == (1024, 3, 1024)
+    p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2047)
+    assert (p.lanes_per_row, p.chunks, p.threads) == (256, 3, 256)
 
 
 def undefined_symbols():
