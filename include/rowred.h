@@ -120,14 +120,12 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
  * are the affine form named in the tolerance list of "Cooperating-program
  * packing: implementation and fixed-plan evidence", section "Predeclared
  * comparison and measurement".  gamma and beta hold `width` floats each
- * (4-byte aligned, read only, must not overlap y); when 16-byte aligned
- * they are read 16 bytes at a time, as whole granules -- up to 12 bytes past
- * the last element, inside its granule -- at any alignment of the rows.
- * With all three NULL
- * this is the no-affine LayerNorm of the same page's "Validation" section.
- * With gamma or beta, rows of more than 6144 granules (24576 floats for
- * 16-byte aligned rows) take the looped kernels (gamma/beta need registers
- * the wider register-resident kernels do not have).
+ * (4-byte aligned, read only, must not overlap y), never read beyond
+ * their `width` elements.  With all three NULL this is the no-affine
+ * LayerNorm of the same page's "Validation" section.  With gamma or beta,
+ * rows of 6145-8192 granules (24577-32768 floats for 16-byte aligned rows)
+ * take the looped kernels (gamma/beta need registers the wider
+ * register-resident kernels do not have), wider rows the head+tail kernels.
  */
 int rowred_layernorm(const float *x, const float *r, const float *gamma,
                      const float *beta, float *y, int64_t rows, int64_t width,

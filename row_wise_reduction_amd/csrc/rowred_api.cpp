@@ -513,14 +513,13 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // beta on 16-byte boundaries read 16 bytes at a time and shifted into the
   // row's phase: 285 and 256 us; 16384x8191 283.6 us); 16383 columns keep
   // 1024 x 5.
-  // Affine rows of at most 2560 granules whose gamma and beta sit on 16-byte
-  // boundaries (read 16 bytes at a time and shifted into the row's phase)
-  // take 5 slots per lane: 131072x1023 335 -> 245 us, 65536x2047 333 -> 255
-  // us (32768x4095 and 16384x8191 already 5).
+  // Affine rows of at most 2560 granules (gamma and beta read 16 bytes at a
+  // time from 4-byte boundaries) take 5 slots per lane, 128-thread
+  // workgroups at 64 lanes: 131072x1023 335 -> 217 us, 65536x2047 333 -> 212
+  // us (32768x4095 and 16384x8191 already 5: 215 and 238 us).
   const bool ln_ragged =
       (kop == ROWRED_OP_LAYERNORM_RESIDUAL || affine) && !rows_aligned && !small && w > 256;
-  const bool affine_shift = affine && ((uintptr_t)c.gamma & 15) == 0 && ((uintptr_t)c.beta & 15) == 0;
-  if (ln_ragged && affine_shift && w <= 2560) {
+  if (ln_ragged && affine && w <= 2560) {
     L = 1;
     while (5 * L < w) L *= 2;
     if (L > 1024) L = 1024;
@@ -546,7 +545,9 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // Row sum and min/max take 512 threads, except calls of at most 2^19
   // elements, where 256 are 0.05-0.2 us faster (1x4096 2.41 -> 2.24 us,
   // 256x1024 2.84 -> 2.68 us).
-  const int64_t t_min = (small && !scalar_out) || affine_256 || (scalar_out && tiny) || ln_ragged ? 256 : 512;
+  const int64_t t_min = ln_ragged && affine && L <= 64 ? 128
+                        : (small && !scalar_out) || affine_256 || (scalar_out && tiny) || ln_ragged ? 256
+                                                                                                     : 512;
   p->threads = (int32_t)(L > t_min ? L : t_min);
   const bool can_stage = stage_ok && p->chunks > 0 && p->chunks <= kMaxStageChunks && p->threads <= kMaxStageThreads;
   int policy = 0;
@@ -602,12 +603,9 @@ int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
                      ? 1
                      : 0;
   a.group_rows = plan.rows_per_group;
-  // affine rows off 16-byte boundaries with gamma / beta on them: 16-byte
-  // gamma / beta loads shifted into each row's phase (a kernel of its own)
-  a.affine_shift = (c.gamma || c.beta) && !a.affine_vec && ((uintptr_t)c.gamma & 15) == 0 &&
-                           ((uintptr_t)c.beta & 15) == 0
-                       ? 1
-                       : 0;
+  // affine rows at another 16-byte phase than gamma / beta: 16-byte gamma /
+  // beta loads from 4-byte boundaries (a kernel of its own)
+  a.affine_shift = (c.gamma || c.beta) && !a.affine_vec ? 1 : 0;
   const bool looped = (plan.policy & kPolicyLooped) != 0, lds = (plan.policy & kPolicyLdsStripe) != 0;
   const int err = (plan.policy & kPolicyFlat) ? launch_flat(kernel_op(c), plan.chunks, plan.grid, plan.threads, a, stream)
                   : looped && lds ? launch_wide_tail(kernel_op(c), plan.grid, a, stream)

@@ -26,7 +26,7 @@ struct RowArgs {
   int32_t y_vec;       // 1: y shares x's address modulo 16 (16-byte stores)
   int32_t affine_vec;  // 1: rows start on 16-byte boundaries and gamma/beta are 16-byte aligned
   int32_t group_rows;  // flat kernels: rows per workgroup (P)
-  int32_t affine_shift;  // 1: rows off 16-byte boundaries, gamma / beta 16-byte aligned (row kernels)
+  int32_t affine_shift;  // 1: gamma / beta at another 16-byte phase than the rows (row kernels)
 };
 
 constexpr int kPolicyNtLoads = ROWRED_POLICY_NT_LOADS;

@@ -48,11 +48,11 @@ namespace {
 // `threads` is blockDim.x, read in the kernel itself: there the compiler
 // knows workgroups are uniform and reads it with a scalar load.
 //
-// SHIFT (affine LayerNorm only): rows that do not start on 16-byte
-// boundaries, with gamma and beta on them.  Element e = 4k + j - off of a
-// row (k the slot's granule) is gamma[e], which lies in gamma granules k - 1
-// and k; both are read 16 bytes at a time and shifted into the row's phase,
-// instead of four 4-byte loads per vector.  A kernel of its own, so the
+// SHIFT (affine LayerNorm only): gamma / beta at another 16-byte phase than
+// the rows.  The four elements e0 = 4k - off .. e0 + 3 of a slot (k its
+// granule) are gamma[e0 .. e0 + 3]: one 16-byte load from a 4-byte boundary
+// (gfx950 serves such loads; the compiler emits them for 4-byte-aligned
+// 16-byte copies) instead of four 4-byte loads.  A kernel of its own, so the
 // other affine kernels keep their code.
 template <int OP, int C, bool RELOAD, bool SHIFT = false>
 __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
@@ -82,7 +82,6 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
   // at the window edges and in slots past the window.
   auto elem = [&](int c, int j) -> int { return 4 * (c * L + li) + j - off; };
   auto valid = [&](int c, int j) -> bool { return (unsigned)elem(c, j) < (unsigned)width; };
-  auto gran = [&](int c) -> int { return min(c * L + li, kmax); };  // slot c's granule, clamped into the row
 
   float s[4 * C];
 
@@ -309,21 +308,19 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
     constexpr bool kAffine = OP == kOpLayerNormAffine;
     constexpr bool kEarlyAffine = kAffine && C <= 4;
     f32x4 gv[kEarlyAffine ? C : 1], bv[kEarlyAffine ? C : 1];
-    // SHIFT: gamma / beta elements 4k - off .. 4k + 3 - off, from granules
-    // k - 1 (its last off floats) and k (its first 4 - off), clamped into the
-    // vector (the clamped granules only feed elements outside the row).
-    auto shifted = [&](const float *v, int k, float dflt) -> f32x4 {
+    // SHIFT: gamma / beta elements e0 = 4k - off .. e0 + 3 of slot c (k its
+    // unclamped granule): one 16-byte load at a 4-byte boundary where all
+    // four lie in the row, element by element (indices clamped into the
+    // vector) in the slots at the row's two ends and past it.
+    auto shifted = [&](const float *v, int c, float dflt) -> f32x4 {
       if (!v) return f32x4(dflt);
-      const f32x4 *vg = reinterpret_cast<const f32x4 *>(v);
-      const f32x4 lo = load_g<false>(vg + max(k - 1, 0));
-      const f32x4 hi = load_g<false>(vg + min(k, (width - 1) >> 2));
+      const int e0 = 4 * (c * L + li) - off;
       f32x4 r;
+      if (e0 >= 0 && e0 + 4 <= width) {
+        __builtin_memcpy(&r, v + e0, sizeof(r));
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {  // r[j] = (lo, hi)[4 - off + j]
-        const float s1 = j == 0 ? lo[3] : hi[j - 1];
-        const float s2 = j < 2 ? lo[2 + j] : hi[j - 2];
-        const float s3 = j < 3 ? lo[1 + j] : hi[j - 3];
-        r[j] = off == 0 ? hi[j] : off == 1 ? s1 : off == 2 ? s2 : s3;
+        for (int j = 0; j < 4; ++j) r[j] = v[max(0, min(e0 + j, width - 1))];
       }
       return r;
     };
@@ -331,8 +328,8 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
       if constexpr (kEarlyAffine && SHIFT) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          gv[c] = shifted(a.gamma, gran(c), 1.0f);
-          bv[c] = shifted(a.beta, gran(c), 0.0f);
+          gv[c] = shifted(a.gamma, c, 1.0f);
+          bv[c] = shifted(a.beta, c, 0.0f);
         }
       } else if constexpr (kEarlyAffine) {
         if (a.affine_vec) {  // rows start on 16-byte boundaries: row granule k is gamma/beta granule k
@@ -374,8 +371,8 @@ __device__ __forceinline__ void row_body(const RowArgs &a, const int threads) {
       for (int c = 0; c < C; ++c) {
         f32x4 g, b;
         if (SHIFT) {
-          g = shifted(a.gamma, gran(c), 1.0f);
-          b = shifted(a.beta, gran(c), 0.0f);
+          g = shifted(a.gamma, c, 1.0f);
+          b = shifted(a.beta, c, 0.0f);
         } else if (a.affine_vec) {
           const int k = min(c * L + li, kmax);
           g = a.gamma ? load_g<false>(reinterpret_cast<const f32x4 *>(a.gamma) + k) : f32x4(1.0f);

@@ -719,17 +719,16 @@ def test_layernorm_plan_query_affine(rows, width, want):
     q = R.rowred_layernorm_plan_query(X, None, None, None, Y, rows=rows, width=width)
     assert q == R.rowred_plan_query("layernorm_residual", X, None, Y, rows=rows, width=width)
     n = R.rowred_layernorm_plan_query(X + 4, None, None, None, Y + 4, rows=rows, width=width - 1)
-    m = R.rowred_layernorm_plan_query(X + 4, None, G + 4, B + 4, Y + 4, rows=rows, width=width - 1)
-    assert (m.lanes_per_row, m.chunks, m.threads) == (n.lanes_per_row, n.chunks, n.threads)
-    assert m.policy == n.policy & ~R.ROWRED_POLICY_XCD_REMAP
-    s = R.rowred_layernorm_plan_query(X + 4, None, G, B, Y + 4, rows=rows, width=width - 1)
-    if rows * width * 4 > 32 << 20:
-        L = 1
-        while 5 * L < s.window:
-            L *= 2
-        assert (s.lanes_per_row, s.chunks, s.threads) == (min(L, 1024), -(-s.window // min(L, 1024)), max(256, L))
-    else:
-        assert (s.lanes_per_row, s.chunks, s.threads) == (n.lanes_per_row, n.chunks, n.threads)
+    for g, b in ((G, B), (G + 4, B + 4)):
+        m = R.rowred_layernorm_plan_query(X + 4, None, g, b, Y + 4, rows=rows, width=width - 1)
+        if rows * width * 4 > 32 << 20 and m.window <= 2560:
+            L = 1
+            while 5 * L < m.window:
+                L *= 2
+            assert (m.lanes_per_row, m.chunks, m.threads) == (L, -(-m.window // L), max(128 if L <= 64 else 256, L))
+        else:
+            assert (m.lanes_per_row, m.chunks, m.threads) == (n.lanes_per_row, n.chunks, n.threads)
+        assert m.policy == n.policy & ~R.ROWRED_POLICY_XCD_REMAP
 
 
 def test_layernorm_plan_query_errors():
@@ -779,12 +778,11 @@ def test_ragged_layernorm_rule():
     """LayerNorm on misaligned rows of more than 256 granules beyond 32 MiB:
     4 slots (5 beyond 1024 granules, 2 at 385-512), at most 512 lanes while
     that takes at most 8 slots, one row per workgroup, XCD remap (not
-    affine).  Affine rows of up to 2560 granules with gamma and beta on
-    16-byte boundaries: 5 slots per lane (with them off the boundaries the
-    plain rule).  RMSNorm rows of 513-3072 granules: 3 slots."""
+    affine).  Affine rows of up to 2560 granules: 5 slots per lane (128
+    threads at 64 lanes).  RMSNorm rows of 513-3072 granules: 3 slots."""
     nl, ns, rm = R.ROWRED_POLICY_NT_LOADS, R.ROWRED_POLICY_NT_STORES, R.ROWRED_POLICY_XCD_REMAP
     G, B = RR + (1 << 30), RR + (1 << 31)
-    shifted = {1023: (64, 5, 256), 1537: (128, 4, 256), 2047: (128, 5, 256), 4095: (256, 5, 256),
+    shifted = {1023: (64, 5, 128), 1537: (128, 4, 256), 2047: (128, 5, 256), 4095: (256, 5, 256),
                8191: (512, 5, 512)}
     for width, want in ((1023, (128, 3, 256)), (1537, (256, 2, 256)), (2047, (256, 3, 256)), (4095, (256, 5, 256)),
                         (8191, (512, 5, 512)), (12287, (512, 7, 512)), (16383, (1024, 5, 1024))):
@@ -792,10 +790,9 @@ def test_ragged_layernorm_rule():
         for r in (None, RR):
             p = R.rowred_layernorm_plan_query(X, r, None, None, Y, rows, width)
             assert (p.lanes_per_row, p.chunks, p.threads, p.policy) == (*want, nl | ns | rm), (width, r, p)
-        a = R.rowred_layernorm_plan_query(X, None, G + 4, B + 4, Y, rows, width)
-        assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*want, nl | ns), (width, a)
-        a = R.rowred_layernorm_plan_query(X, None, G, B, Y, rows, width)
-        assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*shifted.get(width, want), nl | ns), (width, a)
+        for g, b in ((G, B), (G + 4, B + 4)):
+            a = R.rowred_layernorm_plan_query(X, None, g, b, Y, rows, width)
+            assert (a.lanes_per_row, a.chunks, a.threads, a.policy) == (*shifted.get(width, want), nl | ns), (width, a)
     p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=16386, width=8191)
     assert (p.lanes_per_row, p.chunks, p.threads) == (1024, 3, 1024)
     p = R.rowred_plan_query("rmsnorm", X, None, Y, rows=65536, width=2047)

@@ -61,8 +61,9 @@ def test_variants_widths(variant, width):
 @pytest.mark.parametrize("shift", [(1, 1, 1, 0), (0, 0, 0, 1), (2, 3, 1, 3), (0, 0, 0, 0)])
 @pytest.mark.parametrize("width", [6, 129, 4096])
 def test_variants_alignment(variant, shift, width):
-    """gamma/beta 16-byte aligned with aligned rows (vector path) or not
-    (element path); x, r, y at every phase."""
+    """gamma/beta 16-byte aligned with aligned rows (granule path) or at
+    another phase than the rows (16-byte loads from 4-byte boundaries); x,
+    r, y at every phase."""
     x, r, g, b = make(45, width, 5 * width + sum(shift), variant)
     ref = oracle.layernorm(x, r, eps=1e-5, gamma=g, beta=b)
     print_case(variant, shift, width)
@@ -73,9 +74,9 @@ def test_variants_alignment(variant, shift, width):
                          ids=["plain", "residual_affine-gamma_4B", "residual_affine-gamma_16B"])
 @pytest.mark.parametrize("width", [100, 1000, 4096])
 def test_variants_every_plan(variant, width, gshift):
-    """Rows one float past 16-byte boundaries; gamma/beta at another phase
-    (4-byte loads) or 16-byte aligned (two 16-byte loads per granule,
-    shifted into the row's phase)."""
+    """Rows one float past 16-byte boundaries; gamma/beta at the rows' phase
+    or 16-byte aligned, read 16 bytes at a time from 4-byte boundaries
+    (the first and last slots of a row element by element)."""
     rows = 67
     x, r, g, b = make(rows, width, 3 * width, variant)
     ref = oracle.layernorm(x, r, eps=1e-5, gamma=g, beta=b)
@@ -111,23 +112,26 @@ def test_next_workloads_full_size(case):
 @pytest.mark.parametrize("width,xshift", [(8191, 0), (8192, 1), (4097, 3)])
 def test_misaligned_affine_full_size(width, xshift):
     """Affine LayerNorm at full size on rows off 16-byte boundaries (odd width,
-    or the matrix one or three floats past a boundary) with gamma / beta
-    16-byte aligned: the chooser's own plan, sampled rows against the oracle,
-    every element checked for finiteness and the guards."""
+    or the matrix one or three floats past a boundary), gamma / beta on
+    16-byte boundaries and one float past: the chooser's own plan, sampled
+    rows against the oracle, every element checked for finiteness and the
+    guards."""
     rows = 16384
     print_case("affine misaligned", rows, width, xshift)
     x = synthetic.random_matrix(91 + width, rows, width, "uniform")
     g = (1 + 0.1 * synthetic.random_matrix(92 + width, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
     b = (0.1 * synthetic.random_matrix(93 + width, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
     xd = shifted_input(x, xshift)
-    gd, bd = dev(g), dev(b)
-    out = Guarded(rows, width, xshift)
-    R.rowred_layernorm(xd, None, gd, bd, out.y, eps=1e-5)
-    torch().cuda.synchronize()
-    assert out.guards_intact()
-    y = out.host()
-    assert np.isfinite(y).all()
     pick = np.unique(np.concatenate([np.arange(4), rows - 1 - np.arange(4),
                                      np.random.default_rng(width).integers(0, rows, 120)]))
     ref = oracle.layernorm(x[pick], None, eps=1e-5, gamma=g, beta=b)
-    assert_close(y[pick], ref, f"affine {rows}x{width} shift {xshift}")
+    for gshift in (0, 1):
+        gd = shifted_input(g.reshape(1, -1), gshift).reshape(-1)
+        bd = shifted_input(b.reshape(1, -1), gshift).reshape(-1)
+        out = Guarded(rows, width, xshift)
+        R.rowred_layernorm(xd, None, gd, bd, out.y, eps=1e-5)
+        torch().cuda.synchronize()
+        assert out.guards_intact()
+        y = out.host()
+        assert np.isfinite(y).all()
+        assert_close(y[pick], ref, f"affine {rows}x{width} shift {xshift} gamma shift {gshift}")
