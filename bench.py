@@ -188,6 +188,27 @@ class CaseBuffers:
             R.run_op(op, self.x[k], self.r[k], self.y[k], eps=self.case.eps)
 
 
+    def plan(self):
+        """The plan a call runs, as text: lanes per row x slots, threads and
+        policy bits (row plans), or the split / exchange geometry and segments
+        per row (_ws calls on rows wider than the register-resident window)."""
+        import row_wise_reduction_amd as R
+        op, x = self.case.op, self.x[0]
+        if op in ("layernorm", "layernorm_affine"):
+            p = R.rowred_layernorm_plan_query(x, None, self.g, self.b, self.y[0])
+        elif op in ("row_sum", "row_minmax"):
+            p = R.rowred_plan_query(op, x, self.y2[0] if op == "row_minmax" else None, self.y[0])
+        else:
+            p = R.rowred_plan_query(op, x, self.r[0], self.y[0])
+        if self.ws is not None and p.window > 8192:
+            sop = "layernorm_residual" if op.startswith("layernorm") else op
+            sp = R.rowred_split_plan_query(sop, x)
+            if sp.policy & R.ROWRED_POLICY_EXCHANGE:
+                return f"exchange {sp.threads} x {sp.chunks}, S = {sp.segments}, {policy_names(sp.policy)}"
+            if self.case.rows < 2048:
+                return f"split {sp.threads} x {sp.chunks}, S = {sp.segments}, {policy_names(sp.policy)}"
+        return f"{p.lanes_per_row} x {p.chunks}, {p.threads}, {policy_names(p.policy)}"
+
     def call_ws(self, k):
         import row_wise_reduction_amd as R
         op, ws = self.case.op, self.ws
@@ -201,6 +222,19 @@ class CaseBuffers:
             R.rowred_row_sum_ws(self.x[k], self.y[k], ws)
         else:
             R.rowred_row_minmax_ws(self.x[k], self.y[k], self.y2[k], ws)
+
+
+POLICY_NAMES = (("ntL", 1), ("ntS", 2), ("remap", 4), ("stage", 8), ("looped", 64), ("exchange", 128),
+                ("lds", 256), ("flat", 512), ("online", 1024))
+
+
+def policy_names(policy):
+    """Short names of a plan's policy bits (and its workgroups-per-CU cap)."""
+    names = [n for n, bit in POLICY_NAMES if policy & bit and n != "exchange"]
+    cap = (policy >> 12) & 15
+    if cap:
+        names.append(f"cap {cap}")
+    return "+".join(names) or "-"
 
 
 def rotation_sets(case):
@@ -420,7 +454,7 @@ def bench(cfg, steps, warmup, cpu_seconds, lean=False):
         us = float(np.median(case_us[i]))
         gbs = algo_bytes(c) / (us * 1e-6) / 1e9
         entry = {"us_per_call": round(us, 3), "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                 "rounds_us": spread(case_us[i]), "inputs": b.inputs}
+                 "rounds_us": spread(case_us[i]), "plan": b.plan(), "inputs": b.inputs}
         if not lean:
             cold, warm = single_and_warm(b, steps)
             copy = copy_ceiling(algo_bytes(c))
