@@ -588,6 +588,115 @@ def pmc_pass(cfg):
 
 
 # ---------------------------------------------------------------------------
+# exchange kernels: cost of the segments per row
+# ---------------------------------------------------------------------------
+
+# softmax through explicit exchange plans at a fixed segment size, S segments
+# per row, rows = 2^26 elements / width (so every S moves the same bytes and
+# launches the same number of workgroups)
+SEGMENT_SWEEP_S = (4, 8, 16, 32, 64, 128)
+SEGMENT_GEOMETRIES = (("256 x 8", 256, 8, False), ("8 + 8 LDS", 256, 16, True))
+SEGMENT_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE")
+
+
+def segment_cases():
+    for name, T, C, lds in SEGMENT_GEOMETRIES:
+        for S in SEGMENT_SWEEP_S:
+            width = S * T * C * 4
+            rows = (1 << 26) // width
+            if rows >= 1:
+                yield name, T, C, lds, S, rows, width
+
+
+def segment_sweep(calls):
+    """Time softmax exchange plans across S (HIP events, median of `calls`
+    calls after one untimed call); one JSON line per (geometry, S).  Under
+    `rocprofv3 --pmc` the same calls give each dispatch's counters."""
+    import torch
+
+    import row_wise_reduction_amd as R
+    print(f"segments kernel_source_hash {kernel_source_hash()}", flush=True)
+    for name, T, C, lds, S, rows, width in segment_cases():
+        case = synthetic.Case(9, "softmax", rows, width, "normal")
+        x = torch.from_numpy(synthetic.case_input(case, "x")).cuda()
+        y = torch.empty_like(x)
+        pol = R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | \
+            (R.ROWRED_POLICY_LDS_STRIPE if lds else 0)
+        plan = R.SplitPlan(threads=T, chunks=C, policy=pol)
+        q = R.rowred_split_plan_query("softmax", x, plan=plan)
+        assert q.segments == S, (name, S, q)
+        ws = torch.empty(q.workspace_bytes, dtype=torch.uint8, device="cuda")
+        R.rowred_split_run_plan("softmax", x, None, None, None, y, None, plan, ws)
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(calls):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            R.rowred_split_run_plan("softmax", x, None, None, None, y, None, plan, ws)
+            e.record()
+            torch.cuda.synchronize()
+            us.append(a.elapsed_time(e) * 1e3)
+        status = int(ws[:8].view(torch.int64).item())
+        print(json.dumps({"segments": S, "geometry": name, "rows": rows, "width": width, "calls": 1 + calls,
+                          "us_per_call": round(float(np.median(us)), 2), "wait_status": status}), flush=True)
+        del x, y, ws
+        torch.cuda.empty_cache()
+
+
+def segments_summary(counter_csv, log_path, out_path, timing_log=None):
+    """profiles/pmc_exchange_segments.txt: per (geometry, S), the timed
+    calls' median and the exchange kernel's counters per dispatch (mean of
+    the calls): wave lifetime = SQ_WAVE_CYCLES * 4 / SQ_WAVES cycles,
+    waiting share = SQ_WAIT_ANY / SQ_WAVE_CYCLES."""
+    timed = [json.loads(l) for l in open(log_path) if l.startswith("{")]
+    plain = {}
+    if timing_log:  # the same sweep without the profiler
+        for l in open(timing_log):
+            if l.startswith("{"):
+                t = json.loads(l)
+                plain[(t["geometry"], t["segments"])] = t["us_per_call"]
+    disp = {}
+    for r in _csv_rows(counter_csv):
+        if "seg_exchange" not in r["Kernel_Name"] and "seg_xlds" not in r["Kernel_Name"]:
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(disp)
+    lines = ["# exchange kernels (softmax) across segments per row S at a fixed segment size,",
+             "# rows = 2^26 / width: same bytes and same workgroups at every S",
+             "#   cd /tmp && TMPDIR=/tmp rocprofv3 --pmc " + " ".join(SEGMENT_COUNTERS) +
+             " --output-format csv -d <out> -o run -- python3 <repo>/bench.py --segments > <log>",
+             f"# kernel_source_hash: {_logged_hash_prefix(log_path, 'segments kernel_source_hash ')}",
+             "#   python3 <repo>/bench.py --segments > <timing log>   (the same sweep without the profiler)",
+             "# geometry | S | rows x width | us per call (median of 5 eager calls, without the profiler) | "
+             "waves per dispatch | wave lifetime (cycles) | waiting share of wave cycles"]
+    i = 0
+    for t in timed:
+        n = t["calls"]
+        group = [disp[k] for k in ids[i:i + n]]
+        i += n
+        if len(group) < n:
+            break
+        group = group[1:]  # the untimed first call
+        waves = np.mean([g.get("SQ_WAVES", 0) for g in group])
+        cyc = np.mean([g.get("SQ_WAVE_CYCLES", 0) for g in group])
+        wait = np.mean([g.get("SQ_WAIT_ANY", 0) for g in group])
+        life = 4 * cyc / waves if waves else float("nan")
+        us = plain.get((t["geometry"], t["segments"]), "-")
+        lines.append(f"{t['geometry']} | {t['segments']} | {t['rows']}x{t['width']} | {us} | "
+                     f"{waves:.0f} | {life:.0f} | {wait / cyc if cyc else float('nan'):.3f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    return out_path
+
+
+def _logged_hash_prefix(log_path, prefix):
+    for line in open(log_path, errors="replace"):
+        if line.startswith(prefix):
+            return line.split()[-1]
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
 # per-phase reload A/B: the reference design's reloads as a diagnostic
 # ---------------------------------------------------------------------------
 
@@ -915,6 +1024,12 @@ def main(argv=None):
     ap.add_argument("--next", action="store_true", help="one line per next-step workload (6-11)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--pmc", action="store_true", help="counter pass (use under rocprofv3 --pmc)")
+    ap.add_argument("--segments", action="store_true",
+                    help="softmax exchange plans at 4-128 segments per row, same bytes (timing; counters under "
+                         "rocprofv3 --pmc)")
+    ap.add_argument("--segments-summary", nargs="+", metavar="FILE",
+                    help="COUNTER_CSV LOG [TIMING_LOG]: write profiles/pmc_exchange_segments.txt from a --segments "
+                         "counter run (and the same sweep's output without the profiler)")
     ap.add_argument("--reload", action="store_true",
                     help="resident vs per-phase reload A/B at workloads 2-5 (with --pmc: its counter pass)")
     ap.add_argument("--reload-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_LOG", "WRITE_LOG"),
@@ -933,6 +1048,12 @@ def main(argv=None):
     if args.trace_summary:
         print(trace_summary(*args.trace_summary))
         return 0
+    if args.segments_summary:
+        csv_path, log_path = args.segments_summary[:2]
+        timing = args.segments_summary[2] if len(args.segments_summary) > 2 else None
+        print(segments_summary(csv_path, log_path, os.path.join(ROOT, "profiles", "pmc_exchange_segments.txt"),
+                               timing))
+        return 0
     if args.reload_summary:
         fc, wc, fl, wl = args.reload_summary
         print(reload_traffic_summary(fc, wc, os.path.join(ROOT, "profiles", "pmc_traffic_reload.txt"), fl, wl))
@@ -950,6 +1071,9 @@ def main(argv=None):
     if args.pmc and args.reload:
         for cfg in RELOAD_CFGS:
             pmc_reload_pass(cfg)
+        return 0
+    if args.segments:
+        segment_sweep(5)
         return 0
     if args.pmc:
         for cfg in (PMC_CFGS if args.all else [args.config]):

@@ -142,3 +142,44 @@ def test_short_names():
     assert bench.is_library_reduction_kernel(n)
     assert not bench.is_library_reduction_kernel("void rowred::(anonymous namespace)::copy_kernel(float4 const*)")
     assert not bench.is_library_reduction_kernel("void at::native::fill_kernel<float>()")
+
+
+def test_segments_summary_parses_a_counter_run(tmp_path):
+    """The exchange segments summary groups each timed case's exchange
+    dispatches in order (the first call of each untimed) and reports wave
+    lifetime and waiting share from SQ counters."""
+    import bench
+    cases = list(bench.segment_cases())[:2]
+    log = tmp_path / "log.txt"
+    lines = ["segments kernel_source_hash abc123"]
+    rows = []
+    did = 0
+    for k, (name, T, C, lds, S, r, w) in enumerate(cases):
+        lines.append(json.dumps({"segments": S, "geometry": name, "rows": r, "width": w, "calls": 3,
+                                 "us_per_call": 10.0 + k, "wait_status": 0}))
+        for call in range(3):
+            did += 1  # clear kernel, ignored
+            rows.append((did, "rowred::(anonymous namespace)::exchange_clear_kernel", "SQ_WAVES", 1))
+            did += 1
+            kname = "void rowred::(anonymous namespace)::seg_exchange_kernel<2, 8>(rowred::SegArgs)"
+            scale = 1 if call else 100  # the untimed call is dropped
+            for ctr, v in (("SQ_WAVES", 1000), ("SQ_WAVE_CYCLES", 250 * (k + 1) * scale),
+                           ("SQ_WAIT_ANY", 100 * (k + 1) * scale)):
+                rows.append((did, kname, ctr, v))
+    log.write_text("\n".join(lines) + "\n")
+    csv_path = tmp_path / "c.csv"
+    with open(csv_path, "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n')
+        for d, n, c, v in rows:
+            f.write(f'{d},"{n}","{c}",{v}\n')
+    out = tmp_path / "out.txt"
+    bench.segments_summary(str(csv_path), str(log), str(out))
+    body = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert len(body) == 2 and body[0].split(" | ")[3] == "-"
+    bench.segments_summary(str(csv_path), str(log), str(out), str(log))  # with the timing log
+    body = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert body[0].split(" | ")[3] == "10.0" and body[1].split(" | ")[3] == "11.0"
+    # lifetime = 4 * 250 (k+1) / 1000 cycles; waiting share 100/250
+    assert body[0].split(" | ")[5:] == ["1", "0.400"]
+    assert body[1].split(" | ")[5:] == ["2", "0.400"]
+    assert "abc123" in out.read_text()
