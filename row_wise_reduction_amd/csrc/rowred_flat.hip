@@ -154,14 +154,18 @@ __global__ void __launch_bounds__(kFlatMaxThreads) flat_kernel(RowArgs a) {
     // barriers.  -inf elements weigh 0 (also in a part whose max is -inf);
     // NaN and +inf poison the row's sum, as in one pass.
     float *pm = lds, *ps = lds + 2 * G;  // [A parts | B parts] of the max, then of the sum
+    // The exponentials stay in o[] (against their part's max); the output
+    // scales each part by exp(part max - row max) / row sum.
+    float ma[C], mb[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      float ma = -__builtin_inff(), mb = -__builtin_inff();
+      ma[c] = -__builtin_inff();
+      mb[c] = -__builtin_inff();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float t = in_run(c, j) ? xv[c][j] : -__builtin_inff();
-        if (j < split[c]) ma = fmaxf(ma, t);
-        else mb = fmaxf(mb, t);
+        if (j < split[c]) ma[c] = fmaxf(ma[c], t);
+        else mb[c] = fmaxf(mb[c], t);
       }
       float sa = 0.0f, sb = 0.0f;
 #pragma unroll
@@ -170,58 +174,53 @@ __global__ void __launch_bounds__(kFlatMaxThreads) flat_kernel(RowArgs a) {
         const bool a_part = j < split[c];
         const float e = (!in_run(c, j) || x == -__builtin_inff())
                             ? 0.0f
-                            : __builtin_amdgcn_exp2f((x - (a_part ? ma : mb)) * kLog2e);
+                            : __builtin_amdgcn_exp2f((x - (a_part ? ma[c] : mb[c])) * kLog2e);
+        o[4 * c + j] = e;
         if (a_part) sa += e;
         else sb += e;
       }
       const int k = slot_k(c);
-      pm[k] = ma;
-      pm[G + k] = mb;
+      pm[k] = ma[c];
+      pm[G + k] = mb[c];
       ps[k] = sa;
       ps[G + k] = sb;
     }
     __syncthreads();
-    // (m, s) <- (m, s) merged with (m2, s2); commutative, so both lanes of a
-    // butterfly step get the same bits.
-    auto merge = [](float &m, float &s, float m2, float s2) {
-      const float mn = fmaxf(m, m2);
-      const float fa = m == mn ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-      const float fb = m2 == mn ? 1.0f : __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-      s = s * fa + s2 * fb;
-      m = mn;
-    };
+    // Per row: the max over its granule parts (a butterfly finishes the
+    // group), then each part's sum restated under it (s * exp(m - M), s
+    // itself when m == M, so two -inf maxima give 0 rather than NaN) and
+    // added, a second butterfly; the exponentials are independent.
     const int q = threadIdx.x >> lpr_log2, i = threadIdx.x & ((1 << lpr_log2) - 1);
-    float m = -__builtin_inff(), sum = 0.0f;
+    int g0 = 0, g1 = -1;
+    bool starts_inside = false;
     if (q < nr) {
       const int first = q * width + d0;
-      const int g0 = first >> 2, g1 = (first + width - 1) >> 2;
-      const bool starts_inside = q > 0 && (first & 3) != 0;
-      for (int g = g0 + i; g <= g1; g += 1 << lpr_log2) {
-        const int at = (g == g0 && starts_inside) ? G + g : g;
-        merge(m, sum, pm[at], ps[at]);
-      }
+      g0 = first >> 2;
+      g1 = (first + width - 1) >> 2;
+      starts_inside = q > 0 && (first & 3) != 0;
     }
-    if (lpr_log2 >= 1) merge(m, sum, dpp<kDppXor1>(m), dpp<kDppXor1>(sum));
-    if (lpr_log2 >= 2) merge(m, sum, dpp<kDppXor2>(m), dpp<kDppXor2>(sum));
-    if (lpr_log2 >= 3) merge(m, sum, dpp<kDppHalfMirror>(m), dpp<kDppHalfMirror>(sum));
-    if (lpr_log2 >= 4) merge(m, sum, dpp<kDppMirror>(m), dpp<kDppMirror>(sum));
-    if (lpr_log2 >= 5) merge(m, sum, swizzle_xor16(m), swizzle_xor16(sum));
-    if (lpr_log2 >= 6) {
-      float m0 = readlane(m, 0), s0 = readlane(sum, 0);
-      merge(m0, s0, readlane(m, 32), readlane(sum, 32));
-      m = m0;
-      sum = s0;
+    float m = -__builtin_inff();
+    for (int g = g0 + i; g <= g1; g += 1 << lpr_log2) m = fmaxf(m, pm[(g == g0 && starts_inside) ? G + g : g]);
+    m = group_allreduce<MaxOp>(m, lpr_log2);
+    float sum = 0.0f;
+    for (int g = g0 + i; g <= g1; g += 1 << lpr_log2) {
+      const int at = (g == g0 && starts_inside) ? G + g : g;
+      sum += rescale_sum(ps[at], pm[at], m);
     }
+    sum = group_allreduce<SumOp>(sum, lpr_log2);
     if (i == 0 && q < nr) {
       tot0[q] = m;
       tot1[q] = __builtin_amdgcn_rcpf(sum);
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < C; ++c) {
+      const int ra = qa[c] < P ? qa[c] : P, rb = qa[c] + 1 < P ? qa[c] + 1 : P;
+      const float fa = __builtin_amdgcn_exp2f((ma[c] - tot0[ra]) * kLog2e) * tot1[ra];
+      const float fb = __builtin_amdgcn_exp2f((mb[c] - tot0[rb]) * kLog2e) * tot1[rb];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[4 * c + j] = __builtin_amdgcn_exp2f((xv[c][j] - stat(tot0, c, j)) * kLog2e) * stat(tot1, c, j);
+      for (int j = 0; j < 4; ++j) o[4 * c + j] *= j < split[c] ? fa : fb;
+    }
   }
 
   // ---- store: whole granules, except where the run shares a granule with
