@@ -391,14 +391,15 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // geometry x cap (0-10) at 2^27 elements per matrix (MI355X) put the
   // fastest plans at about 40-64 KiB of loads in flight per CU (threads per
   // CU x slots x 16 bytes) for one input and 64-128 KiB with r; more waves
-  // than that only queue behind one another.  Against the rules below:
-  //   RMSNorm    512, 1024, 2048, 4096, 8192 columns: 173.9 -> 164.0,
-  //              170.1 -> 164.6, 170.1 -> 166.1, 169.3 -> 167.8, 170.0 -> 166.9 us
-  //   softmax    170.0 -> 165.6, 170.5 -> 165.3, 169.0 -> 165.7, 167.9 -> 166.0,
-  //              176.3 -> 166.0 us
+  // than that only queue behind one another.  Against the rules below (both
+  // timed in alternating order after a warm-up):
+  //   RMSNorm    512, 1024, 2048, 4096, 8192 columns: 175.7 -> 163.7,
+  //              170.5 -> 164.3, 170.6 -> 166.8, 170.3 -> 167.8, 169.4 -> 167.2 us
+  //   softmax    171.3 -> 166.2, 170.8 -> 164.7, 169.6 -> 165.1, 167.9 -> 166.4,
+  //              171.3 -> 166.4 us
   //   residual LayerNorm 1024, 2048, 4096, 8192, 16384, 32768 columns:
-  //              261.6 -> 246.8, 260.4 -> 252.6, 256.3 -> 247.9, 253.2 -> 247.4,
-  //              291.4 -> 269.1, 290.5 -> 280.6 us
+  //              259.5 -> 246.2, 259.4 -> 251.7, 256.8 -> 248.6, 253.8 -> 247.9,
+  //              292.2 -> 269.0, 290.0 -> 279.9 us
   // (caps of 3 and 5 measured as 2 and 4: use even caps above 1).
   const bool two_in = c.r != nullptr && c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
   if (rows_aligned && in_bytes > (int64_t(64) << 20) && !scalar_out && !affine && w >= 128 &&
@@ -442,9 +443,10 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // beyond 64 MiB: three slots per lane in one row per workgroup (L the
   // smallest power of two >= a third of the window, at least 256), at most 6
   // workgroups per CU at 256 lanes.  MI355X, against the rules below: RMSNorm
-  // 65536x2047, 32768x4095, 16384x8191: 190.6 -> 173.8, 199.7 -> 174.5,
-  // 180.1 -> 178.5 us; softmax 224.9 -> 173.7, 280.1 -> 177.4, 195.2 -> 180.8
-  // us (the rules below leave up to half of each lane's slots past the row).
+  // 65568x2047, 32776x4095, 16386x8191: 187.4 -> 173.6, 198.7 -> 175.7,
+  // 178.7 -> 178.6 us; softmax 219.4 -> 173.5, 232.8 -> 176.9 (283.4 with
+  // one collective), 186.4 -> 181.6 us (the rules below leave up to half of
+  // each lane's slots past the row).
   if ((c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && !rows_aligned && in_bytes > (int64_t(64) << 20) &&
       w > 512 && w <= 3072) {
     int64_t L = 256;
@@ -571,7 +573,8 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // Softmax across a 1024-lane row beyond 64 MiB: one (max, sum) collective
   // instead of two (8192x16384 177.4 -> 174.9 us; 2048x32768 97.7 -> 94.1 us
   // with the LDS stripe) -- on 16-byte aligned rows: rows off the boundaries
-  // in registers measured slower with it (32768x4095 in 1024 x 2: 234 -> 280 us).
+  // in registers measured slower with it (32776x4095 in 1024 x 2: 233 -> 283 us,
+  // in 512 x 3: 176.9 -> 178.6 us).
   if (c.op == ROWRED_OP_SOFTMAX && L == 1024 &&
       ((policy & kPolicyLdsStripe) || (rows_aligned && in_bytes > (int64_t(64) << 20))))
     policy |= kPolicyOnline;
