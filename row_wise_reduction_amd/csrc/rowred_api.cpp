@@ -182,7 +182,15 @@ int finish_flat_plan(const Call &c, rowred_plan *p) {
   return ROWRED_OK;
 }
 
+// The exchange path (defined with the split plans below).
+bool choose_exchange(int op, int64_t rows, int64_t window, rowred_split_plan *p);
+int finish_split(const Call &c, rowred_split_plan *p);
+bool exchange_fits(int op, const rowred_split_plan &p);
+int finish_row_exchange_plan(const Call &c, rowred_plan *p, rowred_split_plan *sp);
+int run_row_exchange(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream);
+
 int finish_plan(const Call &c, rowred_plan *p) {
+  if (p->policy & kPolicyExchange) return finish_row_exchange_plan(c, p, nullptr);
   if (p->policy & kPolicyFlat) return finish_flat_plan(c, p);
   if ((p->policy & kPolicyLooped) && (p->policy & kPolicyLdsStripe)) return finish_wide_tail_plan(c, p);
   if (p->policy & kPolicyLooped) return finish_looped_plan(c, p);
@@ -276,6 +284,31 @@ void choose_looped(const Call &c, rowred_plan *p) {
 constexpr int64_t kLdsStripeMaxGranules = int64_t(2048) * 8192;
 
 void choose_plan(const Call &c, rowred_plan *p) {
+  // LayerNorm, RMSNorm and softmax rows wider than the register-resident
+  // window: the exchange kernels with their words in y's own rows (no
+  // workspace), so the row is read once, where the device holds twice a
+  // row's segments; the geometry is the _ws entry points' (choose_exchange).
+  // Faster than the LDS-stripe and head+tail kernels below at every shape
+  // measured (MI355X): softmax 1024x50257 83.4 -> 75.1 us, 4096x65536 377
+  // -> 336 us, 1024x262144 446 -> 357 us, 128x1048576 295 -> 211 us;
+  // RMSNorm 2048x40000 116 -> 110 us, 2048x131072 385 -> 346 us, 64x1048576
+  // 183 -> 108 us; residual LayerNorm 1024x65536 160 -> 137 us, 4096x32772
+  // 299 -> 276 us, 256x262144 198 -> 154 us.
+  if (c.window > kMaxWindow && c.op <= ROWRED_OP_SOFTMAX) {
+    rowred_split_plan sp;
+    if (choose_exchange(c.op, c.rows, c.window, &sp)) {
+      rowred_plan q = rowred_plan{};
+      q.lanes_per_row = sp.threads;
+      q.threads = sp.threads;
+      q.chunks = sp.chunks;
+      q.policy = sp.policy;
+      rowred_plan t = q;
+      if (finish_row_exchange_plan(c, &t, &sp) == ROWRED_OK && exchange_fits(c.op, sp)) {
+        *p = q;
+        return;
+      }
+    }
+  }
   // RMSNorm and softmax rows of 8193-16384 granules: 8 register and up to 8
   // LDS slots per lane hold the whole row, read once (the looped kernels
   // read it twice).
@@ -584,6 +617,7 @@ void choose_plan(const Call &c, rowred_plan *p) {
 }
 
 int run(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
+  if (plan.policy & kPolicyExchange) return run_row_exchange(c, plan, eps, stream);
   RowArgs a;
   a.x = c.x;
   a.r = c.r;
@@ -900,6 +934,66 @@ bool exchange_fits(int op, const rowred_split_plan &p) {
   return exchange_resident_groups(op, p.chunks, p.threads, p.policy) >= 2 * p.segments;
 }
 
+// A row plan with ROWRED_POLICY_EXCHANGE: LayerNorm, RMSNorm or softmax rows
+// cut into segments of threads * chunks granules, one workgroup each, that
+// swap their statistics through words in y's own row (the first 16-byte
+// boundary of the row on; segment 0 writes its outputs over them last).
+// lanes_per_row == threads; policy: EXCHANGE with NT_LOADS, NT_STORES and
+// LDS_STRIPE as on split plans.  grid = rows * segments.  *sp (optional)
+// receives the matching split plan.
+int finish_row_exchange_plan(const Call &c, rowred_plan *p, rowred_split_plan *sp) {
+  if (c.op > ROWRED_OP_SOFTMAX || p->lanes_per_row != p->threads || p->reserved != 0) return ROWRED_ERR_INVALID_ARG;
+  if (p->policy & ~(kPolicyExchange | kPolicyNtLoads | kPolicyNtStores | kPolicyLdsStripe))
+    return ROWRED_ERR_INVALID_ARG;
+  rowred_split_plan q = rowred_split_plan{};
+  q.threads = p->threads;
+  q.chunks = p->chunks;
+  q.policy = p->policy;
+  const int st = finish_split(c, &q);  // the whole matrix in one launch (block_rows = rows)
+  if (st != ROWRED_OK) return st;
+  // the row's words end inside segment 0's outputs and inside the row
+  const int64_t bytes = row_exchange_bytes(c.op == ROWRED_OP_LAYERNORM_RESIDUAL ? 2 : 1, q.segments);
+  if (bytes > 16 * (int64_t)q.threads * q.chunks - 12 || bytes > 4 * c.width) return ROWRED_ERR_INVALID_ARG;
+  p->rows_per_group = 1;
+  p->window = c.window;
+  p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;
+  p->grid = q.grid;
+  if (sp) *sp = q;
+  return ROWRED_OK;
+}
+
+// Run a row exchange plan: the row clear of each row's words in y, then the
+// exchange kernel.  The device must hold twice a row's segments at once
+// (ROWRED_ERR_UNSUPPORTED otherwise).
+int run_row_exchange(const Call &c, const rowred_plan &plan, float eps, hipStream_t stream) {
+  rowred_plan p = plan;
+  rowred_split_plan q;
+  const int st = finish_row_exchange_plan(c, &p, &q);
+  if (st != ROWRED_OK) return st;
+  if (!exchange_fits(c.op, q)) return ROWRED_ERR_UNSUPPORTED;
+  SegArgs a;
+  a.x = c.x;
+  a.r = c.r;
+  a.gamma = c.gamma;
+  a.beta = c.beta;
+  a.y = c.y;
+  a.y2 = nullptr;
+  a.ws = nullptr;
+  a.ws_in_y = 1;
+  a.rows = c.rows;
+  a.width = (int32_t)c.width;
+  a.segments = (int32_t)q.segments;
+  a.lanes_log2 = ilog2(q.threads);
+  a.seg_granules = q.threads * q.chunks;
+  a.eps = eps;
+  a.inv_width = 1.0f / (float)c.width;
+  a.policy = q.policy;
+  a.r_vec = c.r_vec ? 1 : 0;
+  a.y_vec = c.y_vec ? 1 : 0;
+  a.spin_limit = kExchangeSpinLimit;
+  return launch_exchange(c.op, q.chunks, q.grid, q.threads, a, true, stream) != 0 ? ROWRED_ERR_HIP : ROWRED_OK;
+}
+
 // static_ws: the library's own workspace (rowred_static_ws), whose size is
 // a limit of the library rather than an argument error.
 int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, size_t ws_bytes, bool static_ws,
@@ -921,6 +1015,7 @@ int run_split(const Call &c, const rowred_split_plan &p, float eps, void *ws, si
   a.gamma = c.gamma;
   a.beta = c.beta;
   a.ws = static_cast<double *>(ws);
+  a.ws_in_y = 0;
   a.width = (int32_t)c.width;
   a.segments = (int32_t)p.segments;
   a.lanes_log2 = ilog2(p.threads);

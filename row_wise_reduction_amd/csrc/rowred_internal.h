@@ -151,7 +151,14 @@ struct SegArgs {
   int32_t r_vec;
   int32_t y_vec;
   uint32_t spin_limit;  // exchange kernels: polls of one slot before a wait gives up
+  int32_t ws_in_y;      // exchange kernels: 1 = the words live in each row of y (no workspace)
 };
+
+// Exchange words kept in y's own row (plain entry points, no workspace): from
+// the row's first 16-byte boundary, `rounds * S` slots then one count of the
+// segments done reading them; the last of them must end inside segment 0's
+// outputs, which that segment writes last.
+constexpr int64_t row_exchange_bytes(int rounds, int64_t segments) { return 15 + 8 * (rounds * segments + 1); }
 
 // Polls of one exchange slot before the wait gives up (a second or so: each
 // poll is a load that goes past the XCD's L2, then s_sleep 2).  An explicit

@@ -462,8 +462,48 @@ __device__ __forceinline__ uint64_t encode_pair(float m, float s) {
   return ~(((uint64_t)__builtin_bit_cast(uint32_t, s) << 32) | __builtin_bit_cast(uint32_t, m));
 }
 
+// The exchange words of a row kept in y itself (ws_in_y): from the first
+// 16-byte boundary of the row's outputs.
+// (Pointer arithmetic, not an integer round trip, so that the compiler keeps
+// the global address space and emits global, not flat, accesses.)
+__device__ __forceinline__ uint64_t *row_words(const SegArgs &a, int64_t row) {
+  float *yrow = a.y + row * (int64_t)a.width;
+  const int pad = (int)((16 - (reinterpret_cast<uintptr_t>(yrow) & 15)) & 15);
+  return reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(yrow) + pad);
+}
+
 __device__ __forceinline__ uint64_t *exchange_slots(const SegArgs &a, int round, int64_t row) {
+  if (a.ws_in_y) return row_words(a, row) + (int64_t)round * a.segments;
   return reinterpret_cast<uint64_t *>(a.ws) + 1 + ((int64_t)round * a.rows + row) * a.segments;
+}
+
+// With the words in y's row, segment 0 may write its outputs over them only
+// once every segment of the row has read them.  Each workgroup counts itself
+// done after its fold -- every lane's slot reads have returned by then: the
+// fold's barrier (or, for one wavefront, program order) follows the values'
+// use, so a relaxed count suffices -- and segment 0 waits for all S (bounded
+// like the slot waits) before any of its stores.  A wait that gives up
+// returns true: the caller writes NaN over the row's segment (segments that
+// had not read yet may then see outputs as words).
+__device__ __forceinline__ bool release_row_words(const SegArgs &a, int64_t row, int seg, int rounds) {
+  if (!a.ws_in_y) return false;
+  __shared__ int gave_up;
+  uint64_t *done = row_words(a, row) + (int64_t)rounds * a.segments;
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(done, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (seg != 0) return false;  // uniform over the workgroup
+  if (threadIdx.x == 0) {
+    uint64_t n = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t it = 0;
+#pragma nounroll
+    for (; n < (uint64_t)a.segments && it < a.spin_limit; ++it) {
+      __builtin_amdgcn_s_sleep(2);
+      n = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    gave_up = n < (uint64_t)a.segments ? 1 : 0;
+  }
+  __syncthreads();
+  return gave_up != 0;
 }
 
 __device__ __forceinline__ void publish(uint64_t *slot, uint64_t w) {
@@ -480,8 +520,9 @@ __device__ __forceinline__ uint64_t await_slot(const SegArgs &a, const uint64_t 
 #pragma nounroll
   for (uint32_t it = 0; w == 0; ++it) {
     if (it >= a.spin_limit) {
-      __hip_atomic_store(reinterpret_cast<uint64_t *>(a.ws), (uint64_t)1, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      if (!a.ws_in_y)  // words in y's rows have no status word: the row turns NaN only
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(a.ws), (uint64_t)1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -630,6 +671,7 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
     // partials_d[1]'s reduction passed.
     rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
   }
+  if (release_row_words(a, row, seg, OP == kOpLayerNorm ? 2 : 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
   apply_store<OP, C, OP == kOpLayerNorm>(a, v, row, xv, rv, rr);
 }
 
@@ -852,6 +894,7 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
     publish(slots1 + seg, encode((double)m2));
     rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
   }
+  if (release_row_words(a, row, seg, kLN ? 2 : 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
 
   // ---- map and store, slot by slot.
   float scale = 0.0f, m_hi = 0.0f, m_lo = 0.0f;
@@ -930,6 +973,17 @@ __global__ void __launch_bounds__(256) exchange_clear_kernel(uint64_t *w, int64_
   if (i >= n128) return;
   if (i == 0 && first == 1) w[1] = 0;  // keep the status word
   else reinterpret_cast<u64x2 *>(w)[i] = u64x2{0, 0};
+}
+
+// Zero `words` 64-bit words of each row's exchange area in y (ws_in_y).
+__global__ void __launch_bounds__(256) exchange_clear_row_words_kernel(float *y, int64_t rows, int32_t width,
+                                                                       int32_t words) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * words) return;
+  const int64_t row = i / words;
+  float *yrow = y + row * (int64_t)width;
+  const int pad = (int)((16 - (reinterpret_cast<uintptr_t>(yrow) & 15)) & 15);
+  reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(yrow) + pad)[i - row * words] = 0;
 }
 
 using SegFn = void (*)(SegArgs);
@@ -1047,13 +1101,25 @@ int launch_exchange(int op, int chunks, int64_t grid, int threads, const SegArgs
                     hipStream_t stream) {
   const SegFn fn = exchange_kernel(op, chunks, threads, args.policy);
   if (!fn || args.segments > threads || args.segments > kMaxExchangeSegments) return (int)hipErrorInvalidValue;
-  uint64_t *w = reinterpret_cast<uint64_t *>(args.ws);
-  int64_t n128 = (exchange_words(op, args.rows, args.segments) + 1) / 2;
-  int64_t first = clear_status ? 0 : 1;  // 64-bit word to start clearing at
-  void *clear_params[] = {&w, &first, &n128};
-  int err = (int)hipLaunchKernel(reinterpret_cast<const void *>(exchange_clear_kernel),
-                                 dim3((uint32_t)((n128 + kClearThreads - 1) / kClearThreads)), dim3(kClearThreads),
-                                 clear_params, 0, stream);
+  int err = 0;
+  if (args.ws_in_y) {  // each row's words in y: its slots and its done count
+    float *y = args.y;
+    int64_t rows = args.rows;
+    int32_t width = args.width;
+    int32_t words = (op == kOpLayerNorm ? 2 : 1) * args.segments + 1;
+    void *clear_params[] = {&y, &rows, &width, &words};
+    err = (int)hipLaunchKernel(reinterpret_cast<const void *>(exchange_clear_row_words_kernel),
+                               dim3((uint32_t)((rows * words + kClearThreads - 1) / kClearThreads)),
+                               dim3(kClearThreads), clear_params, 0, stream);
+  } else {
+    uint64_t *w = reinterpret_cast<uint64_t *>(args.ws);
+    int64_t n128 = (exchange_words(op, args.rows, args.segments) + 1) / 2;
+    int64_t first = clear_status ? 0 : 1;  // 64-bit word to start clearing at
+    void *clear_params[] = {&w, &first, &n128};
+    err = (int)hipLaunchKernel(reinterpret_cast<const void *>(exchange_clear_kernel),
+                               dim3((uint32_t)((n128 + kClearThreads - 1) / kClearThreads)), dim3(kClearThreads),
+                               clear_params, 0, stream);
+  }
   if (err) return err;
   SegArgs a = args;
   void *params[] = {&a};

@@ -383,6 +383,48 @@ def test_head_tail_plan_preconditions():
             R.ROWRED_ERR_INVALID_ARG, (op, width, kw)
 
 
+def test_row_exchange_plan_preconditions():
+    """ROWRED_POLICY_EXCHANGE on a row plan: LayerNorm, RMSNorm and softmax
+    rows in segments of threads * chunks granules (lanes_per_row == threads),
+    only the memory bits and LDS_STRIPE beside it, the split plans' geometry
+    limits, and the row's exchange words (2 S + 1 for LayerNorm, S + 1
+    otherwise, 8 bytes each, from the row's first 16-byte boundary) ending
+    inside segment 0's outputs and inside the row.  Valid plans pass the
+    checks (on a host without a device the run then reports the missing
+    residency, never an argument error)."""
+    E, LDS = R.ROWRED_POLICY_EXCHANGE, R.ROWRED_POLICY_LDS_STRIPE
+    lib = R.lib()
+
+    def st(op, width, **kw):
+        c = bad_plan(**kw)._c()
+        if op == "affine":
+            return lib.rowred_layernorm_run_plan(X, None, RR, None, Y, 8, width, f(1e-5), ctypes.byref(c), None)
+        if op == "row_sum":
+            return lib.rowred_row_reduce_run_plan(3, X, RR, None, 8, width, ctypes.byref(c), None)
+        return lib.rowred_run_plan(op, X, RR if op == 0 else None, Y, 8, width, f(1e-5), ctypes.byref(c), None)
+
+    g = dict(lanes_per_row=256, threads=256, chunks=8)
+    for op, width, kw in ((1, 100000, dict(g, policy=E | 3)), (2, 1 << 20, dict(g, chunks=16, policy=E | 3 | LDS)),
+                          (0, 65536, dict(g, policy=E | LDS)), ("affine", 65536, dict(g, policy=E | 3 | LDS)),
+                          (0, 40000, dict(lanes_per_row=1024, threads=1024, chunks=4, policy=E)),
+                          (1, 16377, dict(lanes_per_row=64, threads=64, chunks=1, policy=E))):  # 64 segments
+        assert st(op, width, **kw) != R.ROWRED_ERR_INVALID_ARG, (op, width, kw)
+    for op, width, kw in ((1, 100000, dict(g, lanes_per_row=128, policy=E)),       # lanes != threads
+                          (1, 100000, dict(g, policy=E | R.ROWRED_POLICY_XCD_REMAP)),
+                          (2, 100000, dict(g, policy=E | R.ROWRED_POLICY_ONLINE)),
+                          (2, 100000, dict(g, policy=E | R.ROWRED_POLICY_LOOPED)),
+                          (2, 100000, dict(g, chunks=4, policy=E | R.ROWRED_POLICY_STAGE_STORES)),
+                          (2, 100000, dict(g, policy=E | R.ROWRED_POLICY_RELOAD)),
+                          (2, 100000, dict(g, policy=E, reserved=1)),
+                          ("row_sum", 100000, dict(g, policy=E)),                  # matrix operators only
+                          (0, 100000, dict(g, policy=E)),                         # LayerNorm: 8 slots need LDS
+                          (2, 4 * 1024 * 4 * 128 + 4, dict(lanes_per_row=1024, threads=1024, chunks=4,
+                                                           policy=E)),            # 129 segments
+                          (0, 16377, dict(lanes_per_row=64, threads=64, chunks=1, policy=E)),  # 129 words > 1012 B
+                          (2, 5, dict(lanes_per_row=64, threads=64, chunks=1, policy=E))):     # row < its words
+        assert st(op, width, **kw) == R.ROWRED_ERR_INVALID_ARG, (op, width, kw)
+
+
 def test_stage_policy_preconditions():
     m = R.ROWRED_POLICY_STAGE_STORES
     ok = bad_plan(lanes_per_row=32, chunks=2, threads=256, policy=m)._c()
