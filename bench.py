@@ -190,8 +190,9 @@ class CaseBuffers:
 
     def plan(self):
         """The plan a call runs, as text: lanes per row x slots, threads and
-        policy bits (row plans), or the split / exchange geometry and segments
-        per row (_ws calls on rows wider than the register-resident window)."""
+        policy bits (row plans), or the exchange / split geometry and segments
+        per row (row exchange plans, and _ws calls on rows wider than the
+        register-resident window)."""
         import row_wise_reduction_amd as R
         op, x = self.case.op, self.x[0]
         if op in ("layernorm", "layernorm_affine"):
@@ -207,6 +208,9 @@ class CaseBuffers:
                 return f"exchange {sp.threads} x {sp.chunks}, S = {sp.segments}, {policy_names(sp.policy)}"
             if self.case.rows < 2048:
                 return f"split {sp.threads} x {sp.chunks}, S = {sp.segments}, {policy_names(sp.policy)}"
+        if p.policy & R.ROWRED_POLICY_EXCHANGE:
+            S = p.grid // max(1, self.case.rows)
+            return f"row exchange {p.threads} x {p.chunks}, S = {S}, {policy_names(p.policy)}"
         return f"{p.lanes_per_row} x {p.chunks}, {p.threads}, {policy_names(p.policy)}"
 
     def call_ws(self, k):
@@ -701,21 +705,29 @@ def _logged_hash_prefix(log_path, prefix):
 # ---------------------------------------------------------------------------
 
 RELOAD_CFGS = (2, 3, 4, 5)
-# resident: the chooser's plan; reload: the same plan re-reading the row in
+# resident: the chooser's geometry on the register kernels; reload: that plan re-reading the row in
 # every phase after the first; reload_cached: that without the non-temporal
 # load hint, so the re-reads may hit in L2.
 RELOAD_VARIANTS = ("resident", "reload", "reload_cached")
 
 
 def variant_plan(case, b, variant):
+    """The register-kernel plan of the chooser's geometry (exchange and
+    LDS-stripe plans: one 1024-lane workgroup per row; two softmax
+    collectives: the reload kernels have no one-collective form), then the
+    variant's bits."""
     import row_wise_reduction_amd as R
     p = R.rowred_plan_query(case.op, b.x[0], b.r[0], b.y[0])
-    pol = p.policy
+    L, C, T, pol = p.lanes_per_row, p.chunks, p.threads, p.policy & ~R.ROWRED_POLICY_ONLINE
+    if pol & (R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_LDS_STRIPE):
+        L = T = 1024
+        C = -(-p.window // 1024)
+        pol &= R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP
     if variant != "resident":
         pol |= R.ROWRED_POLICY_RELOAD
     if variant == "reload_cached":
         pol &= ~R.ROWRED_POLICY_NT_LOADS
-    return R.Plan(p.lanes_per_row, 0, p.chunks, p.threads, 0, policy=pol)
+    return R.Plan(L, 0, C, T, 0, policy=pol)
 
 
 def plan_call(b, plan, i):

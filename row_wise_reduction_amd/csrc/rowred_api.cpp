@@ -294,7 +294,9 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // RMSNorm 2048x40000 116 -> 110 us, 2048x131072 385 -> 346 us, 64x1048576
   // 183 -> 108 us; residual LayerNorm 1024x65536 160 -> 137 us, 4096x32772
   // 299 -> 276 us, 256x262144 198 -> 154 us.
-  if (c.window > kMaxWindow && c.op <= ROWRED_OP_SOFTMAX) {
+  // Affine LayerNorm keeps the head+tail kernels there (1024x65536 120 ->
+  // 116 us, 2048x40000 144 -> 133 us, 256x262144 145 -> 134 us).
+  if (c.window > kMaxWindow && c.op <= ROWRED_OP_SOFTMAX && !c.gamma && !c.beta) {
     rowred_split_plan sp;
     if (choose_exchange(c.op, c.rows, c.window, &sp)) {
       rowred_plan q = rowred_plan{};
@@ -364,6 +366,47 @@ void choose_plan(const Call &c, rowred_plan *p) {
   if (c.window > kMaxWindow) {
     choose_looped(c, p);
     return;
+  }
+  // Large calls (128 MiB or more per input; RMSNorm and softmax rows off
+  // 16-byte boundaries 512 MiB) of LayerNorm rows of 2049-8192 granules and
+  // RMSNorm / softmax rows of 4097-8192: the exchange kernels with their
+  // words in y's rows too, in segments of 1024 granules (256 x 4; softmax
+  // rows beyond 6144 granules 128 x 8), LayerNorm in segments of 2048 (256 x
+  // 8, half in LDS) where they pad no more than segments of 1024 would.
+  // MI355X, against the register, LDS-stripe and looped kernels: residual
+  // LayerNorm 6553x20480 332 -> 255 us, 4096x32768 280 -> 259 us, 8192x16384
+  // 270 -> 259 us, 10922x12288 258 -> 256 us, 6710x20001 298 -> 266 us;
+  // plain 8192x16384 217 -> 189 us; affine 4096x32768 415 -> 234 us;
+  // softmax 8192x32768 364 -> 339 us, 5461x24576 183 -> 172 us; RMSNorm
+  // 8192x32768 357 -> 337 us, 1638x20480 53.1 -> 48.8 us.  Smaller calls
+  // lose (16 MiB: 7-11 us against 10-15 us, the row-word clear included).
+  {
+    const bool ln = c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
+    const bool aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
+    const int64_t bytes = c.rows * c.width * 4;
+    const bool large = ln ? c.window > 2048 && bytes >= (int64_t(128) << 20)
+                          : (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && c.window > 4096 &&
+                                bytes >= (int64_t(aligned ? 128 : 512) << 20);
+    if (large) {
+      rowred_plan q = rowred_plan{};
+      q.threads = 256;
+      q.chunks = 4;
+      q.policy = kPolicyExchange | kPolicyNtLoads | kPolicyNtStores;
+      if (ln && ((c.window + 1023) / 1024) % 2 == 0) {
+        q.chunks = 8;
+        q.policy |= kPolicyLdsStripe;
+      } else if (c.op == ROWRED_OP_SOFTMAX && c.window > 6144) {
+        q.threads = 128;
+        q.chunks = 8;
+      }
+      q.lanes_per_row = q.threads;
+      rowred_plan t = q;
+      rowred_split_plan sp;
+      if (finish_row_exchange_plan(c, &t, &sp) == ROWRED_OK && exchange_fits(c.op, sp)) {
+        *p = q;
+        return;
+      }
+    }
   }
   const int64_t w = c.window;
   const int64_t in_bytes = c.rows * c.width * 4;

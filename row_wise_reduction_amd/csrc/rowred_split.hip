@@ -72,6 +72,22 @@ __device__ __forceinline__ int64_t segment_count(int64_t k, int64_t G, int off, 
   return b > a ? b - a : 0;
 }
 
+// gamma (absent: 1) or beta (absent: 0) of the four elements e0 .. e0 + 3
+// of one slot: one 16-byte load from a 4-byte boundary where all four lie in
+// the row (the vectors may sit at any 16-byte phase against the row), element
+// loads clamped into the vector at the row's two ends and past it.
+__device__ __forceinline__ f32x4 affine_slot(const float *p, int e0, int width, float absent) {
+  if (!p) return f32x4(absent);
+  f32x4 r;
+  if (e0 >= 0 && e0 + 4 <= width) {
+    __builtin_memcpy(&r, p + e0, sizeof(r));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = p[max(0, min(e0 + j, width - 1))];
+  }
+  return r;
+}
+
 // Where one workgroup's segment lies.
 struct SegView {
   const float *xrow, *rrow;
@@ -357,21 +373,21 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
       two_sum<C>(v, xv, rv, hi, lo);
     }
     const bool affine = a.gamma != nullptr || a.beta != nullptr;
-    const int emax = a.width - 1;
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < C; ++c) {
+      f32x4 g = f32x4(1.0f), b = f32x4(0.0f);
+      if (affine) {
+        g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
+        b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * c + j;
         float y = ((hi[i] - m_hi) + (lo[i] - m_lo)) * rstd;
-        if (affine) {
-          const int e = max(0, min(v.elem(c, j), emax));
-          const float g = a.gamma ? a.gamma[e] : 1.0f;
-          const float b = a.beta ? a.beta[e] : 0.0f;
-          y = fmaf(y, g, b);
-        }
+        if (affine) y = fmaf(y, g[j], b[j]);
         s[i] = y;
       }
+    }
   }
 
   auto store = [&](auto nt) {
@@ -909,7 +925,6 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
     scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v1, a.inv_width, a.eps));
   }
   const bool affine = kLN && (a.gamma != nullptr || a.beta != nullptr);
-  const int emax = a.width - 1;
   auto map_slot = [&](int c, float (&o)[4]) {
     const f32x4 xx = x_at(c);
     if constexpr (OP == kOpRms) {
@@ -920,17 +935,17 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
       for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f((xx[j] - m) * kLog2e) * scale;
     } else {
       const f32x4 r4 = r_at(c);
+      f32x4 g = f32x4(1.0f), b = f32x4(0.0f);
+      if (affine) {
+        g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
+        b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float h, l;
         pair(xx, r4, j, h, l);
         float y = ((h - m_hi) + (l - m_lo)) * scale;
-        if (affine) {
-          const int e = max(0, min(v.elem(c, j), emax));
-          const float g = a.gamma ? a.gamma[e] : 1.0f;
-          const float b = a.beta ? a.beta[e] : 0.0f;
-          y = fmaf(y, g, b);
-        }
+        if (affine) y = fmaf(y, g[j], b[j]);
         o[j] = y;
       }
     }

@@ -1,7 +1,8 @@
 """The chooser's plans for large calls, at full size, through the plain entry
 points: every width band of the aligned-row rules (geometry and
 workgroups-per-CU cap), the three-slot rule for RMSNorm / softmax rows off
-16-byte boundaries, and the 16-slot residual LayerNorm stripe.  Sampled rows
+16-byte boundaries, and the large-call exchange rule (segments of 1024 or
+2048 granules, words in y's rows).  Sampled rows
 against the FP64 oracle (atol = rtol = 1e-5), every element finite, guard
 bands intact; the plan the chooser reports is checked to be the band's."""
 import numpy as np
@@ -24,8 +25,14 @@ BANDS = {
     ("rmsnorm", 65536, 2048): (256, 2, 256, 6),
     ("softmax", 32768, 4096): (128, 8, 256, 2),
     ("layernorm_residual", 32768, 4096): (256, 4, 512, 2),
-    ("layernorm_residual", 8192, 16384): (512, 8, 512, 0),
-    ("layernorm_residual", 4096, 32768): (512, 16, 512, 0),
+    # large calls of LayerNorm rows beyond 2048 granules and RMSNorm / softmax
+    # rows beyond 4096: the exchange kernels with words in y's rows
+    ("layernorm_residual", 8192, 16384): (256, 8, 256, 0),
+    ("layernorm_residual", 4096, 32768): (256, 8, 256, 0),
+    ("layernorm_residual", 6553, 20480): (256, 4, 256, 0),
+    ("rmsnorm", 6553, 20480): (256, 4, 256, 0),
+    ("softmax", 8192, 32768): (128, 8, 128, 0),
+    ("softmax", 4480, 30001): (128, 8, 128, 0),
     ("layernorm", 131072, 1024): (128, 2, 128, 10),
     ("rmsnorm", 65568, 2047): (256, 3, 256, 6),
     ("softmax", 32776, 4095): (512, 3, 512, 0),
@@ -47,6 +54,10 @@ def test_band_full_size(op, rows, width):
     kop = "layernorm_residual" if op == "layernorm" else op
     p = R.rowred_plan_query(kop, xd, rd, out.y)
     assert (p.lanes_per_row, p.chunks, p.threads, (p.policy >> 12) & 15) == (L, C, T, cap), p
+    exchange = (op, width) in (("layernorm_residual", 16384), ("layernorm_residual", 32768),
+                               ("layernorm_residual", 20480), ("rmsnorm", 20480), ("softmax", 32768),
+                               ("softmax", 30001))
+    assert bool(p.policy & R.ROWRED_POLICY_EXCHANGE) == exchange, p
     eps = synthetic.EPS.get(op, 0.0)
     if op in ("layernorm", "layernorm_residual"):
         R.rowred_layernorm(xd, rd, None, None, out.y, eps=eps)

@@ -58,8 +58,9 @@ def test_reload_matches_resident_bitwise(op, width):
 @pytest.mark.parametrize("case", [synthetic.CORE_WORKLOADS[4][0], synthetic.CORE_WORKLOADS[5][0]], ids=lambda c: c.name)
 def test_reload_full_size(case):
     """The chooser's geometry with the reload bit at a full workload shape:
-    bitwise the resident result (the register kernel of that geometry, with
-    two softmax collectives: the reload kernels have no LDS-stripe or
+    bitwise the resident result (the register kernel of that geometry -- for
+    exchange and LDS-stripe plans one 1024-lane workgroup per row -- with two
+    softmax collectives: the reload kernels have no LDS-stripe, exchange or
     one-collective form)."""
     print_case(case.name)
     x = synthetic.case_input(case, "x")
@@ -67,8 +68,12 @@ def test_reload_full_size(case):
     xd = shifted_input(x, 0)
     rd = shifted_input(r, 0) if r is not None else None
     q = R.rowred_plan_query(case.op, xd, rd, Guarded(case.rows, case.width, 0).y)
-    p = R.Plan(q.lanes_per_row, 0, q.chunks, q.threads, 0,
-               policy=q.policy & ~(R.ROWRED_POLICY_LDS_STRIPE | R.ROWRED_POLICY_ONLINE))
+    L, C, T, pol = q.lanes_per_row, q.chunks, q.threads, q.policy & ~R.ROWRED_POLICY_ONLINE
+    if pol & (R.ROWRED_POLICY_EXCHANGE | R.ROWRED_POLICY_LDS_STRIPE):  # one 1024-lane workgroup per row
+        L = T = 1024
+        C = -(-q.window // 1024)
+        pol &= R.ROWRED_POLICY_NT_LOADS | R.ROWRED_POLICY_NT_STORES | R.ROWRED_POLICY_XCD_REMAP
+    p = R.Plan(L, 0, C, T, 0, policy=pol)
     y0 = run(case.op, xd, rd, p, case.rows, case.width, 0)
     pr = R.Plan(p.lanes_per_row, 0, p.chunks, p.threads, 0, policy=p.policy | R.ROWRED_POLICY_RELOAD)
     y1 = run(case.op, xd, rd, pr, case.rows, case.width, 0)

@@ -165,9 +165,16 @@ def test_row_exchange_many_rows():
     assert_close(y[pick], reference(op, x[pick], None, None, None), "many rows")
 
 
-# the chooser's plans for rows beyond the register window, at full size
+# the chooser's plans for rows beyond the register window, and for large
+# calls of narrower rows, at full size; affine LayerNorm keeps the head+tail
+# kernels beyond the register window; small calls keep the row kernels.
 FULL = [("softmax", 4096, 65536), ("rmsnorm", 2048, 131072), ("layernorm_residual", 1024, 65536),
-        ("softmax", 64, 1 << 20), ("layernorm_residual", 256, 1 << 18), ("rmsnorm", 2048, 40000)]
+        ("softmax", 64, 1 << 20), ("layernorm_residual", 256, 1 << 18), ("rmsnorm", 2048, 40000),
+        ("softmax", 16, 65536), ("layernorm", 5461, 24576), ("layernorm_affine", 4096, 32768),
+        ("layernorm_affine", 1024, 65536), ("rmsnorm", 6710, 20001), ("layernorm_residual", 600, 20480),
+        ("softmax", 1024, 24576)]
+EXPECT_EXCHANGE = {("layernorm_affine", 1024, 65536): False, ("rmsnorm", 6710, 20001): False,
+                   ("layernorm_residual", 600, 20480): False, ("softmax", 1024, 24576): False}
 
 
 @pytest.mark.parametrize("op,rows,width", FULL, ids=lambda v: str(v))
@@ -180,11 +187,19 @@ def test_chooser_full_size(op, rows, width):
     xd = shifted_input(x, 0)
     rd = shifted_input(r, 0) if r is not None else None
     out = Guarded(rows, width)
-    p = R.rowred_plan_query(op, xd, rd, out.y)
+    g = b = gd = bd = None
+    if op == "layernorm_affine":
+        g, b = synthetic.affine_vectors(synthetic.Case(7, op, rows, width, "uniform"))
+        gd, bd = t.from_numpy(g).cuda(), t.from_numpy(b).cuda()
+    if op.startswith("layernorm"):
+        p = R.rowred_layernorm_plan_query(xd, rd, gd, bd, out.y)
+    else:
+        p = R.rowred_plan_query(op, xd, rd, out.y)
     print_case("chooser", op, rows, width, p)
+    assert bool(p.policy & EXCHANGE) == EXPECT_EXCHANGE.get((op, rows, width), True), p
     eps = synthetic.EPS.get("layernorm" if op.startswith("layernorm") else op, 0.0)
-    if op == "layernorm_residual":
-        R.rowred_layernorm(xd, rd, None, None, out.y, eps=eps)
+    if op.startswith("layernorm"):
+        R.rowred_layernorm(xd, rd, gd, bd, out.y, eps=eps)
     elif op == "rmsnorm":
         R.rowred_rmsnorm(xd, out.y, eps=eps)
     else:
@@ -196,5 +211,5 @@ def test_chooser_full_size(op, rows, width):
     pick = np.unique(np.concatenate([np.arange(2), rows - 1 - np.arange(2),
                                      np.random.default_rng(rows ^ width).integers(0, rows, 24)]))
     ref = oracle.run_op(op, x[pick], r[pick] if r is not None else None, eps=synthetic.EPS.get(
-        "layernorm" if op.startswith("layernorm") else op))
+        "layernorm" if op.startswith("layernorm") else op), gamma=g, beta=b)
     assert_close(y[pick], ref, f"{op} {rows}x{width} {p}")

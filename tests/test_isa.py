@@ -199,8 +199,11 @@ def test_split_kernels(asm):
             assert nt == 0 and cached > 0, dn
             assert body.count("s_barrier") == {0: 2, 1: 1, 2: 2, 3: 1, 4: 1}[op], dn
         elif kind == "seg_apply_kernel":
-            # plus at most one cached 16-byte load: the row record
-            assert nt > 0 and cached - nt in (0, 1), (dn, nt, cached)
+            # plus at most one cached 16-byte load (the row record), and for
+            # LayerNorm one each of gamma and beta per slot
+            C = int(dn.split(kind + "<")[1].split(",")[1].split(">")[0])
+            extra = (0, 1, 2 * C, 2 * C + 1) if op == 0 else (0, 1)
+            assert nt > 0 and cached - nt in extra, (dn, nt, cached)
             assert "s_barrier" not in body, dn
             assert "global_store_dwordx4" in body, dn
         else:
