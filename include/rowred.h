@@ -42,15 +42,24 @@
  * A NULL or misaligned pointer otherwise -> ROWRED_ERR_INVALID_ARG.  A row
  * whose 16-byte slot window (ceil((width + misalignment) / 4)) is at most
  * 8192 (width <= 32768 for 16-byte-aligned rows) is held in registers across
- * the phases and read once; RMSNorm and softmax rows of up to 16384 slots
- * (width <= 65536) are held in registers and LDS (ROWRED_POLICY_LDS_STRIPE)
- * and read once too.  Of wider RMSNorm and softmax rows the first 16384
- * slots are held that way, of wider LayerNorm rows x and r of the first 8192,
- * and the rest is walked twice (ROWRED_POLICY_LDS_STRIPE |
- * ROWRED_POLICY_LOOPED).  Wider row sum and min/max rows are walked once by
- * one workgroup (ROWRED_POLICY_LOOPED).  That suits many rows; for few
- * wide rows the _ws entry points at the end split each row over many
- * workgroups.  width > ROWRED_MAX_WIDTH -> ROWRED_ERR_UNSUPPORTED.
+ * the phases and read once.  LayerNorm, RMSNorm and softmax rows wider than
+ * that (up to 64 segments of 4096 slots, about a million columns; LayerNorm
+ * 128), and in calls of 128 MiB or more per input also LayerNorm rows of
+ * 2049-8192 slots and RMSNorm / softmax rows of 4097-8192 (rows off 16-byte
+ * boundaries: 512 MiB), are cut into segments of one workgroup each that
+ * hold their part in registers (and LDS) and swap their statistics through
+ * words kept in y's own row (ROWRED_POLICY_EXCHANGE on a row plan): read
+ * once, no workspace.  That needs the device to hold twice a row's
+ * segments at once.  Where it does not, for wider rows, and for affine
+ * LayerNorm beyond 8192 slots (where the exchange is slower): RMSNorm and
+ * softmax rows of up to 16384 slots are held in registers and LDS
+ * (ROWRED_POLICY_LDS_STRIPE), wider ones have their first 16384 slots held
+ * that way, wider LayerNorm rows x and r of their first 8192, and the rest
+ * is walked twice (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED).  Wider
+ * row sum and min/max rows are walked once by one workgroup
+ * (ROWRED_POLICY_LOOPED); for few of them the _ws entry points at the end
+ * split each row over many workgroups.  width > ROWRED_MAX_WIDTH ->
+ * ROWRED_ERR_UNSUPPORTED.
  *
  * eps must be finite and >= 0, else ROWRED_ERR_INVALID_ARG.  eps = 0 is
  * accepted; a LayerNorm row with zero variance then gives NaN (0/0), as
@@ -124,8 +133,9 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
  * their `width` elements.  With all three NULL this is the no-affine
  * LayerNorm of the same page's "Validation" section.  With gamma or beta,
  * rows of 6145-8192 granules (24577-32768 floats for 16-byte aligned rows)
- * take the looped kernels (gamma/beta need registers the wider
- * register-resident kernels do not have), wider rows the head+tail kernels.
+ * take the exchange kernels in large calls (see Sizes above) and the looped
+ * kernels otherwise (gamma/beta need registers the wider register-resident
+ * kernels do not have), wider rows the head+tail kernels.
  */
 int rowred_layernorm(const float *x, const float *r, const float *gamma,
                      const float *beta, float *y, int64_t rows, int64_t width,
@@ -191,7 +201,8 @@ typedef struct rowred_plan {
   int32_t chunks;         /* 16-byte slots per lane: 1..8, 10, 12 or 16 (affine LayerNorm: <= 12) */
   int32_t threads;        /* workgroup size: multiple of 64, <= 1024 (<= 512 when chunks > 8,
                              and for affine LayerNorm when chunks >= 7) */
-  int64_t grid;           /* workgroups launched: ceil(rows / rows_per_group) */
+  int64_t grid;           /* workgroups launched: ceil(rows / rows_per_group)
+                             (ROWRED_POLICY_EXCHANGE: rows * segments per row) */
   int32_t vector_io;      /* 1: r and y share x's address modulo 16 (all accesses 16 bytes) */
   int32_t window;         /* largest number of 16-byte granules a row of x spans (L*chunks covers it) */
   int32_t policy;         /* memory policy: ROWRED_POLICY_* bits */
@@ -239,7 +250,7 @@ enum rowred_policy {
                                      tiles; REVERSE then walks the tail last tile first in the
                                      second walk and maps the head after it (measured within
                                      3% either way, not chosen) */
-  ROWRED_POLICY_EXCHANGE = 128,   /* split plans only, LayerNorm / RMSNorm / softmax: one kernel
+  ROWRED_POLICY_EXCHANGE = 128,   /* LayerNorm / RMSNorm / softmax.  Split plans: one kernel
                                      instead of three.  Each (row, segment) workgroup keeps its
                                      segment in registers, publishes its statistics to the
                                      workspace and waits for the row's other segments, so x (and
@@ -247,7 +258,23 @@ enum rowred_policy {
                                      chunks may also be 8
                                      (threads <= 512; not LayerNorm).
                                      NT_LOADS / NT_STORES apply to its loads and stores;
-                                     REVERSE may not be set */
+                                     REVERSE may not be set.
+                                     Row plans (lanes_per_row == threads, beside it only
+                                     NT_LOADS, NT_STORES and LDS_STRIPE): the same kernels with
+                                     the geometry of the split plan of these threads, chunks and
+                                     policy (S segments of threads * chunks granules per row,
+                                     grid = rows * S), the statistics swapped through 8-byte
+                                     words in y's own row, from its first 16-byte boundary: 2S +
+                                     1 for LayerNorm, S + 1 otherwise, which must end within the
+                                     first segment's outputs (16 * threads * chunks - 12 bytes)
+                                     and within the row (else ROWRED_ERR_INVALID_ARG).  A small
+                                     kernel zeroes them first; the first segment writes its
+                                     outputs over them once every segment of the row has read
+                                     them.  The device must hold 2S of these workgroups at
+                                     once, else ROWRED_ERR_UNSUPPORTED at run time.  Waits are
+                                     bounded (about a second); a wait that gives up leaves its
+                                     row's segment NaN (there is no status word).  Same results
+                                     bit for bit as the split plan */
   ROWRED_POLICY_LDS_STRIPE = 256, /* row plans: RMSNorm and softmax, lanes_per_row == threads
                                      == 1024, chunks 5-16: slots 0-3 (from 9 chunks on 0-7)
                                      of each lane stay in registers and the rest are loaded
@@ -304,7 +331,10 @@ enum rowred_policy {
  * rowred_layernorm without a residual; for ROWRED_OP_ROW_SUM and
  * ROWRED_OP_ROW_MINMAX, y is out / out_min and r is out_max, vectors of
  * `rows` floats).  No device work, callable without a GPU.  Returns the
- * status the entry point would return before launching.
+ * status the entry point would return before launching.  Exchange plans
+ * depend on how many workgroups the current device holds at once (a host
+ * query of the HIP runtime); without a device the plan is the one the entry
+ * point would take where they do not fit.
  */
 int rowred_plan_query(int op, const float *x, const float *r, const float *y,
                       int64_t rows, int64_t width, rowred_plan *out);
@@ -357,9 +387,13 @@ int rowred_copy(const float *x, float *y, int64_t n, hipStream_t stream);
 /* ------------------------------------------------------------------------
  * Any width, and rows split across workgroups: the _ws entry points.
  *
- * The entry points above give each row one workgroup: rows wider than 8192
- * 16-byte granules are walked twice by it, and a matrix of few wide rows
- * keeps few compute units busy.  "Immutable input reuse
+ * The entry points above split wide LayerNorm, RMSNorm and softmax rows over
+ * workgroups only where the device holds a row's segments twice over and
+ * the row takes at most 64 segments of 4096 granules (RMSNorm, softmax:
+ * about a million columns; LayerNorm 128, about two million); row sum
+ * and min/max rows, and wider rows, get one workgroup each, which walks
+ * rows wider than 8192 16-byte granules twice, and a matrix of few such
+ * rows keeps few compute units busy.  "Immutable input reuse
  * in Metal reductions" leaves rows beyond the private stripe open (section
  * "Next decisions and open questions": mixed cache/reload choices) and times
  * few-row shapes such as 7x1537 (section "Fixed-width GPU and dispatch
