@@ -79,7 +79,7 @@ WORKLOAD_NAMES = {
     8: "row sum and row min/max, 16384x8192 U[-1,1] and 131072x257 N(0,1)",
     9: "any width (_ws entry points): softmax 64x1048576, RMSNorm 1024x131072, residual LayerNorm 256x262144, "
        "row sum 16x4194304, softmax 7x1537",
-    10: "many wide rows (plain entry points: softmax held in registers and LDS, the rest looped): softmax "
+    10: "many wide rows (plain entry points: exchange kernels with words in y's rows, row sum looped): softmax "
         "4096x65536, RMSNorm 2048x131072, residual LayerNorm 1024x65536, row sum 2048x131072",
     11: "many wide rows (_ws entry points: exchange kernels, row sum looped): softmax 4096x65536, "
         "RMSNorm 2048x131072, residual LayerNorm 1024x65536, row sum 2048x131072",
