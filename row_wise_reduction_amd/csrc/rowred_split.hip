@@ -372,21 +372,21 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
     } else {
       two_sum<C>(v, xv, rv, hi, lo);
     }
-    const bool affine = a.gamma != nullptr || a.beta != nullptr;
+    // two loops, so that gamma / beta take no registers without them
+    if (a.gamma != nullptr || a.beta != nullptr) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      f32x4 g = f32x4(1.0f), b = f32x4(0.0f);
-      if (affine) {
-        g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
-        b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
-      }
+      for (int c = 0; c < C; ++c) {
+        const f32x4 g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
+        const f32x4 b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * c + j;
-        float y = ((hi[i] - m_hi) + (lo[i] - m_lo)) * rstd;
-        if (affine) y = fmaf(y, g[j], b[j]);
-        s[i] = y;
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * c + j;
+          s[i] = fmaf(((hi[i] - m_hi) + (lo[i] - m_lo)) * rstd, g[j], b[j]);
+        }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4 * C; ++i) s[i] = ((hi[i] - m_hi) + (lo[i] - m_lo)) * rstd;
     }
   }
 
@@ -935,18 +935,23 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
       for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f((xx[j] - m) * kLog2e) * scale;
     } else {
       const f32x4 r4 = r_at(c);
-      f32x4 g = f32x4(1.0f), b = f32x4(0.0f);
+      // two loops, so that gamma / beta take no registers without them
       if (affine) {
-        g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
-        b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
-      }
+        const f32x4 g = affine_slot(a.gamma, v.elem(c, 0), a.width, 1.0f);
+        const f32x4 b = affine_slot(a.beta, v.elem(c, 0), a.width, 0.0f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float h, l;
-        pair(xx, r4, j, h, l);
-        float y = ((h - m_hi) + (l - m_lo)) * scale;
-        if (affine) y = fmaf(y, g[j], b[j]);
-        o[j] = y;
+        for (int j = 0; j < 4; ++j) {
+          float h, l;
+          pair(xx, r4, j, h, l);
+          o[j] = fmaf(((h - m_hi) + (l - m_lo)) * scale, g[j], b[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float h, l;
+          pair(xx, r4, j, h, l);
+          o[j] = ((h - m_hi) + (l - m_lo)) * scale;
+        }
       }
     }
   };
