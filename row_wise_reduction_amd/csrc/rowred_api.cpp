@@ -373,6 +373,11 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // words in y's rows too, in segments of 1024 granules (256 x 4; softmax
   // rows beyond 6144 granules 128 x 8), LayerNorm in segments of 2048 (256 x
   // 8, half in LDS) where they pad no more than segments of 1024 would.
+  // Aligned RMSNorm / softmax rows of 3073-4096 granules at 128-256 MiB
+  // take two 2048-granule LDS segments (softmax 2048x16384 53.3 -> 49.8 us,
+  // 4096x16384 95.7 -> 93.2 us; RMSNorm 2048x16384 52.1 -> 48.6 us,
+  // 4096x16384 93.6 -> 92.4 us; from 384 MiB the row kernels are 1-2%
+  // ahead).
   // MI355X, against the register, LDS-stripe and looped kernels: residual
   // LayerNorm 6553x20480 332 -> 255 us, 4096x32768 280 -> 259 us, 8192x16384
   // 270 -> 259 us, 10922x12288 258 -> 256 us, 6710x20001 298 -> 266 us;
@@ -384,15 +389,17 @@ void choose_plan(const Call &c, rowred_plan *p) {
     const bool ln = c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
     const bool aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
     const int64_t bytes = c.rows * c.width * 4;
+    const bool rms_sm = c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX;
     const bool large = ln ? c.window > 2048 && bytes >= (int64_t(128) << 20)
-                          : (c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX) && c.window > 4096 &&
-                                bytes >= (int64_t(aligned ? 128 : 512) << 20);
+                          : rms_sm && ((c.window > 4096 && bytes >= (int64_t(aligned ? 128 : 512) << 20)) ||
+                                       (aligned && c.window > 3072 && bytes >= (int64_t(128) << 20) &&
+                                        bytes <= (int64_t(256) << 20)));
     if (large) {
       rowred_plan q = rowred_plan{};
       q.threads = 256;
       q.chunks = 4;
       q.policy = kPolicyExchange | kPolicyNtLoads | kPolicyNtStores;
-      if (ln && ((c.window + 1023) / 1024) % 2 == 0) {
+      if ((ln && ((c.window + 1023) / 1024) % 2 == 0) || (!ln && c.window <= 4096)) {
         q.chunks = 8;
         q.policy |= kPolicyLdsStripe;
       } else if (c.op == ROWRED_OP_SOFTMAX && c.window > 6144) {

@@ -33,6 +33,8 @@ BANDS = {
     ("rmsnorm", 6553, 20480): (256, 4, 256, 0),
     ("softmax", 8192, 32768): (128, 8, 128, 0),
     ("softmax", 4480, 30001): (128, 8, 128, 0),
+    ("softmax", 2048, 16384): (256, 8, 256, 0),
+    ("rmsnorm", 4096, 16384): (256, 8, 256, 0),
     ("layernorm", 131072, 1024): (128, 2, 128, 10),
     ("rmsnorm", 65568, 2047): (256, 3, 256, 6),
     ("softmax", 32776, 4095): (512, 3, 512, 0),
@@ -56,7 +58,7 @@ def test_band_full_size(op, rows, width):
     assert (p.lanes_per_row, p.chunks, p.threads, (p.policy >> 12) & 15) == (L, C, T, cap), p
     exchange = (op, width) in (("layernorm_residual", 16384), ("layernorm_residual", 32768),
                                ("layernorm_residual", 20480), ("rmsnorm", 20480), ("softmax", 32768),
-                               ("softmax", 30001))
+                               ("softmax", 30001), ("softmax", 16384), ("rmsnorm", 16384))
     assert bool(p.policy & R.ROWRED_POLICY_EXCHANGE) == exchange, p
     eps = synthetic.EPS.get(op, 0.0)
     if op in ("layernorm", "layernorm_residual"):
