@@ -367,33 +367,43 @@ void choose_plan(const Call &c, rowred_plan *p) {
     choose_looped(c, p);
     return;
   }
-  // Large calls (128 MiB or more per input; RMSNorm and softmax rows off
-  // 16-byte boundaries 512 MiB) of LayerNorm rows of 2049-8192 granules and
-  // RMSNorm / softmax rows of 4097-8192: the exchange kernels with their
-  // words in y's rows too, in segments of 1024 granules (256 x 4; softmax
-  // rows beyond 6144 granules 128 x 8), LayerNorm in segments of 2048 (256 x
-  // 8, half in LDS) where they pad no more than segments of 1024 would.
-  // Aligned RMSNorm / softmax rows of 3073-4096 granules at 128-256 MiB
-  // take two 2048-granule LDS segments (softmax 2048x16384 53.3 -> 49.8 us,
-  // 4096x16384 95.7 -> 93.2 us; RMSNorm 2048x16384 52.1 -> 48.6 us,
-  // 4096x16384 93.6 -> 92.4 us; from 384 MiB the row kernels are 1-2%
-  // ahead).
-  // MI355X, against the register, LDS-stripe and looped kernels: residual
-  // LayerNorm 6553x20480 332 -> 255 us, 4096x32768 280 -> 259 us, 8192x16384
-  // 270 -> 259 us, 10922x12288 258 -> 256 us, 6710x20001 298 -> 266 us;
-  // plain 8192x16384 217 -> 189 us; affine 4096x32768 415 -> 234 us;
-  // softmax 8192x32768 364 -> 339 us, 5461x24576 183 -> 172 us; RMSNorm
-  // 8192x32768 357 -> 337 us, 1638x20480 53.1 -> 48.8 us.  Smaller calls
-  // lose (16 MiB: 7-11 us against 10-15 us, the row-word clear included).
+  // Large calls of rows of up to 8192 granules: the exchange kernels with
+  // their words in y's rows too, in segments of 1024 granules (256 x 4;
+  // softmax rows beyond 6144 granules 128 x 8), LayerNorm in segments of
+  // 2048 (256 x 8, half in LDS) where they pad no more than segments of 1024
+  // would.  Taken, from 128 MiB per input, for LayerNorm rows on 16-byte
+  // boundaries beyond 2048 granules (residual LayerNorm from 4096), other
+  // LayerNorm rows beyond 4096, RMSNorm / softmax rows on 16-byte boundaries
+  // beyond 4096 granules whose segments pad at most 1/16 of the row (beyond
+  // 6144 granules from 256 MiB: RMSNorm 1024x32768 49.1 -> 50.7 us at 128),
+  // and from 512 MiB any RMSNorm / softmax rows beyond 4096; aligned RMSNorm / softmax
+  // rows of exactly 4096 granules at 128-256 MiB run as two 2048-granule LDS
+  // segments.  MI355X, against the register, LDS-stripe and looped kernels,
+  // alternating order: residual LayerNorm 6553x20480 332 -> 255 us,
+  // 4096x32768 280 -> 259 us, 8192x16384 270 -> 259 us, 8192x16383 312 -> 288
+  // us; plain 11915x11264 238 -> 205 us, 8192x16384 217 -> 189 us; affine
+  // 11915x11264 258 -> 243 us, 4096x32768 415 -> 234 us; softmax 8192x32768
+  // 364 -> 339 us, 32768x16383 823 -> 711 us, 2048x16384 53.3 -> 49.8 us;
+  // RMSNorm 8192x32768 357 -> 337 us, 4096x16384 93.6 -> 92.4 us.  They lose
+  // elsewhere: in calls of 16 MiB by 20-30% (a second launch and the waits),
+  // ragged LayerNorm of 2049-3001 granules by 5-34% (16384x8191 residual 260
+  // -> 317 us), residual LayerNorm below 4096 granules and RMSNorm / softmax
+  // rows of 3073-4095 by up to 13%, and ragged RMSNorm / softmax rows below
+  // 512 MiB by 2-9%.
   {
     const bool ln = c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
     const bool aligned = c.width % 4 == 0 && ((uintptr_t)c.x & 15) == 0;
     const int64_t bytes = c.rows * c.width * 4;
+    const int64_t MiB = int64_t(1) << 20;
+    const int64_t pad = (c.window + 1023) / 1024 * 1024 - c.window;  // of 1024-granule segments
     const bool rms_sm = c.op == ROWRED_OP_RMSNORM || c.op == ROWRED_OP_SOFTMAX;
-    const bool large = ln ? c.window > 2048 && bytes >= (int64_t(128) << 20)
-                          : rms_sm && ((c.window > 4096 && bytes >= (int64_t(aligned ? 128 : 512) << 20)) ||
-                                       (aligned && c.window > 3072 && bytes >= (int64_t(128) << 20) &&
-                                        bytes <= (int64_t(256) << 20)));
+    bool large = false;
+    if (ln)
+      large = bytes >= 128 * MiB && (aligned ? c.window > (c.r ? 4095 : 2048) : c.window > 4096);
+    else if (rms_sm)
+      large = (c.window > 4096 && (bytes >= 512 * MiB || (aligned && 16 * pad <= c.window &&
+                                                            bytes >= (c.window > 6144 ? 256 : 128) * MiB))) ||
+              (aligned && c.window == 4096 && bytes >= 128 * MiB && bytes <= 256 * MiB);
     if (large) {
       rowred_plan q = rowred_plan{};
       q.threads = 256;
