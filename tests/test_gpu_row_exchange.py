@@ -213,3 +213,47 @@ def test_chooser_full_size(op, rows, width):
     ref = oracle.run_op(op, x[pick], r[pick] if r is not None else None, eps=synthetic.EPS.get(
         "layernorm" if op.startswith("layernorm") else op), gamma=g, beta=b)
     assert_close(y[pick], ref, f"{op} {rows}x{width} {p}")
+
+
+def test_graph_capture_and_replay():
+    """Row exchange calls of three operators captured in one HIP graph (the
+    words' clear is a kernel: no memset node), replayed with eager work and
+    garbage written over y in between: every replay equals the eager results
+    bitwise."""
+    t = torch()
+    rows, width = 6, 140001
+    x = synthetic.random_matrix(506, rows, width, "normal")
+    r = synthetic.random_matrix(507, rows, width, "normal", tensor="r")
+    xd, rd = shifted_input(x, 1), shifted_input(r, 1)
+    outs = [t.empty(rows, width, device="cuda") for _ in range(3)]
+    plans = [R.Plan(256, 0, 8, 256, 0, policy=EXCHANGE | STREAM | LDS), R.Plan(256, 0, 8, 256, 0, policy=EXCHANGE | STREAM),
+             R.Plan(256, 0, 16, 256, 0, policy=EXCHANGE | STREAM | LDS)]
+
+    def calls():
+        R.rowred_run_plan("layernorm_residual", xd, rd, outs[0], plans[0], eps=1e-5)
+        R.rowred_run_plan("rmsnorm", xd, None, outs[1], plans[1], eps=1e-6)
+        R.rowred_run_plan("softmax", xd, None, outs[2], plans[2])
+
+    print_case("row exchange graph", rows, width)
+    calls()
+    t.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for i, op in enumerate(("layernorm_residual", "rmsnorm", "softmax")):
+        check(op, eager[i].cpu().numpy(), reference(op, x, r if i == 0 else None, None, None), f"graph {op}")
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            calls()
+    t.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for o in outs:
+            o.view(t.int32).fill_(0x3F800000 + rep)  # nonzero garbage where the words go
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert t.equal(o.view(t.int32), e.view(t.int32)), (rep, i)
+        calls()
+        t.cuda.synchronize()
