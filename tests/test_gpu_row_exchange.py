@@ -257,3 +257,39 @@ def test_graph_capture_and_replay():
             assert t.equal(o.view(t.int32), e.view(t.int32)), (rep, i)
         calls()
         t.cuda.synchronize()
+
+
+def test_two_streams_at_once():
+    """Row exchange calls on two streams at the same time (softmax and
+    residual LayerNorm through the plain entry points): the two kernels share
+    the chip, every wait still ends, and every row is finite and matches the
+    oracle on sampled rows, each replay bitwise the first."""
+    t = torch()
+    rows, width = 512, 65536
+    xs = [synthetic.random_matrix(600 + i, rows, width, "normal") for i in range(2)]
+    r = synthetic.random_matrix(602, rows, width, "normal", tensor="r")
+    xd = [t.from_numpy(x).cuda() for x in xs]
+    rd = t.from_numpy(r).cuda()
+    ys = [t.empty(rows, width, device="cuda") for _ in range(2)]
+    for op, x in (("softmax", xd[0]), ("layernorm_residual", xd[1])):
+        p = R.rowred_plan_query(op, x, rd if op == "layernorm_residual" else None, ys[0])
+        assert p.policy & EXCHANGE, (op, p)
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    first = None
+    t.cuda.synchronize()
+    for rep in range(3):
+        print_case("row exchange two streams", rep)
+        with t.cuda.stream(streams[0]):
+            R.rowred_softmax(xd[0], ys[0])
+        with t.cuda.stream(streams[1]):
+            R.rowred_layernorm_residual(xd[1], rd, ys[1], eps=1e-5)
+        t.cuda.synchronize()
+        got = [y.cpu().numpy() for y in ys]
+        assert all(np.isfinite(g).all() for g in got), rep
+        if first is None:
+            first = got
+        else:
+            assert all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(first, got)), rep
+    pick = [0, 255, 511]
+    assert_close(first[0][pick], oracle.softmax(xs[0][pick]), "softmax stream 0")
+    assert_close(first[1][pick], oracle.layernorm_residual(xs[1][pick], r[pick], 1e-5), "layernorm stream 1")
