@@ -197,14 +197,15 @@ int rowred_row_minmax(const float *x, float *out_min, float *out_max,
  */
 typedef struct rowred_plan {
   int32_t lanes_per_row;  /* L: power of two, 1..1024 */
-  int32_t rows_per_group; /* threads / L */
+  int32_t rows_per_group; /* threads / L (ROWRED_POLICY_EXCHANGE: 1) */
   int32_t chunks;         /* 16-byte slots per lane: 1..8, 10, 12 or 16 (affine LayerNorm: <= 12) */
   int32_t threads;        /* workgroup size: multiple of 64, <= 1024 (<= 512 when chunks > 8,
                              and for affine LayerNorm when chunks >= 7) */
   int64_t grid;           /* workgroups launched: ceil(rows / rows_per_group)
                              (ROWRED_POLICY_EXCHANGE: rows * segments per row) */
   int32_t vector_io;      /* 1: r and y share x's address modulo 16 (all accesses 16 bytes) */
-  int32_t window;         /* largest number of 16-byte granules a row of x spans (L*chunks covers it) */
+  int32_t window;         /* largest number of 16-byte granules a row of x spans (L*chunks covers it;
+                             ROWRED_POLICY_EXCHANGE: segments of L*chunks do) */
   int32_t policy;         /* memory policy: ROWRED_POLICY_* bits */
   int32_t reserved;       /* 0 */
 } rowred_plan;
