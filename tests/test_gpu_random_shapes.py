@@ -113,3 +113,51 @@ def test_boundary_widths(op):
             what = f"{op} {rows}x{width} shifts {shifts} ws {ws_entry}"
             print_case("boundary", what)
             check_case(op, rows, width, shifts, ws_entry, 104729 + 31 * i + ws_entry, what)
+
+
+def test_random_large_calls():
+    """Calls of 128-640 MiB per input at seeded random widths of 8193-40000
+    floats, x, r and y at random 16-byte phases, every matrix operator
+    through the plain entry points: the range where the chooser takes the
+    exchange kernels through y's rows for some rows and the row kernels for
+    others.  Sampled rows against the oracle, every element finite, guard
+    words intact."""
+    t = torch()
+    rng = np.random.default_rng(np.random.SeedSequence([20261204]))
+    ops = ["softmax", "rmsnorm", "layernorm_residual", "layernorm", "layernorm_affine"]
+    taken = 0
+    for i in range(10):
+        op = ops[i % len(ops)]
+        width = int(rng.integers(8193, 40001))
+        rows = int(rng.integers(128, 641)) * (1 << 20) // (4 * width)
+        sx, sr, sy = (int(v) for v in rng.integers(4, size=3))
+        what = f"{op} {rows}x{width} shifts {(sx, sr, sy)}"
+        print_case("large", what)
+        x = synthetic.random_matrix(900 + i, rows, width, "normal")
+        r = synthetic.random_matrix(950 + i, rows, width, "normal", tensor="r") if op == "layernorm_residual" else None
+        g = b = None
+        if op == "layernorm_affine":
+            g = (1.0 + 0.1 * synthetic.random_matrix(980 + i, 1, width, "normal", tensor="gamma")[0]).astype(np.float32)
+            b = (0.1 * synthetic.random_matrix(990 + i, 1, width, "normal", tensor="beta")[0]).astype(np.float32)
+        xd = shifted_input(x, sx)
+        rd = shifted_input(r, sr) if r is not None else None
+        gd = t.from_numpy(g).cuda() if g is not None else None
+        bd = t.from_numpy(b).cuda() if b is not None else None
+        out = Guarded(rows, width, sy)
+        if op.startswith("layernorm"):
+            p = R.rowred_layernorm_plan_query(xd, rd, gd, bd, out.y)
+            R.rowred_layernorm(xd, rd, gd, bd, out.y, eps=1e-5)
+        else:
+            p = R.rowred_plan_query(op, xd, None, out.y)
+            R.rowred_rmsnorm(xd, out.y, eps=1e-6) if op == "rmsnorm" else R.rowred_softmax(xd, out.y)
+        taken += bool(p.policy & R.ROWRED_POLICY_EXCHANGE)
+        t.cuda.synchronize()
+        assert out.guards_intact(), what
+        y = out.host()
+        assert np.isfinite(y).all(), what
+        pick = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 14)]))
+        ref = reference(op, x[pick], r[pick] if r is not None else None, g, b)
+        got = y[pick].astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 1e-5 + 1e-5 * np.abs(ref)), f"{what} {p}"
+        del x, r, xd, rd, out, y
+    assert taken >= 3  # the draw reaches the exchange rule more than once
