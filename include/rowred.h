@@ -267,15 +267,20 @@ enum rowred_policy {
                                      grid = rows * S), the statistics swapped through 8-byte
                                      words in y's own row, from its first 16-byte boundary: 2S +
                                      1 for LayerNorm, S + 1 otherwise, which must end within the
-                                     first segment's outputs (16 * threads * chunks - 12 bytes)
-                                     and within the row (else ROWRED_ERR_INVALID_ARG).  A small
-                                     kernel zeroes them first; the first segment writes its
-                                     outputs over them once every segment of the row has read
-                                     them.  The device must hold 2S of these workgroups at
-                                     once, else ROWRED_ERR_UNSUPPORTED at run time.  Waits are
-                                     bounded (about a second); a wait that gives up leaves its
-                                     row's segment NaN (there is no status word).  Same results
-                                     bit for bit as the split plan */
+                                     first segment's outputs (16 * threads * chunks - 12 bytes;
+                                     LayerNorm: within the granules of its first slot, 16 *
+                                     threads - 12 bytes) and within the row (else
+                                     ROWRED_ERR_INVALID_ARG).  A small kernel zeroes them first.
+                                     RMSNorm and softmax: the first segment writes its outputs
+                                     over them once every segment of the row has read them.
+                                     LayerNorm: the first segment leaves its granules over the
+                                     words unstored, and the workgroup that is the last of the
+                                     row to finish reading them computes and stores those.  The
+                                     device must hold 2S of these workgroups at once, else
+                                     ROWRED_ERR_UNSUPPORTED at run time.  Waits are bounded
+                                     (about a second); a wait that gives up leaves its segment
+                                     of the row NaN (there is no status word).  Same results bit
+                                     for bit as the split plan */
   ROWRED_POLICY_LDS_STRIPE = 256, /* row plans: RMSNorm and softmax, lanes_per_row == threads
                                      == 1024, chunks 5-16: slots 0-3 (from 9 chunks on 0-7)
                                      of each lane stay in registers and the rest are loaded

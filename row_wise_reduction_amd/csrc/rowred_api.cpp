@@ -1011,9 +1011,12 @@ int finish_row_exchange_plan(const Call &c, rowred_plan *p, rowred_split_plan *s
   q.policy = p->policy;
   const int st = finish_split(c, &q);  // the whole matrix in one launch (block_rows = rows)
   if (st != ROWRED_OK) return st;
-  // the row's words end inside segment 0's outputs and inside the row
-  const int64_t bytes = row_exchange_bytes(c.op == ROWRED_OP_LAYERNORM_RESIDUAL ? 2 : 1, q.segments);
-  if (bytes > 16 * (int64_t)q.threads * q.chunks - 12 || bytes > 4 * c.width) return ROWRED_ERR_INVALID_ARG;
+  // the row's words end inside the row and inside segment 0's outputs; for
+  // LayerNorm inside the granules of segment 0's first slot (which the row's
+  // last workgroup stores)
+  const bool ln = c.op == ROWRED_OP_LAYERNORM_RESIDUAL;
+  const int64_t bytes = row_exchange_bytes(ln ? 2 : 1, q.segments);
+  if (bytes > 16 * (int64_t)q.threads * (ln ? 1 : q.chunks) - 12 || bytes > 4 * c.width) return ROWRED_ERR_INVALID_ARG;
   p->rows_per_group = 1;
   p->window = c.window;
   p->vector_io = c.y_vec && (c.r == nullptr || c.r_vec) ? 1 : 0;

@@ -338,9 +338,16 @@ __global__ void __launch_bounds__(256) seg_merge_kernel(SegArgs a) {
 // Apply a row record to one segment held in registers and store it.
 // ---------------------------------------------------------------------------
 // PAIR (LayerNorm): xv and rv already hold the TwoSum pair (hi, lo) of x + r.
-template <int OP, int C, bool PAIR = false>
+// The exchange words in y's rows (defined with the exchange kernels below).
+__device__ __forceinline__ bool holds_row_words(const SegArgs &a, int64_t row, int rounds, int e0);
+
+// HOLD (LayerNorm exchange) with rounds > 0 (segment 0 with the words in
+// y): slot 0's granule is not stored where it overlaps the words (the
+// workgroup that completes the row stores it).  Without HOLD the code is
+// that of a plain apply.
+template <int OP, int C, bool PAIR = false, bool HOLD = false>
 __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, int64_t row, const f32x4 (&xv)[C],
-                                            const f32x4 (&rv)[C], Rec rr) {
+                                            const f32x4 (&rv)[C], Rec rr, int rounds = 0) {
   float s[4 * C];
   if constexpr (OP == kOpRms) {
     const float scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v0, a.inv_width, a.eps));
@@ -390,6 +397,8 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
     }
   }
 
+  bool skip0 = false;
+  if constexpr (HOLD) skip0 = rounds > 0 && holds_row_words(a, row, rounds, v.elem(0, 0));
   auto store = [&](auto nt) {
     constexpr bool NT = decltype(nt)::value;
     float *yrow = a.y + row * (int64_t)a.width;
@@ -397,6 +406,9 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
       f32x4 *yw = reinterpret_cast<f32x4 *>(yrow - v.off);
 #pragma unroll
       for (int c = 0; c < C; ++c) {
+        if constexpr (HOLD) {
+          if (c == 0 && skip0) continue;
+        }
         const int k = v.granule(c);
         const int e0 = 4 * k - v.off;
         if (e0 >= 0 && e0 + 4 <= a.width) {
@@ -409,10 +421,14 @@ __device__ __forceinline__ void apply_store(const SegArgs &a, const SegView &v, 
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < C; ++c)
+      for (int c = 0; c < C; ++c) {
+        if constexpr (HOLD) {
+          if (c == 0 && skip0) continue;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (v.valid(c, j)) store_g<NT>(yrow + v.elem(c, j), s[4 * c + j]);
+      }
     }
   };
   if (a.policy & kPolicyNtStores) store(std::true_type{});
@@ -493,14 +509,26 @@ __device__ __forceinline__ uint64_t *exchange_slots(const SegArgs &a, int round,
   return reinterpret_cast<uint64_t *>(a.ws) + 1 + ((int64_t)round * a.rows + row) * a.segments;
 }
 
-// With the words in y's row, segment 0 may write its outputs over them only
-// once every segment of the row has read them.  Each workgroup counts itself
-// done after its fold -- every lane's slot reads have returned by then: the
-// fold's barrier (or, for one wavefront, program order) follows the values'
-// use, so a relaxed count suffices -- and segment 0 waits for all S (bounded
-// like the slot waits) before any of its stores.  A wait that gives up
-// returns true: the caller writes NaN over the row's segment (segments that
-// had not read yet may then see outputs as words).
+// With the words in y's row, their granules may be stored only once every
+// segment of the row has read them.  Each workgroup counts itself done after
+// its fold -- every lane's slot reads have returned by then: the fold's
+// barrier (or, for one wavefront, program order) follows the values' use, so
+// a relaxed count suffices.  Two ways to honour the count:
+//  - RMSNorm and softmax (one round of words): segment 0 waits for the count
+//    to reach S (bounded like the slot waits) before any of its stores
+//    (release_row_words); the other workgroups add to it without waiting
+//    for the result.
+//  - LayerNorm (two rounds, a longer wait): every workgroup learns whether
+//    its count completed the row (count_row_words_read); segment 0 leaves
+//    its first-slot granules over the words unstored (the host keeps the
+//    words within them) and the completing workgroup stores them
+//    (finish_row_words), so no workgroup waits for another.  One returning
+//    atomic per workgroup: measured faster for LayerNorm (residual
+//    1024x65536 137.0 -> 133.6 us, 4096x32768 260.0 -> 255.5 us), slower
+//    for softmax (8192x32768 340.0 -> 343.2 us) and RMSNorm.
+//
+// The wait: true when it gave up; the caller then writes NaN over the row's
+// segment (segments that had not read yet may see outputs as words).
 __device__ __forceinline__ bool release_row_words(const SegArgs &a, int64_t row, int seg, int rounds) {
   if (!a.ws_in_y) return false;
   __shared__ int gave_up;
@@ -520,6 +548,96 @@ __device__ __forceinline__ bool release_row_words(const SegArgs &a, int64_t row,
   }
   __syncthreads();
   return gave_up != 0;
+}
+
+// The count that completes the row: true in wavefront 0 of the workgroup
+// whose count completed it, false elsewhere.
+__device__ __forceinline__ bool count_row_words_read(const SegArgs &a, int64_t row, int rounds) {
+  uint64_t old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_add(row_words(a, row) + (int64_t)rounds * a.segments, (uint64_t)1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x >= 64) return false;
+  return __builtin_amdgcn_readfirstlane(old + 1 == (uint64_t)a.segments ? 1 : 0) != 0;
+}
+
+// Whether segment 0's first-slot granule starting at row element e0 overlaps
+// the row's words (it is then stored by finish_row_words).
+__device__ __forceinline__ bool holds_row_words(const SegArgs &a, int64_t row, int rounds, int e0) {
+  const char *yrow = reinterpret_cast<const char *>(a.y + row * (int64_t)a.width);
+  const char *end = reinterpret_cast<const char *>(row_words(a, row) + (int64_t)rounds * a.segments + 1);
+  return 4 * (int64_t)e0 < end - yrow;
+}
+
+// Wavefront 0 of the workgroup that completed the row: segment 0's granules
+// over the words, recomputed from x (and r, gamma, beta) with the row record
+// by the arithmetic of the exchange kernels' output map, and stored as
+// segment 0 stores them.  Cached loads: a few granules per row.
+template <int OP>
+__device__ __forceinline__ void finish_row_words(const SegArgs &a, int64_t row, Rec rr, int rounds) {
+  const float *xrow = a.x + row * (int64_t)a.width;
+  const float *rrow = a.r ? a.r + row * (int64_t)a.width : nullptr;
+  float *yrow = a.y + row * (int64_t)a.width;
+  const int off = (int)(((uintptr_t)xrow >> 2) & 3);
+  const int kmax = ((a.width + off + 3) >> 2) - 1;
+  const char *end = reinterpret_cast<const char *>(row_words(a, row) + (int64_t)rounds * a.segments + 1);
+  const int held = (int)((end - reinterpret_cast<const char *>(yrow) + 3) / 4);  // elements [0, held)
+  const int kh = (held + off + 3) >> 2;                                          // granules [0, kh)
+  float scale = 0.0f, m = 0.0f, m_hi = 0.0f, m_lo = 0.0f;
+  if constexpr (OP == kOpRms) {
+    scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v0, a.inv_width, a.eps));
+  } else if constexpr (OP == kOpSoftmax) {
+    m = (float)rr.v0;
+    scale = __builtin_amdgcn_rcpf((float)rr.v1);
+  } else {
+    m_hi = (float)rr.v0;
+    m_lo = (float)(rr.v0 - (double)m_hi);
+    scale = __builtin_amdgcn_rsqf(fmaf((float)rr.v1, a.inv_width, a.eps));
+  }
+  const bool affine = OP == kOpLayerNorm && (a.gamma != nullptr || a.beta != nullptr);
+  for (int k = (int)threadIdx.x; k < kh; k += 64) {
+    const int e0 = 4 * k - off;
+    const f32x4 xx = reinterpret_cast<const f32x4 *>(xrow - off)[k < kmax ? k : kmax];
+    float o[4];
+    if constexpr (OP == kOpRms) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = xx[j] * scale;
+    } else if constexpr (OP == kOpSoftmax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f((xx[j] - m) * kLog2e) * scale;
+    } else {
+      f32x4 r4 = f32x4(0.0f);
+      if (rrow) {
+        if (a.r_vec) {
+          r4 = reinterpret_cast<const f32x4 *>(rrow - off)[k < kmax ? k : kmax];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r4[j] = rrow[max(0, min(e0 + j, a.width - 1))];
+        }
+      }
+      f32x4 g = f32x4(1.0f), b = f32x4(0.0f);
+      if (affine) {
+        g = affine_slot(a.gamma, e0, a.width, 1.0f);
+        b = affine_slot(a.beta, e0, a.width, 0.0f);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = xx[j], r = r4[j];
+        const float h = x + r;  // TwoSum, as the exchange kernels form the pair
+        const float bb = h - x;
+        const float l = (x - (h - bb)) + (r - bb);
+        const float y = ((h - m_hi) + (l - m_lo)) * scale;
+        o[j] = affine ? fmaf(y, g[j], b[j]) : y;
+      }
+    }
+    if (a.y_vec && e0 >= 0 && e0 + 4 <= a.width) {
+      reinterpret_cast<f32x4 *>(yrow - off)[k] = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((unsigned)(e0 + j) < (unsigned)a.width) yrow[e0 + j] = o[j];
+    }
+  }
 }
 
 __device__ __forceinline__ void publish(uint64_t *slot, uint64_t w) {
@@ -687,8 +805,14 @@ __global__ void __launch_bounds__(C >= 8 ? 512 : 1024) seg_exchange_kernel(SegAr
     // partials_d[1]'s reduction passed.
     rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
   }
-  if (release_row_words(a, row, seg, OP == kOpLayerNorm ? 2 : 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
-  apply_store<OP, C, OP == kOpLayerNorm>(a, v, row, xv, rv, rr);
+  if constexpr (OP == kOpLayerNorm) {
+    const bool last = a.ws_in_y && count_row_words_read(a, row, 2);
+    apply_store<OP, C, true, true>(a, v, row, xv, rv, rr, a.ws_in_y && seg == 0 ? 2 : 0);
+    if (last) finish_row_words<OP>(a, row, rr, 2);  // wavefront 0 of the row's last workgroup
+  } else {
+    if (release_row_words(a, row, seg, 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
+    apply_store<OP, C>(a, v, row, xv, rv, rr);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -910,7 +1034,16 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
     publish(slots1 + seg, encode((double)m2));
     rr = layernorm_row_record(a, slots0, slots1, G, v.off, lanes_log2, partials_d[1], partials_d[0]);
   }
-  if (release_row_words(a, row, seg, kLN ? 2 : 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
+  // LayerNorm, segment 0 with the words in y: its first-slot granule over
+  // them is left to the workgroup that completes the row; RMSNorm and
+  // softmax: segment 0 waits for the row's reads before its stores
+  bool last = false, skip0 = false;
+  if constexpr (kLN) {
+    last = a.ws_in_y && count_row_words_read(a, row, 2);
+    skip0 = a.ws_in_y && seg == 0 && holds_row_words(a, row, 2, v.elem(0, 0));
+  } else {
+    if (release_row_words(a, row, seg, 1)) rr = Rec{__builtin_nan(""), __builtin_nan("")};
+  }
 
   // ---- map and store, slot by slot.
   float scale = 0.0f, m_hi = 0.0f, m_lo = 0.0f;
@@ -960,6 +1093,7 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
     float *yrow = a.y + row * (int64_t)a.width;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
+      if (c == 0 && skip0) continue;
       float o[4];
       map_slot(c, o);
       const int k = v.granule(c);
@@ -982,6 +1116,9 @@ __global__ void __launch_bounds__(kXldsThreads) seg_xlds_kernel(SegArgs a) {
   };
   if (a.policy & kPolicyNtStores) store_all(std::true_type{});
   else store_all(std::false_type{});
+  if constexpr (kLN) {
+    if (last) finish_row_words<OP>(a, row, rr, 2);  // wavefront 0 of the row's last workgroup
+  }
 }
 
 // Zero the 64-bit words [first, 2 * n128) of the exchange area (16-byte

@@ -29,10 +29,12 @@ GEOMETRIES = [(64, 1, 0), (256, 2, 0), (1024, 4, 0), (256, 8, 0), (256, 8, LDS),
 
 def max_segments(op, T, C):
     """The most segments whose words (2 S + 1 for LayerNorm, S + 1 otherwise,
-    from the row's first 16-byte boundary) end inside segment 0's outputs."""
-    rounds = 2 if op.startswith("layernorm") else 1
+    from the row's first 16-byte boundary) end inside segment 0's outputs
+    (LayerNorm: inside the granules of its first slot)."""
+    ln = op.startswith("layernorm")
+    rounds = 2 if ln else 1
     S = min(128, T)
-    while 15 + 8 * (rounds * S + 1) > 16 * T * C - 12:
+    while 15 + 8 * (rounds * S + 1) > 16 * T * (1 if ln else C) - 12:
         S -= 1
     return S
 
