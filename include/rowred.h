@@ -51,9 +51,10 @@
  * words kept in y's own row (ROWRED_POLICY_EXCHANGE on a row plan): read
  * once, no workspace.  That needs the device to hold twice a row's
  * segments at once.  Where it does not, for wider rows, and for affine
- * LayerNorm beyond 8192 slots (where the exchange is slower): RMSNorm and
- * softmax rows of up to 16384 slots are held in registers and LDS
- * (ROWRED_POLICY_LDS_STRIPE), wider ones have their first 16384 slots held
+ * LayerNorm beyond 8192 slots with 256 rows or more (where the exchange is
+ * slower): RMSNorm and softmax rows of up to 16384 slots are held in
+ * registers and LDS (ROWRED_POLICY_LDS_STRIPE), wider ones have their first
+ * 16384 slots held
  * that way, wider LayerNorm rows x and r of their first 8192, and the rest
  * is walked twice (ROWRED_POLICY_LDS_STRIPE | ROWRED_POLICY_LOOPED).  Wider
  * row sum and min/max rows are walked once by one workgroup
@@ -135,7 +136,8 @@ int rowred_layernorm_residual(const float *x, const float *r, float *y,
  * rows of 6145-8192 granules (24577-32768 floats for 16-byte aligned rows)
  * take the exchange kernels in large calls (see Sizes above) and the looped
  * kernels otherwise (gamma/beta need registers the wider register-resident
- * kernels do not have), wider rows the head+tail kernels.
+ * kernels do not have), wider rows the head+tail kernels (the exchange
+ * kernels below 256 rows).
  */
 int rowred_layernorm(const float *x, const float *r, const float *gamma,
                      const float *beta, float *y, int64_t rows, int64_t width,

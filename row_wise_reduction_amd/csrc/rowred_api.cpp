@@ -294,9 +294,12 @@ void choose_plan(const Call &c, rowred_plan *p) {
   // RMSNorm 2048x40000 116 -> 110 us, 2048x131072 385 -> 346 us, 64x1048576
   // 183 -> 108 us; residual LayerNorm 1024x65536 160 -> 137 us, 4096x32772
   // 299 -> 276 us, 256x262144 198 -> 154 us.
-  // Affine LayerNorm keeps the head+tail kernels there (1024x65536 120 ->
-  // 116 us, 2048x40000 144 -> 133 us, 256x262144 145 -> 134 us).
-  if (c.window > kMaxWindow && c.op <= ROWRED_OP_SOFTMAX && !c.gamma && !c.beta) {
+  // Affine LayerNorm keeps the head+tail kernels there from 256 rows (one
+  // workgroup per row fills MI355X's 256 CUs; 2048x40000 141 -> 131 us,
+  // 256x262144 145 -> 134 us, 4096x32772 265 -> 226 us); fewer rows leave
+  // CUs idle (64x1048576 377 -> 167 us, 16x65536 20.3 -> 10.8 us through
+  // the exchange kernels).
+  if (c.window > kMaxWindow && c.op <= ROWRED_OP_SOFTMAX && ((!c.gamma && !c.beta) || c.rows < 256)) {
     rowred_split_plan sp;
     if (choose_exchange(c.op, c.rows, c.window, &sp)) {
       rowred_plan q = rowred_plan{};

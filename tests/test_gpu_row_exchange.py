@@ -169,12 +169,13 @@ def test_row_exchange_many_rows():
 
 # the chooser's plans for rows beyond the register window, and for large
 # calls of narrower rows, at full size; affine LayerNorm keeps the head+tail
-# kernels beyond the register window; small calls keep the row kernels.
+# kernels beyond the register window from 256 rows; small calls keep the row
+# kernels.
 FULL = [("softmax", 4096, 65536), ("rmsnorm", 2048, 131072), ("layernorm_residual", 1024, 65536),
         ("softmax", 64, 1 << 20), ("layernorm_residual", 256, 1 << 18), ("rmsnorm", 2048, 40000),
         ("softmax", 16, 65536), ("layernorm", 5461, 24576), ("layernorm_affine", 4096, 32768),
         ("layernorm_affine", 1024, 65536), ("rmsnorm", 6710, 20001), ("layernorm_residual", 600, 20480),
-        ("softmax", 1024, 24576)]
+        ("softmax", 1024, 24576), ("layernorm_affine", 64, 1 << 20)]
 EXPECT_EXCHANGE = {("layernorm_affine", 1024, 65536): False, ("rmsnorm", 6710, 20001): False,
                    ("layernorm_residual", 600, 20480): False, ("softmax", 1024, 24576): False}
 
